@@ -1,0 +1,214 @@
+"""DFlash draft hot path on MI355X (gfx950): thin Python binding of libdflash.so.
+
+The three calls of one speculative cycle -- context injection, the
+single-pass block draft and greedy verification -- run entirely in the HIP
+kernels of libdflash.so.  This module only marshals arguments: it checks that
+tensors are CUDA-resident and contiguous, passes their data pointers, the
+current HIP stream and the sizes through the C ABI declared in
+include/dflash.h, and raises DFlashError for a non-OK status.  PyTorch is used
+for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+from . import _abi
+from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DFLASH_BF16, DFLASH_F32, MAX_BLOCK,
+                   MAX_LAYERS, STATE_BYTES)
+
+__all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy", "load_library",
+           "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "MAX_BLOCK", "MAX_LAYERS"]
+
+LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+GLOBAL_KEYS = ("fc_w", "fc_norm", "embed", "lm_head", "final_norm")
+
+
+def load_library():
+    return _abi.load()
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_abi.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(rc: int):
+    if rc != _abi.DFLASH_OK:
+        raise DFlashError(rc, _abi.load().dflash_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclasses.dataclass
+class DrafterConfig:
+    hidden: int
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    intermediate: int
+    vocab: int
+    n_target_feats: int = 5
+    max_block: int = 16
+    mask_token_id: int | None = None     # default: vocab - 1
+    page_size: int = 16
+    dtype: str = "bf16"                  # "bf16" or "f32"
+    rope_theta: float = 1.0e6
+    rms_eps: float = 1.0e-6
+
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def to_c(self) -> _abi.Config:
+        mask = self.vocab - 1 if self.mask_token_id is None else self.mask_token_id
+        return _abi.Config(self.hidden, self.n_layers, self.n_q_heads, self.n_kv_heads,
+                           self.head_dim, self.intermediate, self.vocab, self.n_target_feats,
+                           self.max_block, mask, self.page_size,
+                           DFLASH_BF16 if self.dtype == "bf16" else DFLASH_F32,
+                           float(self.rope_theta), float(self.rms_eps))
+
+
+class KVCache:
+    """Paged draft cache: pages [n_layers][n_pages][2][Hkv][page_size][dh],
+    page_table int32 [batch][max_pages_per_seq], ctx_lens int32 [batch]."""
+
+    def __init__(self, pages, page_table, ctx_lens):
+        import torch
+        self.pages, self.page_table, self.ctx_lens = pages, page_table, ctx_lens
+        _dev_ptr(pages, "pages")
+        _dev_ptr(page_table, "page_table", torch.int32)
+        _dev_ptr(ctx_lens, "ctx_lens", torch.int32)
+        if pages.dim() != 6 or page_table.dim() != 2 or ctx_lens.dim() != 1:
+            raise ValueError("KVCache: pages must be 6-D, page_table 2-D, ctx_lens 1-D")
+        self.c = _abi.KV(pages.data_ptr(), pages.shape[1], page_table.shape[1],
+                         page_table.data_ptr(), ctx_lens.data_ptr())
+
+    @property
+    def batch(self):
+        return self.page_table.shape[0]
+
+    @property
+    def max_pages_per_seq(self):
+        return self.page_table.shape[1]
+
+
+class Drafter:
+    """A drafter whose weights live in device tensors (names: fc_w, fc_norm,
+    embed, lm_head, final_norm and l{i}.{attn_norm, wq, wk, wv, wo, mlp_norm,
+    w_gate, w_up, w_down})."""
+
+    def __init__(self, cfg: DrafterConfig, weights: dict):
+        import torch
+        self.lib = _abi.load()
+        self.cfg = cfg
+        dt = cfg.torch_dtype()
+        self._weights = weights
+        w = _abi.Weights()
+        for k in GLOBAL_KEYS:
+            setattr(w, k, _dev_ptr(weights[k], k, dt).value)
+        if cfg.n_layers > MAX_LAYERS:
+            raise ValueError(f"at most {MAX_LAYERS} layers")
+        for l in range(cfg.n_layers):
+            for k in LAYER_KEYS:
+                setattr(w.layer[l], k, _dev_ptr(weights[f"l{l}.{k}"], f"l{l}.{k}", dt).value)
+        dev = weights["embed"].device
+        self.state = torch.zeros(STATE_BYTES, dtype=torch.uint8, device=dev)
+        self._c_cfg = cfg.to_c()
+        self._c_w = w
+        h = ctypes.c_void_p()
+        _check(self.lib.dflash_model_create(ctypes.byref(self._c_cfg), ctypes.byref(w),
+                                            ctypes.c_void_p(self.state.data_ptr()), ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.dflash_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, max_batch, max_block, max_new_tokens, max_pages_per_seq) -> int:
+        n = self.lib.dflash_workspace_bytes(self.handle, max_batch, max_block, max_new_tokens,
+                                            max_pages_per_seq)
+        if n == 0:
+            raise DFlashError(-1, "workspace_bytes: invalid arguments")
+        return int(n)
+
+    def inject(self, kv: KVCache, hidden, cu_new, workspace, stream=None):
+        import torch
+        n_tok = int(hidden.shape[0]) if hidden is not None else 0
+        _check(self.lib.dflash_inject_ctx(
+            self.handle, ctypes.byref(kv.c), _dev_ptr(hidden, "hidden", self.cfg.torch_dtype()),
+            _dev_ptr(cu_new, "cu_new", torch.int32), int(cu_new.numel()) - 1, n_tok,
+            _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream)))
+
+    def draft(self, kv: KVCache, anchor, block_size, block_tokens, workspace, logits=None,
+              stream=None):
+        import torch
+        _check(self.lib.dflash_draft_block(
+            self.handle, ctypes.byref(kv.c), _dev_ptr(anchor, "anchor", torch.int32),
+            int(anchor.numel()), int(block_size), _dev_ptr(block_tokens, "block_tokens", torch.int32),
+            _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+    def device_error(self, stream=None) -> int:
+        code = ctypes.c_int32(0)
+        rc = self.lib.dflash_device_error(self.handle, _stream(stream), ctypes.byref(code))
+        if rc not in (0, -6):
+            _check(rc)
+        return int(code.value)
+
+    def profile_enable(self, on: bool = True):
+        _check(self.lib.dflash_profile_enable(self.handle, 1 if on else 0))
+
+    def profile_read(self, reset: bool = False):
+        ms = ctypes.c_double(0.0)
+        cnt = ctypes.c_int64(0)
+        _check(self.lib.dflash_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(cnt),
+                                            1 if reset else 0))
+        return ms.value, cnt.value
+
+
+def verify_greedy(block_tokens, target_logits, accept_len, out_tokens, workspace,
+                  target_argmax=None, stream=None):
+    """Greedy verification through dflash_verify_greedy.  block_tokens int32
+    [B][gamma]; target_logits [B][gamma][V] bf16 or fp32."""
+    import torch
+    lib = _abi.load()
+    if target_logits.dtype == torch.bfloat16:
+        dt = DFLASH_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = DFLASH_F32
+    else:
+        raise ValueError("target_logits must be bf16 or fp32")
+    B, gamma = block_tokens.shape
+    _check(lib.dflash_verify_greedy(
+        _dev_ptr(block_tokens, "block_tokens", torch.int32), _dev_ptr(target_logits, "target_logits"),
+        dt, int(B), int(gamma), int(target_logits.shape[-1]),
+        _dev_ptr(accept_len, "accept_len", torch.int32), _dev_ptr(out_tokens, "out_tokens", torch.int32),
+        _dev_ptr(target_argmax, "target_argmax", torch.int32), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

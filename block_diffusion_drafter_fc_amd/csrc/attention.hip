@@ -1,0 +1,327 @@
+// attention.hip -- block attention of the draft step.
+//
+// Every block query of sequence b sees the sequence's ctx_lens[b] cached
+// context keys and all gamma block keys, with no mask inside the block
+// (summary page, "Block Diffusion Makes Draft Cost Nearly Independent of Block
+// Length" and Figure 2; paper §4.1).  Query head h reads KV head
+// h / (Hq / Hkv).
+//
+// Split-context (flash-decode) layout: workgroup (s, kvh, b) owns one KV head
+// of one sequence and one slice of keys -- context slice s, or the block's
+// own keys for s == n_ctx_splits -- and writes an unnormalised partial
+// (running max in log2 units, sum of weights, weighted values) that
+// k_attn_combine merges in split order.
+//
+// bf16 kernel: one wave per query head of the KV group, the gamma (<= 16)
+// queries of that head form the N side of 16x16x32 MFMAs.  32 keys at a time
+// are staged in LDS (K row-major, V transposed).  Scores are computed as
+// S^T = K Q^T with the key rows of the two 16-row MFMA tiles interleaved so
+// that each lane ends up holding 8 consecutive keys of one query -- exactly the
+// B operand the P V product needs -- and the softmax max/sum runs over the 4
+// lanes of a query with two cross-lane shuffles.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DH>
+__global__ __launch_bounds__(512) void k_attn_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
+    const uint16_t* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
+    int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[32][DH + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][32 + 8];
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  const int G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int h = kvh * G + wave;
+  const int L = ctx_lens[b];
+  const bool blockpart = (s == n_ctx_splits);
+  int kbeg, kend;
+  if (blockpart) {
+    kbeg = 0;
+    kend = gamma;
+  } else {
+    kbeg = s * chunk;
+    kend = min(kbeg + chunk, L);
+  }
+  const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0
+  if (kend <= kbeg) {
+    if (lg == 0 && lr < gamma) {
+      part_ml[(prow + lr) * 2 + 0] = -INFINITY;
+      part_ml[(prow + lr) * 2 + 1] = 0.f;
+    }
+    return;
+  }
+
+  constexpr int NI = DH / 32;   // MFMA K steps over the head dimension
+  constexpr int ND = DH / 16;   // 16-row tiles of the head dimension
+  u32x4 qop[NI];
+  {
+    const int row = b * gamma + (lr < gamma ? lr : 0);
+    const uint16_t* qp = q + ((size_t)row * Hq + h) * DH + lg * 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) qop[i] = lr < gamma ? ld16(qp + i * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x4 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  const int ra = 8 * (lr >> 2) + (lr & 3), rb = ra + 4;
+  const size_t head_stride = (size_t)16 * DH;            // one page of one head
+  const size_t kv_stride = (size_t)Hkv * head_stride;     // K part -> V part
+
+  for (int t0 = kbeg; t0 < kend; t0 += 32) {
+    for (int c = threadIdx.x; c < 32 * (DH / 8); c += blockDim.x) {
+      const int kr = c / (DH / 8), d8 = (c % (DH / 8)) * 8;
+      const int key = t0 + kr;
+      u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < kend) {
+        if (!blockpart) {
+          const int pi = key >> 4;
+          const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
+          if (pg >= 0 && pg < n_pages) {
+            const uint16_t* base = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
+                                   (size_t)(key & 15) * DH + d8;
+            vk = ld16(base);
+            vv = ld16(base + kv_stride);
+          } else if (d8 == 0) {
+            set_dev_error(err, pi < max_pages ? 1u : 2u);
+          }
+        } else {
+          const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * DH + d8;
+          vk = ld16(kb + off);
+          vv = ld16(vb + off);
+        }
+      }
+      st16(&Ks[kr][d8], vk);
+      const uint16_t* ve = (const uint16_t*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[d8 + e][kr] = ve[e];
+    }
+    __syncthreads();
+
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      sa = mfma_16x16x32(ld16(&Ks[ra][i * 32 + lg * 8]), qop[i], sa);
+      sb = mfma_16x16x32(ld16(&Ks[rb][i * 32 + lg * 8]), qop[i], sb);
+    }
+    // lane (query lr, group lg) now holds keys t0 + 8*lg + 0..7
+    float sv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = sa[r] * sl2;
+      sv[4 + r] = sb[r] * sl2;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (t0 + 8 * lg + e >= kend) sv[e] = -INFINITY;
+    float mt = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    uint16_t pb[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[e] = f2bf(exp2f(sv[e] - m_new));
+      psum += bf2f(pb[e]);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 pop;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pop[e] = (uint32_t)pb[2 * e] | ((uint32_t)pb[2 * e + 1] << 16);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      o[d] *= alpha;
+      o[d] = mfma_16x16x32(ld16(&Vt[d * 16 + lr][lg * 8]), pop, o[d]);
+    }
+    __syncthreads();
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lr < gamma) {
+    float* po = part_o + (prow + lr) * DH;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) po[d * 16 + 4 * lg + r] = o[d][r];
+    if (lg == 0) {
+      part_ml[(prow + lr) * 2 + 0] = m_run;
+      part_ml[(prow + lr) * 2 + 1] = l_run;
+    }
+  }
+}
+
+// fp32 models: one workgroup per (query, head, sequence) over all keys, in
+// chunks of 256 with an online softmax; writes the same partial layout as a
+// single split.
+__global__ __launch_bounds__(256) void k_attn_f32(
+    const float* __restrict__ q, const float* __restrict__ kb, const float* __restrict__ vb,
+    const float* __restrict__ pages, int n_pages, const int32_t* __restrict__ page_table,
+    int max_pages, int page_size, const int32_t* __restrict__ ctx_lens, int gamma, int Hq,
+    int Hkv, int dh, int layer, float* __restrict__ part_o, float* __restrict__ part_ml,
+    uint32_t* err) {
+  __shared__ float qs[256];
+  __shared__ float ps[256];
+  __shared__ const float* vrow[256];
+  __shared__ float red[16];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  const int kvh = h / (Hq / Hkv), tid = threadIdx.x;
+  const int L = ctx_lens[b], total = L + gamma;
+  const size_t qrow = (size_t)(b * gamma + j);
+  if (tid < dh) qs[tid] = q[(qrow * Hq + h) * dh + tid];
+  __syncthreads();
+  const float sl2 = kLog2e / sqrtf((float)dh);
+  float m_run = -INFINITY, l_run = 0.f, o_acc = 0.f;
+  const size_t head_stride = (size_t)page_size * dh, kv_stride = (size_t)Hkv * head_stride;
+  for (int c0 = 0; c0 < total; c0 += 256) {
+    const int key = c0 + tid;
+    float sc = -INFINITY;
+    const float* kp = nullptr;
+    const float* vp = nullptr;
+    if (key < total) {
+      if (key < L) {
+        const int pi = key / page_size;
+        const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
+        if (pg >= 0 && pg < n_pages) {
+          kp = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
+               (size_t)(key % page_size) * dh;
+          vp = kp + kv_stride;
+        } else {
+          set_dev_error(err, pi < max_pages ? 1u : 2u);
+        }
+      } else {
+        kp = kb + ((size_t)(b * gamma + key - L) * Hkv + kvh) * dh;
+        vp = vb + ((size_t)(b * gamma + key - L) * Hkv + kvh) * dh;
+      }
+      if (kp) {
+        float acc = 0.f;
+        for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kp[d], acc);
+        sc = acc * sl2;
+      }
+    }
+    vrow[tid] = vp;
+    // chunk maximum
+    float mx = sc;
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) mx = fmaxf(mx, red[i]);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float p = (sc == -INFINITY) ? 0.f : exp2f(sc - m_new);
+    ps[tid] = p;
+    const float psum = block_sum(p, red);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    __syncthreads();
+    if (tid < dh) {
+      float acc = o_acc * alpha;
+      const int n = min(256, total - c0);
+      for (int t = 0; t < n; ++t)
+        if (ps[t] != 0.f) acc = fmaf(ps[t], vrow[t][tid], acc);
+      o_acc = acc;
+    }
+    __syncthreads();
+  }
+  const size_t prow = ((size_t)b * Hq + h) * gamma + j;   // split 0
+  (void)B;
+  if (tid < dh) part_o[prow * dh + tid] = o_acc;
+  if (tid == 0) {
+    part_ml[prow * 2 + 0] = m_run;
+    part_ml[prow * 2 + 1] = l_run;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      int n_parts, int gamma, int Hq, int dh,
+                                                      typename Act<BF16>::T* __restrict__ o) {
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z, d = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < n_parts; ++s) {
+    const size_t pr = ((size_t)(s * B + b) * Hq + h) * gamma + j;
+    if (part_ml[pr * 2 + 1] > 0.f) M = fmaxf(M, part_ml[pr * 2]);
+  }
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < n_parts; ++s) {
+    const size_t pr = ((size_t)(s * B + b) * Hq + h) * gamma + j;
+    const float l = part_ml[pr * 2 + 1];
+    if (!(l > 0.f)) continue;
+    const float wgt = exp2f(part_ml[pr * 2] - M);
+    den += wgt * l;
+    if (d < dh) num += wgt * part_o[pr * dh + d];
+  }
+  if (d < dh) {
+    const float v = den > 0.f ? num / den : 0.f;
+    Act<BF16>::store(o, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
+  }
+}
+
+}  // namespace
+
+AttnPlan plan_attention(int batch, int n_kv_heads, int max_pages, int page_size) {
+  AttnPlan p;
+  const long cap = (long)max_pages * page_size;
+  long chunk = (cap * batch * n_kv_heads + 1023) / 1024;
+  chunk = ((chunk + 31) / 32) * 32;
+  if (chunk < 64) chunk = 64;
+  p.chunk = (int)chunk;
+  p.n_ctx_splits = (int)((cap + chunk - 1) / chunk);
+  if (p.n_ctx_splits < 1) p.n_ctx_splits = 1;
+  return p;
+}
+
+hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+  if (!bf16) {
+    dim3 grid(a.gamma, a.Hq, a.batch);
+    hipLaunchKernelGGL(k_attn_f32, grid, dim3(256), 0, st, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (const float*)a.pages, a.n_pages, a.page_table,
+                       a.max_pages, a.page_size, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.dh, a.layer,
+                       a.part_o, a.part_ml, a.err);
+    return hipGetLastError();
+  }
+  dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
+  dim3 block(64 * (a.Hq / a.Hkv));
+  if (a.dh == 128) {
+    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.pages,
+                       a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
+                       a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+  } else if (a.dh == 64) {
+    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.pages,
+                       a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
+                       a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
+                               int batch, int gamma, int Hq, int dh, void* o, hipStream_t st) {
+  dim3 grid(gamma, Hq, batch);
+  dim3 block(dh < 64 ? 64 : dh);
+  if (bf16)
+    hipLaunchKernelGGL(k_attn_combine<true>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
+                       Hq, dh, (uint16_t*)o);
+  else
+    hipLaunchKernelGGL(k_attn_combine<false>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
+                       Hq, dh, (float*)o);
+  return hipGetLastError();
+}

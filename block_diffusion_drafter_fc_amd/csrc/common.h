@@ -1,0 +1,96 @@
+// common.h -- device helpers shared by the gfx950 kernels of the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define DF_DEV __device__ __forceinline__
+
+DF_DEV float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+DF_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Round an fp32 value to the nearest bf16 value, kept in fp32.
+DF_DEV float round_bf(float f) { return bf2f(f2bf(f)); }
+
+// Activation storage: bf16 bits (BF16 = true) or fp32.
+template <bool BF16> struct Act;
+template <> struct Act<true> {
+  typedef uint16_t T;
+  static DF_DEV float load(const T* p, size_t i) { return bf2f(p[i]); }
+  static DF_DEV void store(T* p, size_t i, float v) { p[i] = f2bf(v); }
+  static DF_DEV float rnd(float v) { return round_bf(v); }
+};
+template <> struct Act<false> {
+  typedef float T;
+  static DF_DEV float load(const T* p, size_t i) { return p[i]; }
+  static DF_DEV void store(T* p, size_t i, float v) { p[i] = v; }
+  static DF_DEV float rnd(float v) { return v; }
+};
+
+// D = A * B + C for one 16x16x32 bf16 MFMA tile.  Lane l (r = l % 16,
+// g = l / 16) supplies A[r][8g..8g+7] and B[8g..8g+7][r]; it receives
+// D[4g + i][r], i = 0..3.
+DF_DEV f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+DF_DEV u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+DF_DEV void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Order-preserving map of an fp32 value onto uint32 (finite inputs).
+DF_DEV uint32_t f32_order(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Argmax key: larger value wins; among equal values the lower index wins.
+DF_DEV uint64_t argmax_key(float v, uint32_t idx) {
+  return ((uint64_t)f32_order(v) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+DF_DEV uint32_t argmax_key_index(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu); }
+
+DF_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Block-wide sum over blockDim.x threads (blockDim.x a multiple of 64,
+// at most 1024).  `red` is shared scratch of >= 16 floats.  All threads get
+// the result.  The summation order is fixed.
+DF_DEV float block_sum(float v, float* red) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// Rotary angle pair for dimension pair i of a head of size dh at position
+// pos: (cos, sin) of pos * theta^(-2i/dh), evaluated in double.
+DF_DEV void rope_cs(int pos, int i, int dh, double theta, float* c, float* s) {
+  double inv = pow(theta, -2.0 * (double)i / (double)dh);
+  double phi = (double)pos * inv;
+  double sd, cd;
+  sincos(phi, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
+// Sticky device error word.
+DF_DEV void set_dev_error(uint32_t* word, uint32_t bit) { atomicOr(word, bit); }

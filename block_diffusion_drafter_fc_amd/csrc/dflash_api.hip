@@ -1,0 +1,459 @@
+// dflash_api.hip -- the C ABI declared in include/dflash.h: argument checks,
+// workspace layout and the launch sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+struct dflash_model {
+  dflash_config cfg;
+  dflash_weights w;
+  uint32_t* err;   // device error word (in the caller's state buffer)
+  int device;
+  bool bf16;
+  bool prof_on;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending, pool;
+  double prof_ms;
+  int64_t prof_count;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(DFLASH_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+  int D, QD, KVD, I, V, NL, Hq, Hkv, dh, F;
+};
+Dims dims_of(const dflash_config& c) {
+  Dims d;
+  d.D = c.hidden;
+  d.Hq = c.n_q_heads;
+  d.Hkv = c.n_kv_heads;
+  d.dh = c.head_dim;
+  d.QD = c.n_q_heads * c.head_dim;
+  d.KVD = c.n_kv_heads * c.head_dim;
+  d.I = c.intermediate;
+  d.V = c.vocab;
+  d.NL = c.n_layers;
+  d.F = c.n_target_feats * c.hidden;
+  return d;
+}
+
+size_t part_floats(bool bf16, int M, int N, int K) {
+  const GemmPlan p = plan_gemm(bf16, M, N, K, false);
+  return (size_t)p.splits * M * N;
+}
+
+struct DraftLayout {
+  size_t x, y, q, k, v, o, h, part, att_o, att_ml, best, total;
+  AttnPlan ap;
+  int parts;
+};
+
+DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages) {
+  const Dims d = dims_of(m->cfg);
+  const bool bf = m->bf16;
+  const size_t ab = bf ? 2 : 4;
+  const size_t M = (size_t)B * gamma;
+  DraftLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.x = take(M * d.D * 4);
+  L.y = take(M * d.D * ab);
+  L.q = take(M * d.QD * ab);
+  L.k = take(M * d.KVD * ab);
+  L.v = take(M * d.KVD * ab);
+  L.o = take(M * d.QD * ab);
+  L.h = take(M * d.I * ab);
+  size_t pf = part_floats(bf, (int)M, d.QD + 2 * d.KVD, d.D);
+  pf = std::max(pf, part_floats(bf, (int)M, d.D, d.QD));
+  pf = std::max(pf, part_floats(bf, (int)M, 2 * d.I, d.D));
+  pf = std::max(pf, part_floats(bf, (int)M, d.D, d.I));
+  L.part = take(pf * 4);
+  L.ap = plan_attention(B, d.Hkv, max_pages, m->cfg.page_size);
+  L.parts = bf ? L.ap.n_ctx_splits + 1 : 1;
+  L.att_o = take((size_t)L.parts * M * d.Hq * d.dh * 4);
+  L.att_ml = take((size_t)L.parts * M * d.Hq * 2 * 4);
+  L.best = take(M * 8);
+  L.total = off;
+  return L;
+}
+
+struct InjectLayout {
+  size_t part, c, total;
+};
+
+InjectLayout inject_layout(const dflash_model* m, int n_tok) {
+  const Dims d = dims_of(m->cfg);
+  const bool bf = m->bf16;
+  InjectLayout L{};
+  size_t pf = part_floats(bf, n_tok, d.D, d.F);
+  pf = std::max(pf, part_floats(bf, n_tok, 2 * d.NL * d.KVD, d.D));
+  size_t off = 0;
+  L.part = off;
+  off = align256(pf * 4);
+  L.c = off;
+  off = align256(off + (size_t)n_tok * d.D * (bf ? 2 : 4));
+  L.total = off;
+  return L;
+}
+
+int check_config(const dflash_config* c) {
+  if (c->hidden <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->intermediate <= 0 || c->vocab <= 1 || c->n_target_feats <= 0)
+    return fail(DFLASH_E_INVAL, "config: all dimensions must be positive (vocab >= 2)");
+  if (c->n_layers > DFLASH_MAX_LAYERS)
+    return fail(DFLASH_E_SHAPE, "config: n_layers %d > %d", c->n_layers, DFLASH_MAX_LAYERS);
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16)
+    return fail(DFLASH_E_DTYPE, "config: unknown dtype %d", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(DFLASH_E_SHAPE, "config: head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 8)
+    return fail(DFLASH_E_SHAPE, "config: n_q_heads must be a multiple of n_kv_heads, ratio <= 8");
+  if (c->max_block < 1 || c->max_block > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_E_SHAPE, "config: max_block must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (c->page_size != 16) return fail(DFLASH_E_SHAPE, "config: page_size must be 16");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return fail(DFLASH_E_INVAL, "config: mask_token_id outside [0, vocab)");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f))
+    return fail(DFLASH_E_INVAL, "config: rope_theta must be > 0 and rms_eps >= 0");
+  if (c->n_layers * 2 > WSEG_MAX) return fail(DFLASH_E_SHAPE, "config: too many layers");
+  if (c->dtype == DFLASH_BF16) {
+    const int qd = c->n_q_heads * c->head_dim;
+    if (c->hidden % 256 || c->intermediate % 256 || qd % 256)
+      return fail(DFLASH_E_SHAPE,
+                  "config: bf16 kernels need hidden, intermediate and n_q_heads*head_dim to be "
+                  "multiples of 256");
+  } else {
+    if (c->head_dim > 256) return fail(DFLASH_E_SHAPE, "config: head_dim too large");
+  }
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void* state,
+                        dflash_model** out) {
+  if (!cfg || !w || !state || !out) return fail(DFLASH_E_INVAL, "model_create: null argument");
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w->fc_w || !w->fc_norm || !w->embed || !w->lm_head || !w->final_norm)
+    return fail(DFLASH_E_INVAL, "model_create: null global weight pointer");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dflash_layer_weights& L = w->layer[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.mlp_norm || !L.w_gate || !L.w_up ||
+        !L.w_down)
+      return fail(DFLASH_E_INVAL, "model_create: null weight pointer in layer %d", l);
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipMemset(state, 0, DFLASH_STATE_BYTES));
+  dflash_model* m = new dflash_model();
+  m->cfg = *cfg;
+  m->w = *w;
+  m->err = (uint32_t*)state;
+  m->device = dev;
+  m->bf16 = cfg->dtype == DFLASH_BF16;
+  m->prof_on = false;
+  m->prof_ms = 0.0;
+  m->prof_count = 0;
+  *out = m;
+  return DFLASH_OK;
+}
+
+void dflash_model_destroy(dflash_model* m) {
+  if (!m) return;
+  for (auto& p : m->pending) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  for (auto& p : m->pool) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  delete m;
+}
+
+size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_block,
+                              int32_t max_new_tokens, int32_t max_pages_per_seq) {
+  if (!m || max_batch < 1 || max_block < 1 || max_block > m->cfg.max_block ||
+      max_new_tokens < 0 || max_pages_per_seq < 1)
+    return 0;
+  size_t need = 0;
+  for (int b = 1; b <= max_batch; ++b)
+    for (int g = 1; g <= max_block; ++g)
+      need = std::max(need, draft_layout(m, b, g, max_pages_per_seq).total);
+  for (int n = 1; n <= max_new_tokens; ++n) need = std::max(need, inject_layout(m, n).total);
+  need = std::max(need, align256((size_t)max_batch * max_block * 8));
+  return need;
+}
+
+int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hidden,
+                      const int32_t* cu_new, int32_t batch, int32_t n_tok, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (!m || !kv || !cu_new) return fail(DFLASH_E_INVAL, "inject_ctx: null argument");
+  if (!kv->pages || !kv->page_table || !kv->ctx_lens)
+    return fail(DFLASH_E_INVAL, "inject_ctx: null pointer in the KV cache description");
+  if (batch < 1) return fail(DFLASH_E_INVAL, "inject_ctx: batch must be >= 1");
+  if (n_tok < 0) return fail(DFLASH_E_INVAL, "inject_ctx: n_tok must be >= 0");
+  if (kv->n_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(DFLASH_E_INVAL, "inject_ctx: empty page pool or page table");
+  if (n_tok == 0) return DFLASH_OK;
+  if (!hidden || !workspace) return fail(DFLASH_E_INVAL, "inject_ctx: null hidden or workspace");
+  const InjectLayout L = inject_layout(m, n_tok);
+  if (L.total > ws_bytes)
+    return fail(DFLASH_E_CAPACITY, "inject_ctx: workspace %zu bytes < %zu needed", ws_bytes,
+                L.total);
+  const Dims d = dims_of(m->cfg);
+  const bool bf = m->bf16;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* part = (float*)(ws + L.part);
+  void* c = ws + L.c;
+
+  WSeg fc{};
+  fc.ptr[0] = m->w.fc_w;
+  fc.row_end[0] = d.D;
+  fc.n = 1;
+  GemmPlan p = plan_gemm(bf, n_tok, d.D, d.F, false);
+  HIPCHK(launch_gemm(p, bf, hidden, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
+  HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c, st));
+
+  WSeg kvw{};
+  for (int l = 0; l < d.NL; ++l) {
+    kvw.ptr[2 * l] = m->w.layer[l].wk;
+    kvw.ptr[2 * l + 1] = m->w.layer[l].wv;
+    kvw.row_end[2 * l] = (2 * l + 1) * d.KVD;
+    kvw.row_end[2 * l + 1] = (2 * l + 2) * d.KVD;
+  }
+  kvw.n = 2 * d.NL;
+  const int Nkv = 2 * d.NL * d.KVD;
+  p = plan_gemm(bf, n_tok, Nkv, d.D, false);
+  HIPCHK(launch_gemm(p, bf, c, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
+  HIPCHK(launch_inject_scatter(bf, part, p.splits, n_tok, cu_new, batch, kv->ctx_lens,
+                               kv->page_table, kv->max_pages_per_seq, kv->n_pages,
+                               m->cfg.page_size, kv->pages, d.NL, d.Hkv, d.dh,
+                               m->cfg.rope_theta, m->err, st));
+  HIPCHK(launch_advance_ctx(kv->ctx_lens, cu_new, batch, st));
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_t* anchor,
+                       int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  dflash_model* m = const_cast<dflash_model*>(mc);
+  if (!m || !kv || !anchor || !block_tokens || !workspace)
+    return fail(DFLASH_E_INVAL, "draft_block: null argument");
+  if (!kv->pages || !kv->page_table || !kv->ctx_lens)
+    return fail(DFLASH_E_INVAL, "draft_block: null pointer in the KV cache description");
+  if (batch < 1) return fail(DFLASH_E_INVAL, "draft_block: batch must be >= 1");
+  if (gamma < 1 || gamma > m->cfg.max_block)
+    return fail(DFLASH_E_CAPACITY, "draft_block: block_size %d outside [1, %d]", gamma,
+                m->cfg.max_block);
+  if (kv->n_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(DFLASH_E_INVAL, "draft_block: empty page pool or page table");
+  const DraftLayout L = draft_layout(m, batch, gamma, kv->max_pages_per_seq);
+  if (L.total > ws_bytes)
+    return fail(DFLASH_E_CAPACITY, "draft_block: workspace %zu bytes < %zu needed", ws_bytes,
+                L.total);
+  const Dims d = dims_of(m->cfg);
+  const bool bf = m->bf16;
+  const float eps = m->cfg.rms_eps;
+  const int M = batch * gamma;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* x = (float*)(ws + L.x);
+  void *y = ws + L.y, *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *o = ws + L.o, *h = ws + L.h;
+  float* part = (float*)(ws + L.part);
+  float* att_o = (float*)(ws + L.att_o);
+  float* att_ml = (float*)(ws + L.att_ml);
+  uint64_t* best = (uint64_t*)(ws + L.best);
+
+  HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
+                      best, m->err, st));
+  HIPCHK(launch_rmsnorm(bf, x, M, d.D, m->w.layer[0].attn_norm, eps, y, st));
+  for (int l = 0; l < d.NL; ++l) {
+    const dflash_layer_weights& W = m->w.layer[l];
+    WSeg qkv{};
+    qkv.ptr[0] = W.wq;
+    qkv.ptr[1] = W.wk;
+    qkv.ptr[2] = W.wv;
+    qkv.row_end[0] = d.QD;
+    qkv.row_end[1] = d.QD + d.KVD;
+    qkv.row_end[2] = d.QD + 2 * d.KVD;
+    qkv.n = 3;
+    const int Nqkv = d.QD + 2 * d.KVD;
+    GemmPlan p = plan_gemm(bf, M, Nqkv, d.D, false);
+    HIPCHK(launch_gemm(p, bf, y, d.D, M, qkv, Nqkv, d.D, part, nullptr, nullptr, st));
+    HIPCHK(launch_qkv_epilogue(bf, part, p.splits, M, gamma, d.Hq, d.Hkv, d.dh, kv->ctx_lens,
+                               m->cfg.rope_theta, q, k, v, st));
+    AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.pages = kv->pages;
+    a.n_pages = kv->n_pages;
+    a.max_pages = kv->max_pages_per_seq;
+    a.page_size = m->cfg.page_size;
+    a.page_table = kv->page_table;
+    a.ctx_lens = kv->ctx_lens;
+    a.batch = batch;
+    a.gamma = gamma;
+    a.Hq = d.Hq;
+    a.Hkv = d.Hkv;
+    a.dh = d.dh;
+    a.layer = l;
+    a.part_o = att_o;
+    a.part_ml = att_ml;
+    a.err = m->err;
+    HIPCHK(launch_attention(bf, a, L.ap, st));
+    HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, st));
+
+    WSeg wo{};
+    wo.ptr[0] = W.wo;
+    wo.row_end[0] = d.D;
+    wo.n = 1;
+    p = plan_gemm(bf, M, d.D, d.QD, false);
+    HIPCHK(launch_gemm(p, bf, o, d.QD, M, wo, d.D, d.QD, part, nullptr, nullptr, st));
+    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, W.mlp_norm, eps, y, st));
+
+    WSeg gu{};
+    gu.ptr[0] = W.w_gate;
+    gu.ptr[1] = W.w_up;
+    gu.row_end[0] = d.I;
+    gu.row_end[1] = 2 * d.I;
+    gu.n = 2;
+    p = plan_gemm(bf, M, 2 * d.I, d.D, false);
+    HIPCHK(launch_gemm(p, bf, y, d.D, M, gu, 2 * d.I, d.D, part, nullptr, nullptr, st));
+    HIPCHK(launch_swiglu(bf, part, p.splits, M, d.I, h, st));
+
+    WSeg dn{};
+    dn.ptr[0] = W.w_down;
+    dn.row_end[0] = d.D;
+    dn.n = 1;
+    p = plan_gemm(bf, M, d.D, d.I, false);
+    HIPCHK(launch_gemm(p, bf, h, d.I, M, dn, d.D, d.I, part, nullptr, nullptr, st));
+    const void* g_next = l + 1 < d.NL ? m->w.layer[l + 1].attn_norm : m->w.final_norm;
+    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, g_next, eps, y, st));
+  }
+
+  WSeg lm{};
+  lm.ptr[0] = m->w.lm_head;
+  lm.row_end[0] = d.V;
+  lm.n = 1;
+  const GemmPlan p = plan_gemm(bf, M, d.V, d.D, true);
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (m->prof_on) {
+    if (!m->pool.empty()) {
+      ev = m->pool.back();
+      m->pool.pop_back();
+    } else {
+      HIPCHK(hipEventCreate(&ev.first));
+      HIPCHK(hipEventCreate(&ev.second));
+    }
+    HIPCHK(hipEventRecord(ev.first, st));
+  }
+  HIPCHK(launch_gemm(p, bf, y, d.D, M, lm, d.V, d.D, nullptr, best, logits, st));
+  if (m->prof_on) {
+    HIPCHK(hipEventRecord(ev.second, st));
+    m->pending.push_back(ev);
+  }
+  HIPCHK(launch_argmax_finalize(best, anchor, batch, gamma, block_tokens, st));
+  return DFLASH_OK;
+}
+
+int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
+                         int32_t logits_dtype, int32_t batch, int32_t gamma, int32_t vocab,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* target_argmax,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!block_tokens || !target_logits || !accept_len || !out_tokens || !workspace)
+    return fail(DFLASH_E_INVAL, "verify_greedy: null argument");
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
+    return fail(DFLASH_E_DTYPE, "verify_greedy: unknown logits dtype %d", logits_dtype);
+  if (batch < 1 || gamma < 1 || vocab < 1)
+    return fail(DFLASH_E_INVAL, "verify_greedy: batch, block_size and vocab must be >= 1");
+  const size_t need = (size_t)batch * gamma * 8;
+  if (ws_bytes < need)
+    return fail(DFLASH_E_CAPACITY, "verify_greedy: workspace %zu bytes < %zu needed", ws_bytes,
+                need);
+  HIPCHK(launch_verify(logits_dtype == DFLASH_BF16, block_tokens, target_logits, batch, gamma,
+                       vocab, (uint64_t*)workspace, accept_len, out_tokens, target_argmax,
+                       (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+int dflash_device_error(const dflash_model* m, void* stream, int32_t* code) {
+  if (!m || !code) return fail(DFLASH_E_INVAL, "device_error: null argument");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(hipStreamSynchronize(st));
+  uint32_t v = 0;
+  HIPCHK(hipMemcpy(&v, m->err, sizeof v, hipMemcpyDeviceToHost));
+  *code = (int32_t)v;
+  if (v) {
+    HIPCHK(launch_clear_word(m->err, st));
+    HIPCHK(hipStreamSynchronize(st));
+    return fail(DFLASH_E_DEVICE, "device error word 0x%x", v);
+  }
+  return DFLASH_OK;
+}
+
+int dflash_profile_enable(dflash_model* m, int32_t on) {
+  if (!m) return fail(DFLASH_E_INVAL, "profile_enable: null model");
+  m->prof_on = on != 0;
+  return DFLASH_OK;
+}
+
+int dflash_profile_read(dflash_model* m, double* total_ms, int64_t* count, int32_t reset) {
+  if (!m || !total_ms || !count) return fail(DFLASH_E_INVAL, "profile_read: null argument");
+  for (auto& p : m->pending) {
+    HIPCHK(hipEventSynchronize(p.second));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, p.first, p.second));
+    m->prof_ms += ms;
+    m->prof_count += 1;
+    m->pool.push_back(p);
+  }
+  m->pending.clear();
+  *total_ms = m->prof_ms;
+  *count = m->prof_count;
+  if (reset) {
+    m->prof_ms = 0.0;
+    m->prof_count = 0;
+  }
+  return DFLASH_OK;
+}
+
+}  // extern "C"

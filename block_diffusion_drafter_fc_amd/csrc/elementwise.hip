@@ -1,0 +1,425 @@
+// elementwise.hip -- row and element kernels around the dense products:
+// embedding gather, RMSNorm, residual update, rotary embedding of q/k,
+// SwiGLU, the draft argmax finaliser, context-injection scatter into the
+// paged cache, and greedy verification.
+//
+// Split-K partial slices are always summed in slice order, so every result
+// is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kRowThreads = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict__ anchor,
+                                                       int gamma, int mask_id, int vocab,
+                                                       const typename Act<BF16>::T* __restrict__ E,
+                                                       int D, float* __restrict__ x,
+                                                       uint64_t* __restrict__ best,
+                                                       uint32_t* err) {
+  const int r = blockIdx.x, b = r / gamma, j = r % gamma;
+  int tok = j == 0 ? anchor[b] : mask_id;
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) set_dev_error(err, 4u);
+    tok = 0;
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    x[(size_t)r * D + d] = Act<BF16>::load(E, (size_t)tok * D + d);
+  if (threadIdx.x == 0) best[r] = 0;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict__ x, int D,
+                                                         const typename Act<BF16>::T* __restrict__ g,
+                                                         float eps, typename Act<BF16>::T* __restrict__ y) {
+  __shared__ float red[16];
+  const float* xr = x + (size_t)blockIdx.x * D;
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) ss = fmaf(xr[d], xr[d], ss);
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    Act<BF16>::store(y, (size_t)blockIdx.x * D + d, xr[d] * inv * Act<BF16>::load(g, d));
+}
+
+// x[r] += sum_s part[s][r]; then y[r] = RMSNorm(x[r]) * g (y optional).
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_residual_norm(float* __restrict__ x,
+                                                               const float* __restrict__ part,
+                                                               int splits, int M, int D,
+                                                               const typename Act<BF16>::T* __restrict__ g,
+                                                               float eps, typename Act<BF16>::T* __restrict__ y) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  float* xr = x + (size_t)r * D;
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float add = 0.f;
+    for (int s = 0; s < splits; ++s) add += part[((size_t)s * M + r) * D + d];
+    const float v = xr[d] + add;
+    xr[d] = v;
+    ss = fmaf(v, v, ss);
+  }
+  if (y == nullptr) return;
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    Act<BF16>::store(y, (size_t)r * D + d, xr[d] * inv * Act<BF16>::load(g, d));
+}
+
+// Sum the QKV partials, rotate q and k (rotate-half form) at position
+// ctx_lens[b] + j, store q [M][Hq][dh], k and v [M][Hkv][dh].
+template <bool BF16>
+__global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M, int gamma,
+                               int Hq, int Hkv, int dh, const int32_t* __restrict__ ctx_lens,
+                               float theta, typename Act<BF16>::T* __restrict__ q,
+                               typename Act<BF16>::T* __restrict__ k,
+                               typename Act<BF16>::T* __restrict__ v) {
+  const int r = blockIdx.x, hh = blockIdx.y, i = threadIdx.x, half = dh / 2;
+  const int N = (Hq + 2 * Hkv) * dh;
+  (void)M;
+  const int col = hh * dh + i;
+  float a = 0.f, c2 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    a += part[((size_t)s * M + r) * N + col];
+    c2 += part[((size_t)s * M + r) * N + col + half];
+  }
+  if (hh < Hq + Hkv) {
+    const int pos = ctx_lens[r / gamma] + r % gamma;
+    float cs, sn;
+    rope_cs(pos, i, dh, (double)theta, &cs, &sn);
+    const float a2 = a * cs - c2 * sn, b2 = c2 * cs + a * sn;
+    a = a2;
+    c2 = b2;
+  }
+  typename Act<BF16>::T* dst;
+  size_t base;
+  if (hh < Hq) {
+    dst = q;
+    base = ((size_t)r * Hq + hh) * dh;
+  } else if (hh < Hq + Hkv) {
+    dst = k;
+    base = ((size_t)r * Hkv + (hh - Hq)) * dh;
+  } else {
+    dst = v;
+    base = ((size_t)r * Hkv + (hh - Hq - Hkv)) * dh;
+  }
+  Act<BF16>::store(dst, base + i, a);
+  Act<BF16>::store(dst, base + i + half, c2);
+}
+
+// h = silu(gate) * up, gate = columns [0, I), up = columns [I, 2I).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, int splits, int M,
+                                                int I, typename Act<BF16>::T* __restrict__ h) {
+  const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= I) return;
+  float gt = 0.f, up = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * M + r) * (2 * (size_t)I);
+    gt += p[c];
+    up += p[I + c];
+  }
+  const float sg = gt / (1.0f + expf(-gt));
+  Act<BF16>::store(h, (size_t)r * I + c, sg * up);
+}
+
+__global__ void k_argmax_finalize(const uint64_t* __restrict__ best,
+                                  const int32_t* __restrict__ anchor, int M, int gamma,
+                                  int32_t* __restrict__ block_tokens) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= M) return;
+  const int j = r % gamma;
+  block_tokens[r] = j == 0 ? anchor[r / gamma] : (int32_t)argmax_key_index(best[r]);
+}
+
+// c = RMSNorm(sum_s part[s]) * g   (the fused context H_t of each new token)
+template <bool BF16>
+__global__ __launch_bounds__(kRowThreads) void k_inject_norm(const float* __restrict__ part,
+                                                             int splits, int n, int D,
+                                                             const typename Act<BF16>::T* __restrict__ g,
+                                                             float eps, typename Act<BF16>::T* __restrict__ c) {
+  __shared__ float red[16];
+  extern __shared__ float row[];
+  const int t = blockIdx.x;
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float u = 0.f;
+    for (int s = 0; s < splits; ++s) u += part[((size_t)s * n + t) * D + d];
+    row[d] = u;
+    ss = fmaf(u, u, ss);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    Act<BF16>::store(c, (size_t)t * D + d, row[d] * inv * Act<BF16>::load(g, d));
+}
+
+// Token t of the inject batch belongs to sequence b with cu_new[b] <= t <
+// cu_new[b+1]; its position is ctx_lens[b] + (t - cu_new[b]).  Columns of
+// the partial product are [K^0 | V^0 | K^1 | V^1 | ...], each Hkv*dh wide.
+template <bool BF16>
+__global__ void k_inject_scatter(const float* __restrict__ part, int splits, int n_tok,
+                                 const int32_t* __restrict__ cu_new, int batch,
+                                 const int32_t* __restrict__ ctx_lens,
+                                 const int32_t* __restrict__ page_table, int max_pages,
+                                 int n_pages, int page_size, typename Act<BF16>::T* __restrict__ pages,
+                                 int n_layers, int Hkv, int dh, float theta, uint32_t* err) {
+  const int t = blockIdx.x, y = blockIdx.y, i = threadIdx.x, half = dh / 2;
+  const int kvh = y % Hkv, kv = (y / Hkv) % 2, layer = y / (2 * Hkv);
+  int lo = 0, hi = batch;   // find b with cu_new[b] <= t < cu_new[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cu_new[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int pos = ctx_lens[b] + (t - cu_new[b]);
+  const int pi = pos / page_size;
+  if (pos < 0 || pi >= max_pages) {
+    if (i == 0) set_dev_error(err, 2u);
+    return;
+  }
+  const int pg = page_table[(size_t)b * max_pages + pi];
+  if (pg < 0 || pg >= n_pages) {
+    if (i == 0) set_dev_error(err, 1u);
+    return;
+  }
+  const size_t N = (size_t)n_layers * 2 * Hkv * dh;
+  const size_t col = (size_t)y * dh + i;
+  float a = 0.f, c2 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    a += part[((size_t)s * n_tok + t) * N + col];
+    c2 += part[((size_t)s * n_tok + t) * N + col + half];
+  }
+  if (kv == 0) {
+    float cs, sn;
+    rope_cs(pos, i, dh, (double)theta, &cs, &sn);
+    const float a2 = a * cs - c2 * sn, b2 = c2 * cs + a * sn;
+    a = a2;
+    c2 = b2;
+  }
+  const size_t dst = ((((size_t)layer * n_pages + pg) * 2 + kv) * Hkv + kvh) * page_size * dh +
+                     (size_t)(pos % page_size) * dh;
+  Act<BF16>::store(pages, dst + i, a);
+  Act<BF16>::store(pages, dst + i + half, c2);
+}
+
+__global__ void k_advance_ctx(int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_new,
+                              int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) ctx_lens[b] += cu_new[b + 1] - cu_new[b];
+}
+
+__global__ void k_zero_u64(uint64_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void k_clear_word(uint32_t* w) { *w = 0u; }
+
+// Row argmax of the target scores: workgroup (chunk, row) scans `chunk`
+// columns with 16-byte loads and merges its key into best[row].
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_verify_argmax(const void* __restrict__ target, int vocab,
+                                                       int chunk, uint64_t* __restrict__ best) {
+  __shared__ uint64_t redk[4];
+  const int row = blockIdx.y;
+  const int c0 = blockIdx.x * chunk, c1 = min(vocab, c0 + chunk);
+  uint64_t key = 0;
+  if (BF16) {
+    const uint16_t* p = (const uint16_t*)target + (size_t)row * vocab;
+    if ((vocab & 7) == 0) {
+      for (int c = c0 + threadIdx.x * 8; c < c1; c += blockDim.x * 8) {
+        const u32x4 v = ld16(p + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t k0 = argmax_key(bf2f((uint16_t)(v[e] & 0xFFFFu)), (uint32_t)(c + 2 * e));
+          const uint64_t k1 = argmax_key(bf2f((uint16_t)(v[e] >> 16)), (uint32_t)(c + 2 * e + 1));
+          key = k0 > key ? k0 : key;
+          key = k1 > key ? k1 : key;
+        }
+      }
+    } else {
+      for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
+        const uint64_t k0 = argmax_key(bf2f(p[c]), (uint32_t)c);
+        key = k0 > key ? k0 : key;
+      }
+    }
+  } else {
+    const float* p = (const float*)target + (size_t)row * vocab;
+    if ((vocab & 3) == 0) {
+      for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4) {
+        const u32x4 v = ld16(p + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t k0 = argmax_key(__uint_as_float(v[e]), (uint32_t)(c + e));
+          key = k0 > key ? k0 : key;
+        }
+      }
+    } else {
+      for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
+        const uint64_t k0 = argmax_key(p[c], (uint32_t)c);
+        key = k0 > key ? k0 : key;
+      }
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(key, m);
+    key = o > key ? o : key;
+  }
+  if ((threadIdx.x & 63) == 0) redk[threadIdx.x >> 6] = key;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) key = redk[w] > key ? redk[w] : key;
+    atomicMax((unsigned long long*)&best[row], (unsigned long long)key);
+  }
+}
+
+// tau = n + 1 with n the longest prefix where block[j] == T_{j-1}.
+__global__ void k_verify_finalize(const uint64_t* __restrict__ best,
+                                  const int32_t* __restrict__ block_tokens, int batch, int gamma,
+                                  int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+                                  int32_t* __restrict__ target_argmax) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int32_t* blk = block_tokens + (size_t)b * gamma;
+  const uint64_t* bk = best + (size_t)b * gamma;
+  int n = 0;
+  while (n < gamma - 1 && blk[n + 1] == (int32_t)argmax_key_index(bk[n])) ++n;
+  accept_len[b] = n + 1;
+  int32_t* out = out_tokens + (size_t)b * gamma;
+  for (int j = 0; j < gamma; ++j) {
+    const int32_t T = (int32_t)argmax_key_index(bk[j]);
+    out[j] = j < n ? blk[j + 1] : (j == n ? T : -1);
+    if (target_argmax) target_argmax[(size_t)b * gamma + j] = T;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
+                        int vocab, const void* embed, int D, float* x, uint64_t* best,
+                        uint32_t* err, hipStream_t st) {
+  dim3 grid(batch * gamma);
+  if (bf16)
+    hipLaunchKernelGGL(k_embed<true>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
+                       vocab, (const uint16_t*)embed, D, x, best, err);
+  else
+    hipLaunchKernelGGL(k_embed<false>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
+                       vocab, (const float*)embed, D, x, best, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(bool bf16, const float* x, int M, int D, const void* g, float eps,
+                          void* y, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_rmsnorm<true>, dim3(M), dim3(kRowThreads), 0, st, x, D,
+                       (const uint16_t*)g, eps, (uint16_t*)y);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<false>, dim3(M), dim3(kRowThreads), 0, st, x, D,
+                       (const float*)g, eps, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int splits, int M, int D,
+                                const void* g, float eps, void* y, hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL(k_residual_norm<true>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
+                       M, D, (const uint16_t*)g, eps, (uint16_t*)y);
+  else
+    hipLaunchKernelGGL(k_residual_norm<false>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
+                       M, D, (const float*)g, eps, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int gamma, int Hq,
+                               int Hkv, int dh, const int32_t* ctx_lens, float theta, void* q,
+                               void* k, void* v, hipStream_t st) {
+  dim3 grid(M, Hq + 2 * Hkv);
+  dim3 block(dh / 2);
+  if (bf16)
+    hipLaunchKernelGGL(k_qkv_epilogue<true>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
+                       dh, ctx_lens, theta, (uint16_t*)q, (uint16_t*)k, (uint16_t*)v);
+  else
+    hipLaunchKernelGGL(k_qkv_epilogue<false>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
+                       dh, ctx_lens, theta, (float*)q, (float*)k, (float*)v);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
+                         hipStream_t st) {
+  dim3 grid((I + 255) / 256, M);
+  if (bf16)
+    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, st, part, splits, M, I, (uint16_t*)h);
+  else
+    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, st, part, splits, M, I, (float*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finalize(const uint64_t* best, const int32_t* anchor, int batch, int gamma,
+                                  int32_t* block_tokens, hipStream_t st) {
+  const int M = batch * gamma;
+  hipLaunchKernelGGL(k_argmax_finalize, dim3((M + 255) / 256), dim3(256), 0, st, best, anchor, M,
+                     gamma, block_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
+                              float eps, void* c, hipStream_t st) {
+  const size_t lds = (size_t)D * sizeof(float);
+  if (bf16)
+    hipLaunchKernelGGL(k_inject_norm<true>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n, D,
+                       (const uint16_t*)g, eps, (uint16_t*)c);
+  else
+    hipLaunchKernelGGL(k_inject_norm<false>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n,
+                       D, (const float*)g, eps, (float*)c);
+  return hipGetLastError();
+}
+
+hipError_t launch_inject_scatter(bool bf16, const float* part, int splits, int n_tok,
+                                 const int32_t* cu_new, int batch, const int32_t* ctx_lens,
+                                 const int32_t* page_table, int max_pages, int n_pages,
+                                 int page_size, void* pages, int n_layers, int Hkv, int dh,
+                                 float theta, uint32_t* err, hipStream_t st) {
+  dim3 grid(n_tok, n_layers * 2 * Hkv);
+  dim3 block(dh / 2);
+  if (bf16)
+    hipLaunchKernelGGL(k_inject_scatter<true>, grid, block, 0, st, part, splits, n_tok, cu_new,
+                       batch, ctx_lens, page_table, max_pages, n_pages, page_size,
+                       (uint16_t*)pages, n_layers, Hkv, dh, theta, err);
+  else
+    hipLaunchKernelGGL(k_inject_scatter<false>, grid, block, 0, st, part, splits, n_tok, cu_new,
+                       batch, ctx_lens, page_table, max_pages, n_pages, page_size,
+                       (float*)pages, n_layers, Hkv, dh, theta, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance_ctx(int32_t* ctx_lens, const int32_t* cu_new, int batch,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_advance_ctx, dim3((batch + 255) / 256), dim3(256), 0, st, ctx_lens, cu_new,
+                     batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(bool bf16, const int32_t* block_tokens, const void* target, int batch,
+                         int gamma, int vocab, uint64_t* best, int32_t* accept_len,
+                         int32_t* out_tokens, int32_t* target_argmax, hipStream_t st) {
+  const int rows = batch * gamma;
+  hipLaunchKernelGGL(k_zero_u64, dim3((rows + 255) / 256), dim3(256), 0, st, best, rows);
+  const int chunk = 8192;
+  dim3 grid((vocab + chunk - 1) / chunk, rows);
+  if (bf16)
+    hipLaunchKernelGGL(k_verify_argmax<true>, grid, dim3(256), 0, st, target, vocab, chunk, best);
+  else
+    hipLaunchKernelGGL(k_verify_argmax<false>, grid, dim3(256), 0, st, target, vocab, chunk, best);
+  hipLaunchKernelGGL(k_verify_finalize, dim3((batch + 63) / 64), dim3(64), 0, st, best,
+                     block_tokens, batch, gamma, accept_len, out_tokens, target_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_word(uint32_t* word, hipStream_t st) {
+  hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, st, word);
+  return hipGetLastError();
+}

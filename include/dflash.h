@@ -1,0 +1,222 @@
+/* dflash.h -- C ABI of the DFlash draft hot path on MI355X (gfx950).
+ *
+ * DFlash ("DFlash: Block Diffusion for Flash Speculative Decoding"; the paper
+ * is arXiv 2602.06036) speculates a block of tokens with a small drafter that
+ * reads the target model's hidden states.  One speculative cycle (summary
+ * page, "Putting It Together", steps 2-4) is three calls here:
+ *
+ *   dflash_inject_ctx    fuse the target features of new context tokens and
+ *                        append their per-layer K/V to the draft cache
+ *   dflash_draft_block   one parallel forward over [anchor, mask, ..., mask]
+ *                        -> proposed block
+ *   dflash_verify_greedy compare the block with the target's argmax tokens
+ *                        -> accepted length and output tokens
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE memory unless marked [host].  The caller owns all
+ *     memory (weights, KV pages, page table, context lengths, workspace,
+ *     outputs); the library allocates nothing in these calls.
+ *   - Matrices are row-major [out][in].  Element type is the model dtype
+ *     (DFLASH_BF16: raw bf16 bits; DFLASH_F32: float) unless stated.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream).  No call synchronises except
+ *     dflash_device_error and dflash_profile_read.
+ *   - Return value: DFLASH_OK or a negative dflash_status.  Host-checkable
+ *     problems (null pointers, shapes, dtype, sizes, workspace too small) are
+ *     reported before anything is launched; dflash_last_error() gives the
+ *     message.  Problems only the device can see (a page index outside the
+ *     pool, a position beyond the page table, an anchor outside the vocab)
+ *     set a sticky device error word and the offending reads/writes are
+ *     skipped; dflash_device_error() reads it.
+ *   - Calls that share a model, cache or workspace and overlap in time race;
+ *     order them on one stream.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVAL = -1,    /* null pointer or out-of-range scalar argument */
+  DFLASH_E_SHAPE = -2,    /* dimensions the kernels do not support */
+  DFLASH_E_DTYPE = -3,    /* unknown or mismatched element type */
+  DFLASH_E_CAPACITY = -4, /* workspace / batch / block larger than provisioned */
+  DFLASH_E_HIP = -5,      /* a HIP runtime call failed */
+  DFLASH_E_DEVICE = -6    /* the device error word was set (see below) */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Device error word bits (dflash_device_error). */
+#define DFLASH_DEVERR_PAGE 1u     /* page-table entry outside [0, n_pages) */
+#define DFLASH_DEVERR_POS 2u      /* position beyond max_pages_per_seq*page_size */
+#define DFLASH_DEVERR_TOKEN 4u    /* anchor token outside [0, vocab) (row uses token 0) */
+
+#define DFLASH_MAX_LAYERS 16
+#define DFLASH_MAX_BLOCK 16
+#define DFLASH_STATE_BYTES 256
+
+/* Drafter dimensions.  Constraints checked at model creation:
+ *   hidden % 32 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
+ *   n_q_heads / n_kv_heads <= 8, intermediate % 32 == 0, n_target_feats >= 1,
+ *   1 <= max_block <= DFLASH_MAX_BLOCK, page_size == 16,
+ *   0 <= mask_token_id < vocab, n_layers <= DFLASH_MAX_LAYERS. */
+typedef struct {
+  int32_t hidden;          /* D */
+  int32_t n_layers;        /* draft layers (5 for the Qwen3-8B-shaped drafter) */
+  int32_t n_q_heads;       /* Hq */
+  int32_t n_kv_heads;      /* Hkv */
+  int32_t head_dim;        /* dh */
+  int32_t intermediate;    /* SwiGLU width I */
+  int32_t vocab;           /* V, shared with the target's embedding and LM head */
+  int32_t n_target_feats;  /* m: target layers fused per token (5) */
+  int32_t max_block;       /* largest block size (anchor included) */
+  int32_t mask_token_id;   /* token id of the mask positions */
+  int32_t page_size;       /* tokens per KV page (16) */
+  int32_t dtype;           /* dflash_dtype of weights, activations and cache */
+  float rope_theta;        /* rotary base (1e6) */
+  float rms_eps;           /* RMSNorm epsilon (1e-6) */
+} dflash_config;
+
+/* Per-layer weights, device pointers in the model dtype:
+ *   attn_norm, mlp_norm [D]; wq [Hq*dh][D]; wk, wv [Hkv*dh][D];
+ *   wo [D][Hq*dh]; w_gate, w_up [I][D]; w_down [D][I]. */
+typedef struct {
+  const void* attn_norm;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const void* mlp_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} dflash_layer_weights;
+
+/* fc_w [D][m*D] is W_c, the context projection (summary page, "Target Hidden
+ * States Supply the Missing Context"; paper §7.3), with gain fc_norm [D].
+ * embed and lm_head [V][D] are the target's (frozen, shared; paper §4.2
+ * "Shared embedding and LM head"); they may alias.  final_norm [D]. */
+typedef struct {
+  const void* fc_w;
+  const void* fc_norm;
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  dflash_layer_weights layer[DFLASH_MAX_LAYERS];
+} dflash_weights;
+
+/* Paged draft KV cache: the injected target context of every draft layer
+ * (paper §4.1: the projected features are stored in the draft model's KV
+ * cache and reused across drafting iterations).  Block K/V are never stored.
+ *   pages      [n_layers][n_pages][2 (K, V)][n_kv_heads][page_size][head_dim]
+ *   page_table [batch][max_pages_per_seq]: page of tokens
+ *              [i*page_size, (i+1)*page_size) of each sequence
+ *   ctx_lens   [batch]: tokens already in the cache per sequence; K is
+ *              stored after rotary embedding at its absolute position. */
+typedef struct {
+  void* pages;
+  int32_t n_pages;
+  int32_t max_pages_per_seq;
+  const int32_t* page_table;
+  int32_t* ctx_lens;
+} dflash_kv;
+
+typedef struct dflash_model dflash_model;   /* opaque host handle */
+
+/* Create a model handle.  cfg and w are [host] structs; the weight pointers
+ * are device pointers the caller keeps alive for the handle's lifetime.
+ * state: device buffer of DFLASH_STATE_BYTES bytes owned by the caller (it
+ * holds the sticky device error word); it is cleared here (synchronously).
+ * The handle binds to the device current at creation. */
+int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void* state,
+                        dflash_model** out /* [host] */);
+void dflash_model_destroy(dflash_model* model);
+
+/* Bytes of workspace the three calls need for at most max_batch sequences,
+ * blocks of at most max_block positions, at most max_new_tokens tokens per
+ * inject call, and page tables of at most max_pages_per_seq entries.
+ * Returns 0 for invalid arguments. */
+size_t dflash_workspace_bytes(const dflash_model* model, int32_t max_batch, int32_t max_block,
+                              int32_t max_new_tokens, int32_t max_pages_per_seq);
+
+/* Context injection (summary page: "Target Hidden States Supply the Missing
+ * Context", eq. H_t = RMSNorm(W_c [H^(l1); ...; H^(lm)]), and "Per-Layer K/V
+ * Injection Prevents Context Dilution", K_i = [W_i^K H_t; ...],
+ * V_i = [W_i^V H_t; ...]; paper §4.1 and §7.3).
+ *   target_hidden [n_tok][m*D]: the new tokens' target features, per token
+ *                 the m selected layers concatenated shallow to deep; the
+ *                 tokens of sequence b are rows cu_new[b] .. cu_new[b+1]-1
+ *   cu_new        [batch+1] device prefix sums of new tokens per sequence,
+ *                 cu_new[0] = 0, cu_new[batch] = n_tok
+ *   n_tok         [host] total new tokens (grid sizing; 0 is a no-op)
+ * For token i of sequence b, position p = ctx_lens[b] + i:
+ *   c = RMSNorm(W_c f) and, for every layer l, K = RoPE(W_K^l c, p),
+ *   V = W_V^l c are written to page page_table[b][p / page_size], slot
+ *   p % page_size; afterwards ctx_lens[b] += cu_new[b+1] - cu_new[b]. */
+int dflash_inject_ctx(const dflash_model* model, const dflash_kv* kv, const void* target_hidden,
+                      const int32_t* cu_new, int32_t batch, int32_t n_tok, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Single-pass block draft (summary page: "Block Diffusion Makes Draft Cost
+ * Nearly Independent of Block Length" and "Putting It Together", step 3;
+ * paper §3.2 and §4.1 "Parallel diffusion drafting").
+ *   anchor       [batch] the clean anchor token of each sequence
+ *   block_size   gamma, 1..max_block, positions in the block incl. the anchor
+ *   block_tokens [batch][gamma] out: [anchor, d_1, ..., d_{gamma-1}],
+ *                d_j = lowest-index argmax of the logits of row j
+ *   logits       [batch][gamma][V] fp32 out, or NULL
+ * Row j of sequence b holds token (j == 0 ? anchor : mask_token_id) at
+ * position ctx_lens[b] + j; its attention sees the sequence's ctx_lens[b]
+ * cached keys and all gamma block keys (bidirectional, no mask inside the
+ * block).  The cache and ctx_lens are read only. */
+int dflash_draft_block(const dflash_model* model, const dflash_kv* kv, const int32_t* anchor,
+                       int32_t batch, int32_t block_size, int32_t* block_tokens, float* logits,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Greedy verification (summary page: "The Target Verifier Remains the
+ * Correctness Anchor" -- at temperature 0 the acceptance rule
+ * min(1, p_t/p_d) accepts a proposal exactly when it is the target's argmax;
+ * paper §3.1 for the accepted length).
+ *   block_tokens  [batch][gamma]: [anchor, d_1, ..., d_{gamma-1}]
+ *   target_logits [batch][gamma][vocab] in logits_dtype: row j is the
+ *                 target's scores for the token after block[0..j]
+ *   accept_len    [batch] out: tau = n + 1, n = longest prefix with
+ *                 block[j] == T_{j-1} for j = 1..n, T_j = lowest-index
+ *                 argmax of row j
+ *   out_tokens    [batch][gamma] out: block[1..n], T_n, then -1
+ *   target_argmax [batch][gamma] out (T_j), or NULL
+ *   workspace     at least batch*gamma*8 bytes (covered by
+ *                 dflash_workspace_bytes) */
+int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
+                         int32_t logits_dtype, int32_t batch, int32_t block_size, int32_t vocab,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* target_argmax,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* dflash_last_error(void);
+
+/* Synchronise `stream`, then read and clear the model's device error word
+ * into *code [host] (a mask of DFLASH_DEVERR_*).  Returns DFLASH_OK,
+ * DFLASH_E_DEVICE if the word was non-zero, or DFLASH_E_HIP. */
+int dflash_device_error(const dflash_model* model, void* stream, int32_t* code);
+
+/* Timing of the LM-head kernel of dflash_draft_block (the largest single
+ * launch of the draft step).  While enabled, each draft call records a HIP
+ * event pair on its stream around that launch.  dflash_profile_read waits
+ * for the recorded events and returns the summed milliseconds and the
+ * number of launches timed since the last reset. */
+int dflash_profile_enable(dflash_model* model, int32_t on);
+int dflash_profile_read(dflash_model* model, double* total_ms /* [host] */,
+                        int64_t* count /* [host] */, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -297,7 +297,6 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
 
   std::vector<double> q((size_t)R * QD), k((size_t)R * KV), v((size_t)R * KV);
   std::vector<double> o((size_t)R * QD), t1((size_t)R * D);
-  std::vector<double> qh((size_t)R * dh), kh((size_t)NK * dh), vh((size_t)NK * dh), oh((size_t)R * dh);
 
   for (int l = 0; l < NL; ++l) {
     for (int j = 0; j < R; ++j) {
@@ -315,24 +314,32 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
     for (auto& e : k) e = rnd(d, e);
     for (auto& e : v) e = rnd(d, e);
 
-    for (int h = 0; h < Hq; ++h) {
-      int kvh = h / group;
-      for (int r = 0; r < Lc; ++r)
-        for (int t = 0; t < dh; ++t) {
-          size_t src = (((size_t)l * Lbuf + r) * Hkv + kvh) * dh + t;
-          kh[(size_t)r * dh + t] = ld(ctx_k, src, d->bf16);
-          vh[(size_t)r * dh + t] = ld(ctx_v, src, d->bf16);
-        }
-      for (int r = 0; r < R; ++r)
-        for (int t = 0; t < dh; ++t) {
-          kh[(size_t)(Lc + r) * dh + t] = k[(size_t)r * KV + kvh * dh + t];
-          vh[(size_t)(Lc + r) * dh + t] = v[(size_t)r * KV + kvh * dh + t];
-        }
-      for (int j = 0; j < R; ++j)
-        for (int t = 0; t < dh; ++t) qh[(size_t)j * dh + t] = q[(size_t)j * QD + h * dh + t];
-      oracle_attention_dense(qh.data(), R, kh.data(), vh.data(), NK, dh, visible, oh.data());
-      for (int j = 0; j < R; ++j)
-        for (int t = 0; t < dh; ++t) o[(size_t)j * QD + h * dh + t] = rnd(d, oh[(size_t)j * dh + t]);
+    // Heads are independent; threads take whole heads, each with its own
+    // buffers, so every head's arithmetic is the same as in a serial loop.
+    #pragma omp parallel
+    {
+      std::vector<double> qh((size_t)R * dh), kh((size_t)NK * dh), vh((size_t)NK * dh);
+      std::vector<double> oh((size_t)R * dh);
+      #pragma omp for schedule(dynamic, 1)
+      for (int h = 0; h < Hq; ++h) {
+        int kvh = h / group;
+        for (int r = 0; r < Lc; ++r)
+          for (int t = 0; t < dh; ++t) {
+            size_t src = (((size_t)l * Lbuf + r) * Hkv + kvh) * dh + t;
+            kh[(size_t)r * dh + t] = ld(ctx_k, src, d->bf16);
+            vh[(size_t)r * dh + t] = ld(ctx_v, src, d->bf16);
+          }
+        for (int r = 0; r < R; ++r)
+          for (int t = 0; t < dh; ++t) {
+            kh[(size_t)(Lc + r) * dh + t] = k[(size_t)r * KV + kvh * dh + t];
+            vh[(size_t)(Lc + r) * dh + t] = v[(size_t)r * KV + kvh * dh + t];
+          }
+        for (int j = 0; j < R; ++j)
+          for (int t = 0; t < dh; ++t) qh[(size_t)j * dh + t] = q[(size_t)j * QD + h * dh + t];
+        oracle_attention_dense(qh.data(), R, kh.data(), vh.data(), NK, dh, visible, oh.data());
+        for (int j = 0; j < R; ++j)
+          for (int t = 0; t < dh; ++t) o[(size_t)j * QD + h * dh + t] = rnd(d, oh[(size_t)j * dh + t]);
+      }
     }
     matvec_rows(w->wo[l], d->bf16, D, QD, o.data(), R, t1.data());
     for (size_t i = 0; i < (size_t)R * D; ++i) x[i] += t1[i];

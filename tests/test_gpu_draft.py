@@ -1,0 +1,162 @@
+"""Single-pass block draft on the GPU vs the oracle, per call: both sides get
+the same seeded weights, the same synthetic context cache and the same
+anchors.  Logits must agree within the stated tolerance (fp32 models: 1e-4 of
+the largest reference logit; bf16 models: 2e-2 absolute) and every proposed
+token must be the oracle's argmax unless the oracle's top-2 gap there is
+below that tolerance.
+
+Covers: the five workloads (the batch-32, long-context and wide ones on
+sampled sequences), every GEMM path (1, 2, 4 row tiles and the tiled kernel),
+ragged and empty contexts, several context splits, ragged blocks, a block of
+one, determinism, batch invariance, and the device error word."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (PagedCache, check_tokens, log, logits_tolerance, make_drafter, workspace)
+from synth.configs import CONFIGS, Shape, anchors, context_kv, context_lengths, make_weights
+
+pytestmark = pytest.mark.gpu
+
+MINI = Shape("mini-bf16", 512, 2, 4, 2, 128, 768, 1000, 16, 1, True, seed=991)
+MINI_F32 = Shape("mini-f32", 256, 2, 4, 2, 64, 768, 1001, 5, 1, False, seed=992)
+
+
+def pages_for(L_max, extra=2):
+    return (int(L_max) + 15) // 16 + extra
+
+
+def setup_cache(s, ctx_lens, pages_per_seq):
+    cache = PagedCache(s, len(ctx_lens), pages_per_seq)
+    dense = {}
+    for b, L in enumerate(ctx_lens):
+        k, v = context_kv(s, b, int(L))
+        cache.write_dense(b, k, v)
+        dense[b] = (k, v)
+    kv = cache.upload(ctx_lens)
+    return cache, kv, dense
+
+
+def gpu_draft(drafter, kv, anc, gamma, pages_per_seq, logits=True):
+    import torch
+    B = len(anc)
+    ws = workspace(drafter, B, gamma, 1, pages_per_seq)
+    a = torch.from_numpy(np.asarray(anc, np.int32)).cuda()
+    blk = torch.full((B, gamma), -5, dtype=torch.int32, device="cuda")
+    lg = torch.full((B, gamma, drafter.cfg.vocab), float("nan"), device="cuda") if logits else None
+    drafter.draft(kv, a, gamma, blk, ws, logits=lg)
+    torch.cuda.synchronize()
+    return blk.cpu().numpy(), (lg.cpu().numpy() if logits else None)
+
+
+def check_seq(s, model, dense, L, anchor, gamma, gpu_block, gpu_logits):
+    k, v = dense
+    toks = np.full(gamma, s.mask_id, np.int32)
+    toks[0] = anchor
+    ref, ref_block = model.draft(k, v, int(L), toks)
+    tol = logits_tolerance(s, ref)
+    err = float(np.max(np.abs(gpu_logits.astype(np.float64) - ref)))
+    log(f"  L={L} gamma={gamma}: max|dlogit|={err:.3e} (tol {tol:.1e}), ref max {np.max(np.abs(ref)):.2f}")
+    assert np.all(np.isfinite(gpu_logits))
+    assert err <= tol
+    assert gpu_block[0] == anchor
+    tolerated = check_tokens(gpu_block, ref, 2e-2 if s.bf16 else tol)
+    return err, tolerated
+
+
+def run_case(s, ctx_lens, gamma, sample=None, weights=None):
+    log(f"draft {s.name}: batch {len(ctx_lens)} block {gamma} contexts {list(ctx_lens)[:8]}")
+    w = weights if weights is not None else make_weights(s)
+    drafter, w, _ = make_drafter(s, w)
+    pps = pages_for(max(ctx_lens))
+    cache, kv, dense = setup_cache(s, ctx_lens, pps)
+    anc = anchors(s, len(ctx_lens), tag=f"draft.anchor.{gamma}")
+    blk, lg = gpu_draft(drafter, kv, anc, gamma, pps)
+    assert drafter.device_error() == 0
+    model = oracle.Model(s, w)
+    seqs = range(len(ctx_lens)) if sample is None else sample
+    for b in seqs:
+        check_seq(s, model, dense[b], ctx_lens[b], anc[b], gamma, blk[b], lg[b])
+    return drafter, kv, anc, blk, lg, pps
+
+
+# ---------------------------------------------------------------- workloads
+def test_draft_tiny_fp32_workload():
+    s = CONFIGS[1]
+    run_case(s, context_lengths(s), s.block)
+
+
+def test_draft_qwen3_8b_batch1_workload():
+    s = CONFIGS[2]
+    run_case(s, context_lengths(s), s.block)
+
+
+def test_draft_qwen3_8b_batch32_workload_sampled():
+    s = CONFIGS[3]
+    L = context_lengths(s)
+    run_case(s, L, s.block, sample=[0, int(np.argmax(L)), int(np.argmin(L))])
+
+
+def test_draft_qwen3_8b_long_context_workload_sampled():
+    s = CONFIGS[4]
+    run_case(s, context_lengths(s), s.block, sample=[3])
+
+
+def test_draft_wide_workload_sampled():
+    s = CONFIGS[5]
+    L = context_lengths(s)
+    run_case(s, L, s.block, sample=[int(np.argmax(L))])
+
+
+# --------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("ctx", [[37], [0, 300], [5, 0, 129], [64, 17, 300, 31, 96]])
+def test_draft_mini_bf16_paths_and_ragged_contexts(ctx):
+    # batch 1/2/3/5 -> 16/32/48/80 block rows: 1, 2 and 4 row tiles of the
+    # skinny product, then the tiled product; contexts include 0, non-multiples
+    # of 16 and of 32, and several context splits.
+    run_case(MINI, ctx, 16)
+
+
+@pytest.mark.parametrize("gamma", [1, 7])
+def test_draft_mini_bf16_ragged_block(gamma):
+    run_case(MINI, [45, 200], gamma)
+
+
+def test_draft_mini_f32_batch():
+    run_case(MINI_F32, [3, 0, 70], MINI_F32.block)
+
+
+def test_draft_is_deterministic_and_batch_invariant():
+    s = MINI
+    w = make_weights(s)
+    ctx = [33, 250, 7]
+    drafter, kv, anc, blk, lg, pps = run_case(s, ctx, 16, weights=w)
+    blk2, lg2 = gpu_draft(drafter, kv, anc, 16, pps)
+    assert np.array_equal(blk, blk2) and np.array_equal(lg, lg2)        # bit-identical rerun
+    for b in range(len(ctx)):                                           # one sequence at a time
+        cache1 = PagedCache(s, 1, pps, tag=f"single{b}")
+        k, v = context_kv(s, b, ctx[b])
+        cache1.write_dense(0, k, v)
+        kv1 = cache1.upload([ctx[b]])
+        b1, l1 = gpu_draft(drafter, kv1, [anc[b]], 16, pps)
+        assert np.max(np.abs(l1[0] - lg[b])) <= 2e-2
+        check_tokens(b1[0], lg[b].astype(np.float64), 2e-2)
+
+
+def test_draft_device_error_word_reports_bad_page_and_anchor():
+    import torch
+    s = MINI
+    drafter, _, _ = make_drafter(s)
+    cache = PagedCache(s, 2, 4)
+    kv = cache.allocate_empty()
+    cache.ctx_dev.copy_(torch.tensor([20, 10], dtype=torch.int32))
+    bad = torch.from_numpy(cache.table.copy())
+    bad[0, 1] = cache.n_pages + 5            # outside the pool: reads are skipped
+    kv_bad = cache.KVCache(cache.pages, bad.cuda(), cache.ctx_dev)
+    ws = workspace(drafter, 2, 16, 1, 4)
+    blk = torch.zeros((2, 16), dtype=torch.int32, device="cuda")
+    drafter.draft(kv_bad, torch.tensor([1, 2], dtype=torch.int32, device="cuda"), 16, blk, ws)
+    assert drafter.device_error() & 1
+    assert drafter.device_error() == 0       # cleared by the read
+    drafter.draft(kv, torch.tensor([1, s.vocab + 3], dtype=torch.int32, device="cuda"), 16, blk, ws)
+    assert drafter.device_error() & 4
