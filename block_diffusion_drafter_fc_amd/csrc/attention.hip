@@ -7,18 +7,20 @@
 // h / (Hq / Hkv).
 //
 // Split-context (flash-decode) layout: workgroup (s, kvh, b) owns one KV head
-// of one sequence and one slice of keys -- context slice s, or the block's
-// own keys for s == n_ctx_splits -- and writes an unnormalised partial
-// (running max in log2 units, sum of weights, weighted values) that
-// k_attn_combine merges in split order.
+// of one sequence and one slice of keys -- context slice s < n_ctx_splits, or
+// the block's own keys (s == n_ctx_splits, k_attn_block) -- and writes an
+// unnormalised partial (running max in log2 units, sum of weights, weighted
+// values) that k_attn_combine merges in split order.
 //
-// bf16 kernel: one wave per query head of the KV group, the gamma (<= 16)
-// queries of that head form the N side of 16x16x32 MFMAs.  32 keys at a time
-// are staged in LDS (K row-major, V transposed).  Scores are computed as
-// S^T = K Q^T with the key rows of the two 16-row MFMA tiles interleaved so
-// that each lane ends up holding 8 consecutive keys of one query -- exactly the
-// B operand the P V product needs -- and the softmax max/sum runs over the 4
-// lanes of a query with two cross-lane shuffles.
+// bf16 context kernel: one wave per query head of the KV group, the gamma
+// (<= 16) queries of that head form the N side of 16x16x32 MFMAs.  32 cached
+// keys at a time are staged in LDS (K row-major, V transposed).  Scores are
+// computed as S^T = K Q^T with the key rows of the two 16-row MFMA tiles
+// interleaved so that each lane ends up holding 8 consecutive keys of one
+// query -- exactly the B operand the P V product needs -- and the softmax
+// max/sum runs over the 4 lanes of a query with two cross-lane shuffles.
+// The cached K/V are exact bf16; the queries and the softmax weights are fp32
+// values carried as hi+lo bf16 pairs, so each product is two MFMAs.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,10 +30,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DH>
 __global__ __launch_bounds__(512) void k_attn_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
-    const uint16_t* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
-    int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
+    const uint16_t* __restrict__ q, size_t q_plane, const uint16_t* __restrict__ pages,
+    int n_pages, const int32_t* __restrict__ page_table, int max_pages,
+    const int32_t* __restrict__ ctx_lens, int gamma, int Hq, int Hkv, int layer, int chunk,
     float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[32][DH + 8];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][32 + 8];
@@ -40,15 +41,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int h = kvh * G + wave;
   const int L = ctx_lens[b];
-  const bool blockpart = (s == n_ctx_splits);
-  int kbeg, kend;
-  if (blockpart) {
-    kbeg = 0;
-    kend = gamma;
-  } else {
-    kbeg = s * chunk;
-    kend = min(kbeg + chunk, L);
-  }
+  const int kbeg = s * chunk;
+  const int kend = min(kbeg + chunk, L);
   const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0
   if (kend <= kbeg) {
     if (lg == 0 && lr < gamma) {
@@ -60,12 +54,15 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
 
   constexpr int NI = DH / 32;   // MFMA K steps over the head dimension
   constexpr int ND = DH / 16;   // 16-row tiles of the head dimension
-  u32x4 qop[NI];
+  u32x4 qop[NI], qlo[NI];
   {
     const int row = b * gamma + (lr < gamma ? lr : 0);
     const uint16_t* qp = q + ((size_t)row * Hq + h) * DH + lg * 8;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) qop[i] = lr < gamma ? ld16(qp + i * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NI; ++i) {
+      qop[i] = lr < gamma ? ld16(qp + i * 32) : u32x4{0u, 0u, 0u, 0u};
+      qlo[i] = lr < gamma ? ld16(qp + q_plane + i * 32) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   f32x4 o[ND];
 #pragma unroll
@@ -82,21 +79,15 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
       const int key = t0 + kr;
       u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (key < kend) {
-        if (!blockpart) {
-          const int pi = key >> 4;
-          const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
-          if (pg >= 0 && pg < n_pages) {
-            const uint16_t* base = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
-                                   (size_t)(key & 15) * DH + d8;
-            vk = ld16(base);
-            vv = ld16(base + kv_stride);
-          } else if (d8 == 0) {
-            set_dev_error(err, pi < max_pages ? 1u : 2u);
-          }
-        } else {
-          const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * DH + d8;
-          vk = ld16(kb + off);
-          vv = ld16(vb + off);
+        const int pi = key >> 4;
+        const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
+        if (pg >= 0 && pg < n_pages) {
+          const uint16_t* base = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
+                                 (size_t)(key & 15) * DH + d8;
+          vk = ld16(base);
+          vv = ld16(base + kv_stride);
+        } else if (d8 == 0) {
+          set_dev_error(err, pi < max_pages ? 1u : 2u);
         }
       }
       st16(&Ks[kr][d8], vk);
@@ -109,8 +100,11 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      sa = mfma_16x16x32(ld16(&Ks[ra][i * 32 + lg * 8]), qop[i], sa);
-      sb = mfma_16x16x32(ld16(&Ks[rb][i * 32 + lg * 8]), qop[i], sb);
+      const u32x4 ka = ld16(&Ks[ra][i * 32 + lg * 8]), kb2 = ld16(&Ks[rb][i * 32 + lg * 8]);
+      sa = mfma_16x16x32(ka, qop[i], sa);
+      sa = mfma_16x16x32(ka, qlo[i], sa);
+      sb = mfma_16x16x32(kb2, qop[i], sb);
+      sb = mfma_16x16x32(kb2, qlo[i], sb);
     }
     // lane (query lr, group lg) now holds keys t0 + 8*lg + 0..7
     float sv[8];
@@ -129,22 +123,29 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2f(m_run - m_new);
-    uint16_t pb[8];
+    uint16_t pb[8], pl[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[e] = f2bf(exp2f(sv[e] - m_new));
-      psum += bf2f(pb[e]);
+      const float pe = exp2f(sv[e] - m_new);
+      pb[e] = f2bf(pe);
+      pl[e] = f2bf(pe - bf2f(pb[e]));
+      psum += pe;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    u32x4 pop;
+    u32x4 pop, plo;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pop[e] = (uint32_t)pb[2 * e] | ((uint32_t)pb[2 * e + 1] << 16);
+    for (int e = 0; e < 4; ++e) {
+      pop[e] = (uint32_t)pb[2 * e] | ((uint32_t)pb[2 * e + 1] << 16);
+      plo[e] = (uint32_t)pl[2 * e] | ((uint32_t)pl[2 * e + 1] << 16);
+    }
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       o[d] *= alpha;
-      o[d] = mfma_16x16x32(ld16(&Vt[d * 16 + lr][lg * 8]), pop, o[d]);
+      const u32x4 vt = ld16(&Vt[d * 16 + lr][lg * 8]);
+      o[d] = mfma_16x16x32(vt, pop, o[d]);
+      o[d] = mfma_16x16x32(vt, plo, o[d]);
     }
     __syncthreads();
   }
@@ -159,6 +160,76 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     if (lg == 0) {
       part_ml[(prow + lr) * 2 + 0] = m_run;
       part_ml[(prow + lr) * 2 + 1] = l_run;
+    }
+  }
+}
+
+// The block's own gamma keys (bf16 models): fp32 on the vector ALUs, since
+// the block keys and values are transient fp32 values.  Workgroup (kvh, b),
+// one wave per query head; lane = (query j = lane / 4, key group lane % 4).
+// Writes the partial of split index `split`.
+__global__ __launch_bounds__(512) void k_attn_block(
+    const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
+    const float* __restrict__ vb, int gamma, int Hq, int Hkv, int dh, int split,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ float ks[16][129];
+  __shared__ float vs[16][129];
+  __shared__ float ps[8][16][16];
+  const int kvh = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const int G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = kvh * G + wave;
+  for (int c = threadIdx.x; c < gamma * dh; c += blockDim.x) {
+    const int key = c / dh, d = c % dh;
+    const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * dh + d;
+    ks[key][d] = kb[off];
+    vs[key][d] = vb[off];
+  }
+  __syncthreads();
+  const int j = lane >> 2, kg = lane & 3;
+  const float sl2 = kLog2e / sqrtf((float)dh);
+  float sc[4];
+  float mx = -INFINITY;
+  if (j < gamma) {
+    const size_t qo = ((size_t)(b * gamma + j) * Hq + h) * dh;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = kg + 4 * t;
+      sc[t] = -INFINITY;
+      if (key < gamma) {
+        float acc = 0.f;
+        for (int d = 0; d < dh; ++d)
+          acc = fmaf(bf2f(q[qo + d]) + bf2f(q[q_plane + qo + d]), ks[key][d], acc);
+        sc[t] = acc * sl2;
+      }
+      mx = fmaxf(mx, sc[t]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  float l = 0.f;
+  if (j < gamma) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = kg + 4 * t;
+      const float p = key < gamma ? exp2f(sc[t] - mx) : 0.f;
+      if (key < 16) ps[wave][j][key] = p;
+      l += p;
+    }
+  }
+  l += __shfl_xor(l, 1, 64);
+  l += __shfl_xor(l, 2, 64);
+  __syncthreads();
+  if (j < gamma) {
+    const size_t pr = ((size_t)(split * B + b) * Hq + h) * gamma + j;
+    for (int d = kg; d < dh; d += 4) {
+      float acc = 0.f;
+      for (int key = 0; key < gamma; ++key) acc = fmaf(ps[wave][j][key], vs[key][d], acc);
+      part_o[pr * dh + d] = acc;
+    }
+    if (kg == 0) {
+      part_ml[pr * 2 + 0] = mx;
+      part_ml[pr * 2 + 1] = l;
     }
   }
 }
@@ -250,7 +321,7 @@ template <bool BF16>
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_parts, int gamma, int Hq, int dh,
-                                                      typename Act<BF16>::T* __restrict__ o) {
+                                                      void* __restrict__ o, size_t o_plane) {
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z, d = threadIdx.x;
   float M = -INFINITY;
   for (int s = 0; s < n_parts; ++s) {
@@ -268,7 +339,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   }
   if (d < dh) {
     const float v = den > 0.f ? num / den : 0.f;
-    Act<BF16>::store(o, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
+    Split<BF16>::store(o, o_plane, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
   }
 }
 
@@ -295,33 +366,37 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
                        a.part_o, a.part_ml, a.err);
     return hipGetLastError();
   }
-  dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
+  dim3 grid(p.n_ctx_splits, a.Hkv, a.batch);
   dim3 block(64 * (a.Hq / a.Hkv));
   if (a.dh == 128) {
-    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.pages,
-                       a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
-                       a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
+                       (const uint16_t*)a.pages, a.n_pages, a.page_table, a.max_pages,
+                       a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk, a.part_o, a.part_ml,
+                       a.err);
   } else if (a.dh == 64) {
-    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.pages,
-                       a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
-                       a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
+                       (const uint16_t*)a.pages, a.n_pages, a.page_table, a.max_pages,
+                       a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk, a.part_o, a.part_ml,
+                       a.err);
   } else {
     return hipErrorInvalidValue;
   }
+  hipLaunchKernelGGL(k_attn_block, dim3(a.Hkv, a.batch), block, 0, st, (const uint16_t*)a.q,
+                     a.q_plane, (const float*)a.k, (const float*)a.v, a.gamma, a.Hq, a.Hkv, a.dh,
+                     p.n_ctx_splits, a.part_o, a.part_ml);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
-                               int batch, int gamma, int Hq, int dh, void* o, hipStream_t st) {
+                               int batch, int gamma, int Hq, int dh, void* o, size_t o_plane,
+                               hipStream_t st) {
   dim3 grid(gamma, Hq, batch);
   dim3 block(dh < 64 ? 64 : dh);
   if (bf16)
     hipLaunchKernelGGL(k_attn_combine<true>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, (uint16_t*)o);
+                       Hq, dh, o, o_plane);
   else
     hipLaunchKernelGGL(k_attn_combine<false>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, (float*)o);
+                       Hq, dh, o, o_plane);
   return hipGetLastError();
 }

@@ -22,19 +22,41 @@ DF_DEV uint16_t f2bf(float f) {
 // Round an fp32 value to the nearest bf16 value, kept in fp32.
 DF_DEV float round_bf(float f) { return bf2f(f2bf(f)); }
 
-// Activation storage: bf16 bits (BF16 = true) or fp32.
+// Storage of the model dtype (weights, gains, hidden-state inputs, the K/V
+// cache): bf16 bits (BF16 = true) or fp32.
 template <bool BF16> struct Act;
 template <> struct Act<true> {
   typedef uint16_t T;
   static DF_DEV float load(const T* p, size_t i) { return bf2f(p[i]); }
   static DF_DEV void store(T* p, size_t i, float v) { p[i] = f2bf(v); }
-  static DF_DEV float rnd(float v) { return round_bf(v); }
 };
 template <> struct Act<false> {
   typedef float T;
   static DF_DEV float load(const T* p, size_t i) { return p[i]; }
   static DF_DEV void store(T* p, size_t i, float v) { p[i] = v; }
-  static DF_DEV float rnd(float v) { return v; }
+};
+
+// Transient activations that feed a matrix product.  fp32 models keep one
+// fp32 plane.  bf16 models keep the fp32 value as two bf16 planes, hi and lo
+// (hi = bf16(v), lo = bf16(v - hi), |v - hi - lo| <= 2^-17 |v|), laid out
+// back to back: lo starts `plane` elements after hi.  The products then run
+// as two bf16 MFMAs (hi and lo against the same weights).
+template <bool BF16> struct Split;
+template <> struct Split<true> {
+  static DF_DEV void store(void* base, size_t plane, size_t i, float v) {
+    uint16_t* hi = (uint16_t*)base;
+    const uint16_t h = f2bf(v);
+    hi[i] = h;
+    hi[plane + i] = f2bf(v - bf2f(h));
+  }
+  static DF_DEV float load(const void* base, size_t plane, size_t i) {
+    const uint16_t* hi = (const uint16_t*)base;
+    return bf2f(hi[i]) + bf2f(hi[plane + i]);
+  }
+};
+template <> struct Split<false> {
+  static DF_DEV void store(void* base, size_t, size_t i, float v) { ((float*)base)[i] = v; }
+  static DF_DEV float load(const void* base, size_t, size_t i) { return ((const float*)base)[i]; }
 };
 
 // D = A * B + C for one 16x16x32 bf16 MFMA tile.  Lane l (r = l % 16,

@@ -78,7 +78,6 @@ struct DraftLayout {
 DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages) {
   const Dims d = dims_of(m->cfg);
   const bool bf = m->bf16;
-  const size_t ab = bf ? 2 : 4;
   const size_t M = (size_t)B * gamma;
   DraftLayout L{};
   size_t off = 0;
@@ -87,13 +86,14 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
     off = align256(off + bytes);
     return o;
   };
+  // Transient activations take 4 bytes per element: fp32, or two bf16 planes.
   L.x = take(M * d.D * 4);
-  L.y = take(M * d.D * ab);
-  L.q = take(M * d.QD * ab);
-  L.k = take(M * d.KVD * ab);
-  L.v = take(M * d.KVD * ab);
-  L.o = take(M * d.QD * ab);
-  L.h = take(M * d.I * ab);
+  L.y = take(M * d.D * 4);
+  L.q = take(M * d.QD * 4);
+  L.k = take(M * d.KVD * 4);
+  L.v = take(M * d.KVD * 4);
+  L.o = take(M * d.QD * 4);
+  L.h = take(M * d.I * 4);
   size_t pf = part_floats(bf, (int)M, d.QD + 2 * d.KVD, d.D);
   pf = std::max(pf, part_floats(bf, (int)M, d.D, d.QD));
   pf = std::max(pf, part_floats(bf, (int)M, 2 * d.I, d.D));
@@ -122,7 +122,7 @@ InjectLayout inject_layout(const dflash_model* m, int n_tok) {
   L.part = off;
   off = align256(pf * 4);
   L.c = off;
-  off = align256(off + (size_t)n_tok * d.D * (bf ? 2 : 4));
+  off = align256(off + (size_t)n_tok * d.D * 4);
   L.total = off;
   return L;
 }
@@ -243,14 +243,17 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   char* ws = (char*)workspace;
   float* part = (float*)(ws + L.part);
   void* c = ws + L.c;
+  const size_t c_plane = (size_t)n_tok * d.D;
+  const void* c_lo = bf ? (const void*)((const uint16_t*)c + c_plane) : nullptr;
 
   WSeg fc{};
   fc.ptr[0] = m->w.fc_w;
   fc.row_end[0] = d.D;
   fc.n = 1;
   GemmPlan p = plan_gemm(bf, n_tok, d.D, d.F, false);
-  HIPCHK(launch_gemm(p, bf, hidden, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
-  HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c, st));
+  HIPCHK(launch_gemm(p, bf, hidden, nullptr, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
+  HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c,
+                            c_plane, st));
 
   WSeg kvw{};
   for (int l = 0; l < d.NL; ++l) {
@@ -262,7 +265,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   kvw.n = 2 * d.NL;
   const int Nkv = 2 * d.NL * d.KVD;
   p = plan_gemm(bf, n_tok, Nkv, d.D, false);
-  HIPCHK(launch_gemm(p, bf, c, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
+  HIPCHK(launch_gemm(p, bf, c, c_lo, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
   HIPCHK(launch_inject_scatter(bf, part, p.splits, n_tok, cu_new, batch, kv->ctx_lens,
                                kv->page_table, kv->max_pages_per_seq, kv->n_pages,
                                m->cfg.page_size, kv->pages, d.NL, d.Hkv, d.dh,
@@ -296,7 +299,14 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* x = (float*)(ws + L.x);
-  void *y = ws + L.y, *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *o = ws + L.o, *h = ws + L.h;
+  void *y = ws + L.y, *q = ws + L.q, *o = ws + L.o, *h = ws + L.h;
+  float* k = (float*)(ws + L.k);
+  float* v = (float*)(ws + L.v);
+  // planes of the split activations (bf16 models) and their lo halves
+  const size_t y_pl = (size_t)M * d.D, q_pl = (size_t)M * d.QD, h_pl = (size_t)M * d.I;
+  auto lo = [&](void* base, size_t plane) -> const void* {
+    return bf ? (const void*)((const uint16_t*)base + plane) : nullptr;
+  };
   float* part = (float*)(ws + L.part);
   float* att_o = (float*)(ws + L.att_o);
   float* att_ml = (float*)(ws + L.att_ml);
@@ -304,7 +314,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
 
   HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
                       best, m->err, st));
-  HIPCHK(launch_rmsnorm(bf, x, M, d.D, m->w.layer[0].attn_norm, eps, y, st));
+  HIPCHK(launch_rmsnorm(bf, x, M, d.D, m->w.layer[0].attn_norm, eps, y, y_pl, st));
   for (int l = 0; l < d.NL; ++l) {
     const dflash_layer_weights& W = m->w.layer[l];
     WSeg qkv{};
@@ -317,11 +327,12 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     qkv.n = 3;
     const int Nqkv = d.QD + 2 * d.KVD;
     GemmPlan p = plan_gemm(bf, M, Nqkv, d.D, false);
-    HIPCHK(launch_gemm(p, bf, y, d.D, M, qkv, Nqkv, d.D, part, nullptr, nullptr, st));
+    HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, qkv, Nqkv, d.D, part, nullptr, nullptr, st));
     HIPCHK(launch_qkv_epilogue(bf, part, p.splits, M, gamma, d.Hq, d.Hkv, d.dh, kv->ctx_lens,
-                               m->cfg.rope_theta, q, k, v, st));
+                               m->cfg.rope_theta, q, q_pl, k, v, st));
     AttnArgs a{};
     a.q = q;
+    a.q_plane = q_pl;
     a.k = k;
     a.v = v;
     a.pages = kv->pages;
@@ -340,15 +351,15 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     a.part_ml = att_ml;
     a.err = m->err;
     HIPCHK(launch_attention(bf, a, L.ap, st));
-    HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, st));
+    HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, q_pl, st));
 
     WSeg wo{};
     wo.ptr[0] = W.wo;
     wo.row_end[0] = d.D;
     wo.n = 1;
     p = plan_gemm(bf, M, d.D, d.QD, false);
-    HIPCHK(launch_gemm(p, bf, o, d.QD, M, wo, d.D, d.QD, part, nullptr, nullptr, st));
-    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, W.mlp_norm, eps, y, st));
+    HIPCHK(launch_gemm(p, bf, o, lo(o, q_pl), d.QD, M, wo, d.D, d.QD, part, nullptr, nullptr, st));
+    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, W.mlp_norm, eps, y, y_pl, st));
 
     WSeg gu{};
     gu.ptr[0] = W.w_gate;
@@ -357,17 +368,17 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     gu.row_end[1] = 2 * d.I;
     gu.n = 2;
     p = plan_gemm(bf, M, 2 * d.I, d.D, false);
-    HIPCHK(launch_gemm(p, bf, y, d.D, M, gu, 2 * d.I, d.D, part, nullptr, nullptr, st));
-    HIPCHK(launch_swiglu(bf, part, p.splits, M, d.I, h, st));
+    HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, gu, 2 * d.I, d.D, part, nullptr, nullptr, st));
+    HIPCHK(launch_swiglu(bf, part, p.splits, M, d.I, h, h_pl, st));
 
     WSeg dn{};
     dn.ptr[0] = W.w_down;
     dn.row_end[0] = d.D;
     dn.n = 1;
     p = plan_gemm(bf, M, d.D, d.I, false);
-    HIPCHK(launch_gemm(p, bf, h, d.I, M, dn, d.D, d.I, part, nullptr, nullptr, st));
+    HIPCHK(launch_gemm(p, bf, h, lo(h, h_pl), d.I, M, dn, d.D, d.I, part, nullptr, nullptr, st));
     const void* g_next = l + 1 < d.NL ? m->w.layer[l + 1].attn_norm : m->w.final_norm;
-    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, g_next, eps, y, st));
+    HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, g_next, eps, y, y_pl, st));
   }
 
   WSeg lm{};
@@ -386,7 +397,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     }
     HIPCHK(hipEventRecord(ev.first, st));
   }
-  HIPCHK(launch_gemm(p, bf, y, d.D, M, lm, d.V, d.D, nullptr, best, logits, st));
+  HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st));
   if (m->prof_on) {
     HIPCHK(hipEventRecord(ev.second, st));
     m->pending.push_back(ev);

@@ -33,7 +33,8 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
 template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict__ x, int D,
                                                          const typename Act<BF16>::T* __restrict__ g,
-                                                         float eps, typename Act<BF16>::T* __restrict__ y) {
+                                                         float eps, void* __restrict__ y,
+                                                         size_t y_plane) {
   __shared__ float red[16];
   const float* xr = x + (size_t)blockIdx.x * D;
   float ss = 0.f;
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
   for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Act<BF16>::store(y, (size_t)blockIdx.x * D + d, xr[d] * inv * Act<BF16>::load(g, d));
+    Split<BF16>::store(y, y_plane, (size_t)blockIdx.x * D + d, xr[d] * inv * Act<BF16>::load(g, d));
 }
 
 // x[r] += sum_s part[s][r]; then y[r] = RMSNorm(x[r]) * g (y optional).
@@ -50,7 +51,8 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(float* __restrict
                                                                const float* __restrict__ part,
                                                                int splits, int M, int D,
                                                                const typename Act<BF16>::T* __restrict__ g,
-                                                               float eps, typename Act<BF16>::T* __restrict__ y) {
+                                                               float eps, void* __restrict__ y,
+                                                               size_t y_plane) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * D;
@@ -66,17 +68,17 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(float* __restrict
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
   for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Act<BF16>::store(y, (size_t)r * D + d, xr[d] * inv * Act<BF16>::load(g, d));
+    Split<BF16>::store(y, y_plane, (size_t)r * D + d, xr[d] * inv * Act<BF16>::load(g, d));
 }
 
 // Sum the QKV partials, rotate q and k (rotate-half form) at position
-// ctx_lens[b] + j, store q [M][Hq][dh], k and v [M][Hkv][dh].
+// ctx_lens[b] + j, store q [M][Hq][dh] (split planes for bf16 models) and the
+// block's k and v [M][Hkv][dh] in fp32.
 template <bool BF16>
 __global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M, int gamma,
                                int Hq, int Hkv, int dh, const int32_t* __restrict__ ctx_lens,
-                               float theta, typename Act<BF16>::T* __restrict__ q,
-                               typename Act<BF16>::T* __restrict__ k,
-                               typename Act<BF16>::T* __restrict__ v) {
+                               float theta, void* __restrict__ q, size_t q_plane,
+                               float* __restrict__ k, float* __restrict__ v) {
   const int r = blockIdx.x, hh = blockIdx.y, i = threadIdx.x, half = dh / 2;
   const int N = (Hq + 2 * Hkv) * dh;
   (void)M;
@@ -94,26 +96,22 @@ __global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M
     a = a2;
     c2 = b2;
   }
-  typename Act<BF16>::T* dst;
-  size_t base;
   if (hh < Hq) {
-    dst = q;
-    base = ((size_t)r * Hq + hh) * dh;
-  } else if (hh < Hq + Hkv) {
-    dst = k;
-    base = ((size_t)r * Hkv + (hh - Hq)) * dh;
+    const size_t base = ((size_t)r * Hq + hh) * dh;
+    Split<BF16>::store(q, q_plane, base + i, a);
+    Split<BF16>::store(q, q_plane, base + i + half, c2);
   } else {
-    dst = v;
-    base = ((size_t)r * Hkv + (hh - Hq - Hkv)) * dh;
+    float* dst = hh < Hq + Hkv ? k : v;
+    const size_t base = ((size_t)r * Hkv + (hh < Hq + Hkv ? hh - Hq : hh - Hq - Hkv)) * dh;
+    dst[base + i] = a;
+    dst[base + i + half] = c2;
   }
-  Act<BF16>::store(dst, base + i, a);
-  Act<BF16>::store(dst, base + i + half, c2);
 }
 
 // h = silu(gate) * up, gate = columns [0, I), up = columns [I, 2I).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, int splits, int M,
-                                                int I, typename Act<BF16>::T* __restrict__ h) {
+                                                int I, void* __restrict__ h, size_t h_plane) {
   const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= I) return;
   float gt = 0.f, up = 0.f;
@@ -123,7 +121,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, 
     up += p[I + c];
   }
   const float sg = gt / (1.0f + expf(-gt));
-  Act<BF16>::store(h, (size_t)r * I + c, sg * up);
+  Split<BF16>::store(h, h_plane, (size_t)r * I + c, sg * up);
 }
 
 __global__ void k_argmax_finalize(const uint64_t* __restrict__ best,
@@ -140,7 +138,8 @@ template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void k_inject_norm(const float* __restrict__ part,
                                                              int splits, int n, int D,
                                                              const typename Act<BF16>::T* __restrict__ g,
-                                                             float eps, typename Act<BF16>::T* __restrict__ c) {
+                                                             float eps, void* __restrict__ c,
+                                                             size_t c_plane) {
   __shared__ float red[16];
   extern __shared__ float row[];
   const int t = blockIdx.x;
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(kRowThreads) void k_inject_norm(const float* __rest
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
   for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Act<BF16>::store(c, (size_t)t * D + d, row[d] * inv * Act<BF16>::load(g, d));
+    Split<BF16>::store(c, c_plane, (size_t)t * D + d, row[d] * inv * Act<BF16>::load(g, d));
 }
 
 // Token t of the inject batch belongs to sequence b with cu_new[b] <= t <
@@ -313,48 +312,49 @@ hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, 
 }
 
 hipError_t launch_rmsnorm(bool bf16, const float* x, int M, int D, const void* g, float eps,
-                          void* y, hipStream_t st) {
+                          void* y, size_t y_plane, hipStream_t st) {
   if (bf16)
     hipLaunchKernelGGL(k_rmsnorm<true>, dim3(M), dim3(kRowThreads), 0, st, x, D,
-                       (const uint16_t*)g, eps, (uint16_t*)y);
+                       (const uint16_t*)g, eps, y, y_plane);
   else
     hipLaunchKernelGGL(k_rmsnorm<false>, dim3(M), dim3(kRowThreads), 0, st, x, D,
-                       (const float*)g, eps, (float*)y);
+                       (const float*)g, eps, y, y_plane);
   return hipGetLastError();
 }
 
 hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int splits, int M, int D,
-                                const void* g, float eps, void* y, hipStream_t st) {
+                                const void* g, float eps, void* y, size_t y_plane,
+                                hipStream_t st) {
   if (bf16)
     hipLaunchKernelGGL(k_residual_norm<true>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
-                       M, D, (const uint16_t*)g, eps, (uint16_t*)y);
+                       M, D, (const uint16_t*)g, eps, y, y_plane);
   else
     hipLaunchKernelGGL(k_residual_norm<false>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
-                       M, D, (const float*)g, eps, (float*)y);
+                       M, D, (const float*)g, eps, y, y_plane);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int gamma, int Hq,
                                int Hkv, int dh, const int32_t* ctx_lens, float theta, void* q,
-                               void* k, void* v, hipStream_t st) {
+                               size_t q_plane, float* k, float* v, hipStream_t st) {
   dim3 grid(M, Hq + 2 * Hkv);
   dim3 block(dh / 2);
   if (bf16)
     hipLaunchKernelGGL(k_qkv_epilogue<true>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
-                       dh, ctx_lens, theta, (uint16_t*)q, (uint16_t*)k, (uint16_t*)v);
+                       dh, ctx_lens, theta, q, q_plane, k, v);
   else
     hipLaunchKernelGGL(k_qkv_epilogue<false>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
-                       dh, ctx_lens, theta, (float*)q, (float*)k, (float*)v);
+                       dh, ctx_lens, theta, q, q_plane, k, v);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
-                         hipStream_t st) {
+                         size_t h_plane, hipStream_t st) {
   dim3 grid((I + 255) / 256, M);
   if (bf16)
-    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, st, part, splits, M, I, (uint16_t*)h);
+    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
   else
-    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, st, part, splits, M, I, (float*)h);
+    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
   return hipGetLastError();
 }
 
@@ -367,14 +367,14 @@ hipError_t launch_argmax_finalize(const uint64_t* best, const int32_t* anchor, i
 }
 
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
-                              float eps, void* c, hipStream_t st) {
+                              float eps, void* c, size_t c_plane, hipStream_t st) {
   const size_t lds = (size_t)D * sizeof(float);
   if (bf16)
     hipLaunchKernelGGL(k_inject_norm<true>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n, D,
-                       (const uint16_t*)g, eps, (uint16_t*)c);
+                       (const uint16_t*)g, eps, c, c_plane);
   else
     hipLaunchKernelGGL(k_inject_norm<false>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n,
-                       D, (const float*)g, eps, (float*)c);
+                       D, (const float*)g, eps, c, c_plane);
   return hipGetLastError();
 }
 

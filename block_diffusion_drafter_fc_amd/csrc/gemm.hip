@@ -11,6 +11,8 @@
 //                  partial slices) so that thousands of waves keep HBM busy.
 //   k_gemm_tiled   bf16, larger M: 128x128 output tiles, both operands staged
 //                  through double-buffered LDS, 4 waves of 64x64.
+// With SPLIT the activations arrive as two bf16 planes (hi, lo) of an fp32
+// value and every weight fragment meets both: acc += hi*W + lo*W.
 //   k_gemm_f32     fp32 models: one thread per output, plain K loop.
 // All three can end in a fused row argmax (the LM head): the row maximum of
 // the tile is packed with its column into a 64-bit key (value order, then
@@ -45,10 +47,11 @@ DF_DEV uint64_t max16(uint64_t k) {
 }
 
 // ----------------------------------------------------------------------------
-template <int MT, int NT, int U>
+template <int MT, int NT, int U, bool SPLIT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
-    const uint16_t* __restrict__ A, int lda, int M, WSeg w, int N, int K, int kpw,
-    float* __restrict__ part, uint64_t* __restrict__ best, float* __restrict__ logits) {
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
+    int N, int K, int kpw, float* __restrict__ part, uint64_t* __restrict__ best,
+    float* __restrict__ logits) {
   extern __shared__ float red[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -64,11 +67,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
     bp[t] = seg_row_bf16(w, row, K) + kbeg + lg * 8;
   }
   const uint16_t* ap[MT];
+  const uint16_t* apl[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     int row = m * 16 + lr;
     row = row < M ? row : M - 1;
     ap[m] = A + (size_t)row * lda + kbeg + lg * 8;
+    apl[m] = SPLIT ? Alo + (size_t)row * lda + kbeg + lg * 8 : ap[m];
   }
 
   f32x4 acc[MT][NT];
@@ -93,17 +98,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 #pragma unroll
         for (int t = 0; t < NT; ++t) bnxt[u][t] = ld16(bp[t] + kk + 32 * U + u * 32);
     }
-    u32x4 a[U][MT];
+    u32x4 a[U][MT], al[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) a[u][m] = ld16(ap[m] + kk + u * 32);
+      for (int m = 0; m < MT; ++m) {
+        a[u][m] = ld16(ap[m] + kk + u * 32);
+        if (SPLIT) al[u][m] = ld16(apl[m] + kk + u * 32);
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[m][t] = mfma_16x16x32(a[u][m], bcur[u][t], acc[m][t]);
+        for (int t = 0; t < NT; ++t) {
+          acc[m][t] = mfma_16x16x32(a[u][m], bcur[u][t], acc[m][t]);
+          if (SPLIT) acc[m][t] = mfma_16x16x32(al[u][m], bcur[u][t], acc[m][t]);
+        }
     if (it + 1 < iters) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -177,12 +188,18 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 }
 
 // ----------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 64, TPAD = 8;
+constexpr int TBM = 128, TBN = 128, TPAD = 8;
 
+// BK = 64 without split, 32 with split (two A planes must fit LDS).
+template <bool SPLIT, int TBK>
 __global__ __launch_bounds__(256) void k_gemm_tiled(
-    const uint16_t* __restrict__ A, int lda, int M, WSeg w, int N, int K, int kps,
-    float* __restrict__ part, uint64_t* __restrict__ best, float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][TBM][TBK + TPAD];
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
+    int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
+    float* __restrict__ logits) {
+  constexpr int NP = SPLIT ? 2 : 1;               // A planes
+  constexpr int CPR = TBK / 8;                    // 16-byte chunks per tile row
+  constexpr int NCH = TBM * CPR / 256;            // chunks per thread per operand
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][TBM][TBK + TPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TBN][TBK + TPAD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -190,18 +207,21 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
   const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * TBN, split = blockIdx.z;
   const int kbeg = split * kps;
 
-  // Each thread moves 4 chunks of 16 bytes of A and of B per K step.
-  const uint16_t* ag[4];
-  const uint16_t* bg[4];
-  int lrow[4], lcol[4];
+  // Each thread moves NCH chunks of 16 bytes of every A plane and of B per
+  // K step.
+  const uint16_t* ag[NCH];
+  const uint16_t* agl[NCH];
+  const uint16_t* bg[NCH];
+  int lrow[NCH], lcol[NCH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = tid + i * 256;
-    lrow[i] = c >> 3;
-    lcol[i] = (c & 7) * 8;
+    lrow[i] = c / CPR;
+    lcol[i] = (c % CPR) * 8;
     int ar = m0 + lrow[i];
     ar = ar < M ? ar : M - 1;
     ag[i] = A + (size_t)ar * lda + kbeg + lcol[i];
+    agl[i] = SPLIT ? Alo + (size_t)ar * lda + kbeg + lcol[i] : ag[i];
     int br = n0 + lrow[i];
     br = br < N ? br : N - 1;
     bg[i] = seg_row_bf16(w, br, K) + kbeg + lcol[i];
@@ -213,15 +233,17 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[NCH], ral[NCH], rb[NCH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     ra[i] = ld16(ag[i]);
+    if (SPLIT) ral[i] = ld16(agl[i]);
     rb[i] = ld16(bg[i]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st16(&As[0][lrow[i]][lcol[i]], ra[i]);
+  for (int i = 0; i < NCH; ++i) {
+    st16(&As[0][0][lrow[i]][lcol[i]], ra[i]);
+    if (SPLIT) st16(&As[0][NP - 1][lrow[i]][lcol[i]], ral[i]);
     st16(&Bs[0][lrow[i]][lcol[i]], rb[i]);
   }
   __syncthreads();
@@ -232,27 +254,34 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
     if (s + 1 < steps) {
       const int ko = (s + 1) * TBK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NCH; ++i) {
         ra[i] = ld16(ag[i] + ko);
+        if (SPLIT) ral[i] = ld16(agl[i] + ko);
         rb[i] = ld16(bg[i] + ko);
       }
     }
 #pragma unroll
     for (int ks = 0; ks < TBK / 32; ++ks) {
-      u32x4 fa[4], fb[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) fa[a] = ld16(&As[cur][wm * 64 + a * 16 + lr][ks * 32 + lg * 8]);
+      u32x4 fb[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) fb[b] = ld16(&Bs[cur][wn * 64 + b * 16 + lr][ks * 32 + lg * 8]);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int pl = 0; pl < NP; ++pl) {
+        u32x4 fa[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_16x16x32(fa[a], fb[b], acc[a][b]);
+        for (int a = 0; a < 4; ++a)
+          fa[a] = ld16(&As[cur][pl][wm * 64 + a * 16 + lr][ks * 32 + lg * 8]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = mfma_16x16x32(fa[a], fb[b], acc[a][b]);
+      }
     }
     if (s + 1 < steps) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st16(&As[cur ^ 1][lrow[i]][lcol[i]], ra[i]);
+      for (int i = 0; i < NCH; ++i) {
+        st16(&As[cur ^ 1][0][lrow[i]][lcol[i]], ra[i]);
+        if (SPLIT) st16(&As[cur ^ 1][NP - 1][lrow[i]][lcol[i]], ral[i]);
         st16(&Bs[cur ^ 1][lrow[i]][lcol[i]], rb[i]);
       }
     }
@@ -322,13 +351,20 @@ __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, in
 }
 
 template <int MT, int NT, int U>
-hipError_t run_skinny(const GemmPlan& p, const void* A, int lda, int M, const WSeg& w, int N, int K,
-                      float* part, uint64_t* best, float* logits, hipStream_t st) {
+hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda, int M,
+                      const WSeg& w, int N, int K, float* part, uint64_t* best, float* logits,
+                      hipStream_t st) {
   dim3 grid((N + 16 * NT - 1) / (16 * NT), p.splits);
   dim3 block(64 * p.waves);
   size_t lds = p.waves > 1 ? (size_t)(p.waves - 1) * MT * NT * 4 * 64 * sizeof(float) : 0;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U>), grid, block, lds, st, (const uint16_t*)A, lda,
-                     M, w, N, K, p.kpw, part, best, logits);
+  if (Alo)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true>), grid, block, lds, st,
+                       (const uint16_t*)A, (const uint16_t*)Alo, lda, M, w, N, K, p.kpw, part,
+                       best, logits);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false>), grid, block, lds, st,
+                       (const uint16_t*)A, (const uint16_t*)nullptr, lda, M, w, N, K, p.kpw,
+                       part, best, logits);
   return hipGetLastError();
 }
 
@@ -377,16 +413,16 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
   int splits = 1;
   if (!argmax && tiles < 512) {
     const int want = (int)((512 + tiles - 1) / tiles);
-    splits = largest_divisor_at_most(K / TBK, want < 8 ? want : 8);
+    splits = largest_divisor_at_most(K / 64, want < 8 ? want : 8);
   }
   p.splits = splits;
   p.kpw = K / splits;
   return p;
 }
 
-hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, int lda, int M, const WSeg& w,
-                       int N, int K, float* part, uint64_t* best, float* logits,
-                       hipStream_t st) {
+hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
+                       int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
+                       float* logits, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (p.kind == GEMM_F32) {
     dim3 grid((N + 63) / 64, M);
@@ -397,15 +433,22 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, int lda, int
   (void)bf16;
   if (p.kind == GEMM_TILED) {
     dim3 grid((N + TBN - 1) / TBN, (M + TBM - 1) / TBM, p.splits);
-    hipLaunchKernelGGL(k_gemm_tiled, grid, dim3(256), 0, st, (const uint16_t*)A, lda, M, w, N, K,
-                       p.kpw, part, best, logits);
+    if (Alo)
+      hipLaunchKernelGGL((k_gemm_tiled<true, 32>), grid, dim3(256), 0, st, (const uint16_t*)A,
+                         (const uint16_t*)Alo, lda, M, w, N, K, p.kpw, part, best, logits);
+    else
+      hipLaunchKernelGGL((k_gemm_tiled<false, 64>), grid, dim3(256), 0, st, (const uint16_t*)A,
+                         (const uint16_t*)nullptr, lda, M, w, N, K, p.kpw, part, best, logits);
     return hipGetLastError();
   }
-  if (p.mt == 1 && p.nt == 2) return run_skinny<1, 2, 8>(p, A, lda, M, w, N, K, part, best, logits, st);
-  if (p.mt == 1 && p.nt == 1) return run_skinny<1, 1, 8>(p, A, lda, M, w, N, K, part, best, logits, st);
-  if (p.mt == 2 && p.nt == 2) return run_skinny<2, 2, 4>(p, A, lda, M, w, N, K, part, best, logits, st);
-  if (p.mt == 2 && p.nt == 1) return run_skinny<2, 1, 4>(p, A, lda, M, w, N, K, part, best, logits, st);
-  if (p.mt == 4 && p.nt == 2) return run_skinny<4, 2, 2>(p, A, lda, M, w, N, K, part, best, logits, st);
-  if (p.mt == 4 && p.nt == 1) return run_skinny<4, 1, 2>(p, A, lda, M, w, N, K, part, best, logits, st);
+#define DF_SKINNY(MT, NT, U) \
+  if (p.mt == MT && p.nt == NT) return run_skinny<MT, NT, U>(p, A, Alo, lda, M, w, N, K, part, best, logits, st)
+  DF_SKINNY(1, 2, 8);
+  DF_SKINNY(1, 1, 8);
+  DF_SKINNY(2, 2, 4);
+  DF_SKINNY(2, 1, 4);
+  DF_SKINNY(4, 2, 2);
+  DF_SKINNY(4, 1, 2);
+#undef DF_SKINNY
   return hipErrorInvalidValue;
 }

@@ -30,13 +30,15 @@ struct GemmPlan {
 // argmax: the product feeds the fused row-argmax (no K split across groups).
 GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax);
 
-// Run the plan.  Without `best`: part[s][M][N] (fp32) receives the partial
-// product of split s.  With `best` (argmax mode, splits == 1): best[row] is
-// raised (atomic max) to the argmax key of each row, and logits[M][N]
-// receives the fp32 products when non-null.
-hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, int lda, int M, const WSeg& w,
-                       int N, int K, float* part, uint64_t* best, float* logits,
-                       hipStream_t stream);
+// Run the plan.  A: fp32 [M][lda] for fp32 models; bf16 [M][lda] for bf16
+// models, with Alo the lo plane of a split activation (or null when A is an
+// exact bf16 input).  Without `best`: part[s][M][N] (fp32) receives the
+// partial product of split s.  With `best` (argmax mode, splits == 1):
+// best[row] is raised (atomic max) to the argmax key of each row, and
+// logits[M][N] receives the fp32 products when non-null.
+hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
+                       int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
+                       float* logits, hipStream_t stream);
 
 // ---- attention ------------------------------------------------------------
 struct AttnPlan {
@@ -46,39 +48,45 @@ struct AttnPlan {
 AttnPlan plan_attention(int batch, int n_kv_heads, int max_pages, int page_size);
 
 struct AttnArgs {
-  const void* q;        // [M][Hq][dh]
-  const void* k;        // [M][Hkv][dh]  block keys of this layer
-  const void* v;        // [M][Hkv][dh]
+  const void* q;        // [M][Hq][dh]: fp32, or the hi plane of a split (bf16 models)
+  size_t q_plane;       // elements from the hi plane to the lo plane
+  const void* k;        // [M][Hkv][dh] fp32: block keys of this layer
+  const void* v;        // [M][Hkv][dh] fp32
   const void* pages;    // cache base
   int n_pages, max_pages, page_size;
   const int32_t* page_table;
   const int32_t* ctx_lens;
   int batch, gamma, Hq, Hkv, dh, layer;
-  float* part_o;        // [splits+1][B][Hq][gamma][dh]
-  float* part_ml;       // [splits+1][B][Hq][gamma][2]  (max in log2 units, sum)
+  float* part_o;        // [n_ctx_splits+1][B][Hq][gamma][dh]
+  float* part_ml;       // [n_ctx_splits+1][B][Hq][gamma][2]  (max in log2 units, sum)
   uint32_t* err;
 };
 hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
-                               int batch, int gamma, int Hq, int dh, void* o, hipStream_t stream);
+                               int batch, int gamma, int Hq, int dh, void* o, size_t o_plane,
+                               hipStream_t stream);
 
 // ---- element-wise and row kernels -----------------------------------------
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
                         int vocab, const void* embed, int D, float* x, uint64_t* best,
                         uint32_t* err, hipStream_t stream);
+// Outputs named y, q, h, c are transient activations: fp32 for fp32 models,
+// split hi/lo bf16 planes for bf16 models (the lo plane starts *_plane
+// elements after the hi plane).
 hipError_t launch_rmsnorm(bool bf16, const float* x, int M, int D, const void* g, float eps,
-                          void* y, hipStream_t stream);
+                          void* y, size_t y_plane, hipStream_t stream);
 hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int splits, int M, int D,
-                                const void* g, float eps, void* y, hipStream_t stream);
+                                const void* g, float eps, void* y, size_t y_plane,
+                                hipStream_t stream);
 hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int gamma, int Hq,
                                int Hkv, int dh, const int32_t* ctx_lens, float theta, void* q,
-                               void* k, void* v, hipStream_t stream);
+                               size_t q_plane, float* k, float* v, hipStream_t stream);
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
-                         hipStream_t stream);
+                         size_t h_plane, hipStream_t stream);
 hipError_t launch_argmax_finalize(const uint64_t* best, const int32_t* anchor, int batch, int gamma,
                                   int32_t* block_tokens, hipStream_t stream);
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
-                              float eps, void* c, hipStream_t stream);
+                              float eps, void* c, size_t c_plane, hipStream_t stream);
 hipError_t launch_inject_scatter(bool bf16, const float* part, int splits, int n_tok,
                                  const int32_t* cu_new, int batch, const int32_t* ctx_lens,
                                  const int32_t* page_table, int max_pages, int n_pages,

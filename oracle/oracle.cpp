@@ -9,12 +9,18 @@
 //
 // Every sum is accumulated in double, in the natural index order, one output
 // at a time.  OpenMP only spreads independent outputs over threads; it never
-// changes the order of the additions inside one output.  In bf16 mode values
-// are rounded to bf16 (round to nearest, ties to even) at exactly these
-// points: the fused context c, the stored context k and v, the block q, k, v,
-// the attention output o, every RMSNorm output that feeds a matrix product,
-// and the SwiGLU product.  The residual stream and the logits stay in double.
-// In fp32 mode nothing is rounded.
+// changes the order of the additions inside one output.
+//
+// Precision.  Weights, the target's hidden states and the draft K/V cache are
+// stored in the model dtype.  In bf16 mode the only value the method itself
+// rounds is what it stores: the context keys and values written into the
+// cache by the injection (round to nearest, ties to even).  Every transient
+// value of a pass -- the fused context, norms, q/k/v of the block, attention
+// weights and outputs, the SwiGLU product, the residual stream, the logits --
+// stays in double.  (The pages fix bf16 for the weights and for the stored
+// context activations -- paper §7.3, "KV Injection Mechanism and Memory
+// Overhead" -- and say nothing of the transient activations.)  In fp32 mode
+// nothing is rounded.
 //
 // Sources (titles of the pages the method is described on):
 //   [S] "DFlash: Block Diffusion for Flash Speculative Decoding", the
@@ -164,17 +170,14 @@ void oracle_rope(double* x, int heads, int dh, double pos, double theta) {
 static double silu(double a) { return a / (1.0 + std::exp(-a)); }
 
 // SwiGLU MLP on R rows (a reading: the pages do not print the layer; the
-// drafter is taken as a Qwen3-style decoder layer):  out = W_down( silu(W_gate z) * W_up z ),
-// the product rounded to bf16 in bf16 mode.  z: [R][D], out: [R][D].
+// drafter is taken as a Qwen3-style decoder layer):
+// out = W_down( silu(W_gate z) * W_up z ).  z: [R][D], out: [R][D].
 void oracle_swiglu(const void* w_gate, const void* w_up, const void* w_down, int bf16,
                    int D, int I, const double* z, int R, double* out) {
   std::vector<double> g((size_t)R * I), u((size_t)R * I), hh((size_t)R * I);
   matvec_rows(w_gate, bf16, I, D, z, R, g.data());
   matvec_rows(w_up, bf16, I, D, z, R, u.data());
-  for (size_t i = 0; i < (size_t)R * I; ++i) {
-    double p = silu(g[i]) * u[i];
-    hh[i] = bf16 ? oracle_round_bf16(p) : p;
-  }
+  for (size_t i = 0; i < (size_t)R * I; ++i) hh[i] = silu(g[i]) * u[i];
   matvec_rows(w_down, bf16, D, I, hh.data(), R, out);
 }
 
@@ -234,8 +237,8 @@ void oracle_attention_dense(const double* q, int nq, const double* k,
 //
 // hidden: [n_tok][n_feats*D] (bf16 bits or fp32 per dims->bf16)
 // pos:    [n_tok] absolute positions
-// out_k, out_v: [n_tok][n_layers][Hkv][dh] doubles (already bf16-rounded in
-//         bf16 mode)
+// out_k, out_v: [n_tok][n_layers][Hkv][dh] doubles: the stored values, rounded
+//         to bf16 in bf16 mode
 void oracle_inject(const oracle_dims* d, const oracle_weights* w,
                    const void* hidden, const int32_t* pos, int n_tok,
                    double* out_k, double* out_v) {
@@ -246,7 +249,6 @@ void oracle_inject(const oracle_dims* d, const oracle_weights* w,
   matvec_rows(w->fc_w, d->bf16, D, F, f.data(), n_tok, u.data());
   for (int t = 0; t < n_tok; ++t) {
     oracle_rmsnorm(&u[(size_t)t * D], D, w->fc_norm, d->bf16, d->eps, &c[(size_t)t * D]);
-    for (int i = 0; i < D; ++i) c[(size_t)t * D + i] = rnd(d, c[(size_t)t * D + i]);
   }
   std::vector<double> kk((size_t)n_tok * KV), vv((size_t)n_tok * KV);
   for (int l = 0; l < NL; ++l) {
@@ -301,7 +303,6 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
   for (int l = 0; l < NL; ++l) {
     for (int j = 0; j < R; ++j) {
       oracle_rmsnorm(&x[(size_t)j * D], D, w->attn_norm[l], d->bf16, d->eps, &y[(size_t)j * D]);
-      for (int i = 0; i < D; ++i) y[(size_t)j * D + i] = rnd(d, y[(size_t)j * D + i]);
     }
     matvec_rows(w->wq[l], d->bf16, QD, D, y.data(), R, q.data());
     matvec_rows(w->wk[l], d->bf16, KV, D, y.data(), R, k.data());
@@ -310,9 +311,6 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
       oracle_rope(&q[(size_t)j * QD], Hq, dh, (double)pos[j], d->rope_theta);
       oracle_rope(&k[(size_t)j * KV], Hkv, dh, (double)pos[j], d->rope_theta);
     }
-    for (auto& e : q) e = rnd(d, e);
-    for (auto& e : k) e = rnd(d, e);
-    for (auto& e : v) e = rnd(d, e);
 
     // Heads are independent; threads take whole heads, each with its own
     // buffers, so every head's arithmetic is the same as in a serial loop.
@@ -338,7 +336,7 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
           for (int t = 0; t < dh; ++t) qh[(size_t)j * dh + t] = q[(size_t)j * QD + h * dh + t];
         oracle_attention_dense(qh.data(), R, kh.data(), vh.data(), NK, dh, visible, oh.data());
         for (int j = 0; j < R; ++j)
-          for (int t = 0; t < dh; ++t) o[(size_t)j * QD + h * dh + t] = rnd(d, oh[(size_t)j * dh + t]);
+          for (int t = 0; t < dh; ++t) o[(size_t)j * QD + h * dh + t] = oh[(size_t)j * dh + t];
       }
     }
     matvec_rows(w->wo[l], d->bf16, D, QD, o.data(), R, t1.data());
@@ -346,14 +344,12 @@ void oracle_forward(const oracle_dims* d, const oracle_weights* w,
 
     for (int j = 0; j < R; ++j) {
       oracle_rmsnorm(&x[(size_t)j * D], D, w->mlp_norm[l], d->bf16, d->eps, &y[(size_t)j * D]);
-      for (int i = 0; i < D; ++i) y[(size_t)j * D + i] = rnd(d, y[(size_t)j * D + i]);
     }
     oracle_swiglu(w->w_gate[l], w->w_up[l], w->w_down[l], d->bf16, D, I, y.data(), R, t1.data());
     for (size_t i = 0; i < (size_t)R * D; ++i) x[i] += t1[i];
   }
   for (int j = 0; j < R; ++j) {
     oracle_rmsnorm(&x[(size_t)j * D], D, w->final_norm, d->bf16, d->eps, &y[(size_t)j * D]);
-    for (int i = 0; i < D; ++i) y[(size_t)j * D + i] = rnd(d, y[(size_t)j * D + i]);
   }
   matvec_rows(w->lm_head, d->bf16, V, D, y.data(), R, logits);
 }

@@ -62,6 +62,14 @@ def test_cycle_matches_oracle(s, prompt_lens):
     assert drafter.device_error() == 0
     assert np.array_equal(cache.ctx_dev.cpu().numpy(), prompt_lens)
     model = oracle.Model(s, w)
+    cache.fetch()
+    for b, L in enumerate(prompt_lens):
+        rk, rv = model.inject(hidden_states(s, b, 0, L), np.arange(L, dtype=np.int32))
+        gk, gv = cache.read_dense(b, 0, L)
+        dk = np.abs(np.transpose(gk, (1, 0, 2, 3)) - rk)
+        dv = np.abs(np.transpose(gv, (1, 0, 2, 3)) - rv)
+        log(f"  seq {b}: cache max|dK| {dk.max():.3e} max|dV| {dv.max():.3e}, "
+            f"fraction of K/V values that differ {np.mean(dk > 0):.3f}/{np.mean(dv > 0):.3f}")
     ref = oracle_cycle(s, model, prompt_lens, anc, gamma)
     gblk = blk.cpu().numpy()
     glg = lg.cpu().numpy()
