@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft hot path on one MI355X.
+
+One step is one speculative cycle of the hot path for every sequence of the
+batch: inject the target features of the tokens accepted in the previous
+cycle (context fusion, per-layer K/V projection, rotary embedding, paged
+store), draft a block of 16 (anchor + 15 masks, one forward pass, LM-head
+argmax), and verify it greedily against planted target scores.  All inputs
+of all steps are resident in HBM before the timed region starts.
+
+The printed JSON line reports draft blocks/s (value) and draft tokens/s for
+the whole step, the LM-head kernel's achieved HBM bandwidth against the
+MI355X peak (timed live with HIP events on the launch stream), the whole
+step's algorithmic bytes as a fraction of the HBM roofline, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload qwen3-8b-bs1|qwen3-8b-bs32|qwen3-8b-long|wide-8layer|tiny-fp32]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft blocks/s & draft tokens/s (block 16, Qwen3-8B-shaped, bs 1/32); %HBM peak"
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- bytes model
+def fc_memory(hidden: int, n_tokens: int, n_feats: int = 5, elem: int = 2):
+    """Context projection memory (paper §7.3): W_c [D][m*D], the projection's
+    input [n][m*D] and output [n][D], in bytes."""
+    return (hidden * n_feats * hidden * elem, n_tokens * n_feats * hidden * elem,
+            n_tokens * hidden * elem)
+
+
+def algorithmic_bytes(s, ctx_lens_at_draft, n_new_total: int, batch: int, gamma: int) -> dict:
+    """Bytes the hot path must move once per step: every weight once, every
+    cached context K/V read once, the new K/V written once, the inputs read
+    and outputs written once.  Transient activations are small and counted
+    at 4 bytes per element where they cross kernels of the LM head."""
+    e = 2 if s.bf16 else 4
+    D, NL, V, I = s.hidden, s.n_layers, s.vocab, s.inter
+    QD, KVD = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    M = batch * gamma
+    layer_w = ((QD + 2 * KVD) * D + D * QD + 2 * I * D + D * I) * e
+    lm_w = V * D * e
+    kv_read = int(np.sum(ctx_lens_at_draft)) * NL * 2 * KVD * e
+    lm_head = lm_w + M * D * 4 + M * 8
+    draft = NL * (layer_w + 2 * s.hidden * e) + lm_head + kv_read + M * D * e + M * 4
+    w_fc, in_fc, _ = fc_memory(D, n_new_total, s.n_feats, e)
+    inject = w_fc + NL * 2 * KVD * D * e + in_fc + n_new_total * NL * 2 * KVD * e
+    verify = M * V * e + M * 4 * 3
+    return {"draft": draft, "inject": inject, "verify": verify, "lm_head": lm_head,
+            "step": draft + inject + verify, "kv_read": kv_read}
+
+
+def draft_flops(s, ctx_lens, batch, gamma):
+    D, NL, V, I = s.hidden, s.n_layers, s.vocab, s.inter
+    QD, KVD = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    M = batch * gamma
+    gemm = 2 * M * (NL * ((QD + 2 * KVD) * D + D * QD + 3 * I * D) + V * D)
+    attn = 4 * int(np.sum(np.asarray(ctx_lens) + gamma)) * gamma * s.n_q_heads * s.head_dim * NL
+    return gemm + attn
+
+
+# ------------------------------------------------------------------ workload
+class Workload:
+    """Seeded inputs of every step, resident on the device."""
+
+    def __init__(self, s, n_steps: int):
+        import torch
+        from synth import Gen
+        from synth.configs import context_lengths, planted_tau, anchors
+        self.s = s
+        self.B, self.gamma = s.batch, s.block
+        g = Gen(s.seed)
+        self.L0 = context_lengths(s).astype(np.int64)
+        B, S = self.B, n_steps
+        self.S = S
+        self.tau = np.stack([planted_tau(s, B, f"bench.tau.{k}") for k in range(S)])
+        if s.name == "qwen3-8b-bs32":      # 1..16 newly accepted tokens per step
+            self.n_new = np.stack([g.uniform_int(f"bench.new.{k}", B, 1, 16) for k in range(S)])
+        else:                               # the previous cycle's accepted length
+            first = planted_tau(s, B, "bench.tau.first")
+            self.n_new = np.concatenate([first[None], self.tau[:-1]], axis=0)
+        self.anchor = np.stack([anchors(s, B, tag=f"bench.anchor.{k}") for k in range(S)])
+        self.L_at = np.zeros((S, B), np.int64)      # context length seen by each draft
+        L = self.L0.copy()
+        for k in range(S):
+            L = L + self.n_new[k]
+            self.L_at[k] = L
+        self.Lmax = int(self.L_at[-1].max())
+        self.dev = torch.device("cuda")
+
+    def step_hidden(self, k):
+        from synth.configs import hidden_states
+        rows = []
+        start = self.L_at[k] - self.n_new[k]
+        for b in range(self.B):
+            rows.append(hidden_states(self.s, b, int(start[b]), int(self.n_new[k][b])))
+        return np.ascontiguousarray(np.concatenate(rows, axis=0))
+
+
+def to_dev(a, bf16):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if bf16:
+        t = t.view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def run_gpu(s, steps, warmup):
+    import torch
+    from block_diffusion_drafter_fc_amd import (Drafter, DrafterConfig, KVCache, verify_greedy)
+    from synth import Gen
+    from synth.configs import hidden_states, make_weights, page_pool
+
+    t0 = time.time()
+    S = warmup + steps
+    wl = Workload(s, S)
+    B, gamma = wl.B, wl.gamma
+    w_host = make_weights(s)
+    wdev = {k: to_dev(v, s.bf16) for k, v in w_host.items()}
+    cfg = DrafterConfig(hidden=s.hidden, n_layers=s.n_layers, n_q_heads=s.n_q_heads,
+                        n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, intermediate=s.inter,
+                        vocab=s.vocab, n_target_feats=s.n_feats, max_block=16,
+                        mask_token_id=s.mask_id, dtype=s.dtype, rope_theta=s.rope_theta,
+                        rms_eps=s.eps)
+    drafter = Drafter(cfg, wdev)
+    log(f"weights ready ({time.time() - t0:.1f}s)")
+
+    pps = (wl.Lmax + 15) // 16 + 1
+    n_pages, table = page_pool(s, pps, extra=4, tag="bench.pages")
+    dt = torch.bfloat16 if s.bf16 else torch.float32
+    pages = torch.zeros((s.n_layers, n_pages, 2, s.n_kv_heads, 16, s.head_dim), dtype=dt,
+                        device="cuda")
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kv = KVCache(pages, torch.from_numpy(table).cuda(), ctx)
+    chunk = 4096
+    ws = torch.empty(drafter.workspace_bytes(B, gamma, max(chunk, B * 16), pps),
+                     dtype=torch.uint8, device="cuda")
+
+    # prefill: inject each prompt in chunks of up to 4096 tokens
+    torch.cuda.synchronize()
+    tp = time.time()
+    prefill_tokens = 0
+    for b in range(B):
+        for c0 in range(0, int(wl.L0[b]), chunk):
+            n = min(chunk, int(wl.L0[b]) - c0)
+            cu = np.zeros(B + 1, np.int32)
+            cu[b + 1:] = n
+            drafter.inject(kv, to_dev(hidden_states(s, b, c0, n), s.bf16),
+                           torch.from_numpy(cu).cuda(), ws)
+            prefill_tokens += n
+    torch.cuda.synchronize()
+    prefill_s = time.time() - tp
+    assert np.array_equal(ctx.cpu().numpy(), wl.L0), "prefill did not advance the context"
+    log(f"prefill of {prefill_tokens} tokens: {prefill_s * 1e3:.1f} ms (incl. host input upload)")
+
+    # per-step inputs, resident on the device
+    hid = [to_dev(wl.step_hidden(k), s.bf16) for k in range(S)]
+    cus = [torch.from_numpy(np.concatenate([[0], np.cumsum(wl.n_new[k])]).astype(np.int32)).cuda()
+           for k in range(S)]
+    anc = [torch.from_numpy(wl.anchor[k]).cuda() for k in range(S)]
+    blk = [torch.zeros((B, gamma), dtype=torch.int32, device="cuda") for _ in range(S)]
+    acc = [torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(S)]
+    out = [torch.zeros((B, gamma), dtype=torch.int32, device="cuda") for _ in range(S)]
+    L0_dev = torch.from_numpy(wl.L0.astype(np.int32)).cuda()
+
+    # pre-pass: the drafted blocks decide the planted target scores
+    for k in range(S):
+        drafter.inject(kv, hid[k], cus[k], ws)
+        drafter.draft(kv, anc[k], gamma, blk[k], ws)
+    torch.cuda.synchronize()
+    assert drafter.device_error() == 0
+    g = Gen(s.seed)
+    tgt = []
+    for k in range(S):
+        t = g.plant_target(f"bench.target.{k}", blk[k].cpu().numpy(), wl.tau[k], s.vocab,
+                           dtype=s.dtype)
+        tgt.append(to_dev(t, s.bf16))
+    log(f"inputs of {S} steps resident ({time.time() - t0:.1f}s)")
+
+    def step(k):
+        drafter.inject(kv, hid[k], cus[k], ws)
+        drafter.draft(kv, anc[k], gamma, blk[k], ws)
+        verify_greedy(blk[k], tgt[k], acc[k], out[k], ws)
+
+    ctx.copy_(L0_dev)
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    drafter.profile_read(reset=True)
+    drafter.profile_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(warmup, S):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    drafter.profile_enable(False)
+    lm_ms, lm_count = drafter.profile_read(reset=True)
+    assert drafter.device_error() == 0
+
+    accepted = np.stack([acc[k].cpu().numpy() for k in range(warmup, S)])
+    planted = wl.tau[warmup:S]
+    replay_ok = float(np.mean(accepted == planted))
+
+    # draft call alone, on the final context
+    n_draft = min(steps, 30)
+    torch.cuda.synchronize()
+    td = time.perf_counter()
+    for k in range(n_draft):
+        drafter.draft(kv, anc[k], gamma, blk[k], ws)
+    torch.cuda.synchronize()
+    draft_only_ms = (time.perf_counter() - td) * 1e3 / n_draft
+
+    res = dict(elapsed=elapsed, steps=steps, warmup=warmup, lm_ms=lm_ms, lm_count=lm_count,
+               replay_ok=replay_ok, draft_only_ms=draft_only_ms, prefill_s=prefill_s,
+               prefill_tokens=prefill_tokens, wl=wl)
+    drafter.close()
+    return res, w_host
+
+
+def cpu_baseline(s, w_host, budget_s=15.0):
+    """The oracle, as committed, on a bounded sample: whole draft blocks of one
+    sequence (its real context length, synthetic cached context) plus the
+    greedy verification of each block, until about budget_s of CPU work."""
+    import oracle
+    from synth import Gen
+    from synth.configs import anchors, context_kv, context_lengths
+    L = int(context_lengths(s)[0])
+    ck, cv = context_kv(s, 0, L)
+    m = oracle.Model(s, w_host)
+    toks = np.full(s.block, s.mask_id, np.int32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        toks[0] = anchors(s, 1, tag=f"cpu.anchor.{n}")[0]
+        _, block = m.draft(ck, cv, L, toks)
+        tgt = Gen(s.seed).plant_target(f"cpu.target.{n}", block[None], np.array([4]), s.vocab,
+                                       dtype=s.dtype)
+        oracle.verify(block, tgt[0], s.bf16)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s or n >= 50:
+            break
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n / dt, 4), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} draft blocks (block {s.block}) + greedy verification of each, one "
+                      f"sequence with a {L}-token synthetic context, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-bs1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the DFlash hot path here is built for and timed on a "
+              f"single MI355X (sequences shard across GPUs with no exchange); --gpus {args.gpus} "
+              f"is not run.", file=sys.stderr)
+        sys.exit(2)
+    from synth.configs import CONFIGS
+    by_name = {c.name: c for c in CONFIGS.values()}
+    if args.workload not in by_name:
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(by_name)}")
+    s = by_name[args.workload]
+
+    res, w_host = run_gpu(s, args.steps, args.warmup)
+    wl = res["wl"]
+    B, gamma = wl.B, wl.gamma
+    timed = slice(args.warmup, args.warmup + args.steps)
+    ms_step = res["elapsed"] * 1e3 / args.steps
+    blocks_per_s = B * args.steps / res["elapsed"]
+    # algorithmic bytes over the timed steps
+    step_bytes = [algorithmic_bytes(s, wl.L_at[k], int(wl.n_new[k].sum()), B, gamma)
+                  for k in range(timed.start, timed.stop)]
+    mean_step_bytes = float(np.mean([b["step"] for b in step_bytes]))
+    mean_draft_bytes = float(np.mean([b["draft"] for b in step_bytes]))
+    lm_bytes = step_bytes[0]["lm_head"]
+    lm_avg_ms = res["lm_ms"] / max(res["lm_count"], 1)
+    lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
+    step_gbs = mean_step_bytes / (ms_step * 1e-3) / 1e9
+    draft_gbs = mean_draft_bytes / (res["draft_only_ms"] * 1e-3) / 1e9
+    flops = draft_flops(s, wl.L_at[-1], B, gamma)
+    line = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": s.name, "batch": B, "block": gamma, "hidden": s.hidden,
+                   "draft_layers": s.n_layers, "heads": f"{s.n_q_heads}/{s.n_kv_heads}",
+                   "intermediate": s.inter, "vocab": s.vocab,
+                   "context_start": int(wl.L0.mean()), "context_end": int(wl.L_at[-1].mean()),
+                   "step": "inject accepted tokens + draft block + greedy verify",
+                   "parallelism": "single GPU"},
+        "draft_tokens_per_s": round(blocks_per_s * (gamma - 1), 2),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_algorithmic_GB": round(mean_step_bytes / 1e9, 4),
+        "draft_only": {"ms": round(res["draft_only_ms"], 4),
+                       "blocks_per_s": round(B * 1e3 / res["draft_only_ms"], 3),
+                       "hbm_frac": round(draft_gbs / HBM_PEAK_GBS, 4),
+                       "algorithmic_GB": round(mean_draft_bytes / 1e9, 4),
+                       "tflops": round(flops / (res["draft_only_ms"] * 1e-3) / 1e12, 2)},
+        "replay_accept_match": res["replay_ok"],
+        "prefill": {"tokens": res["prefill_tokens"], "s": round(res["prefill_s"], 4)},
+        "roofline": {"kernel": "LM head + fused argmax (k_gemm_skinny, argmax epilogue)",
+                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "avg_launch_ms": round(lm_avg_ms, 5), "launches": res["lm_count"],
+                     "bytes_per_launch": lm_bytes, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(s, w_host, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,6 +27,8 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxCtxSplits = 256;            // bounded by plan_attention
+constexpr int kMaxParts = kMaxCtxSplits + 1;  // + the block's own keys
 
 template <int DH>
 __global__ __launch_bounds__(512) void k_attn_bf16(
@@ -165,57 +167,65 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
 }
 
 // The block's own gamma keys (bf16 models): fp32 on the vector ALUs, since
-// the block keys and values are transient fp32 values.  Workgroup (kvh, b),
-// one wave per query head; lane = (query j = lane / 4, key group lane % 4).
-// Writes the partial of split index `split`.
-__global__ __launch_bounds__(512) void k_attn_block(
+// the block keys and values are transient fp32 values.  One wave per (query
+// head, sequence): q, k, v of the block are staged in LDS with 16-byte loads
+// that are all in flight together; lane = (query j = lane / 4, key group
+// lane % 4).  Writes the partial of split index `split`.
+__global__ __launch_bounds__(64) void k_attn_block(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
     const float* __restrict__ vb, int gamma, int Hq, int Hkv, int dh, int split,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ float ks[16][129];
-  __shared__ float vs[16][129];
-  __shared__ float ps[8][16][16];
-  const int kvh = blockIdx.x, b = blockIdx.y, B = gridDim.y;
-  const int G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = kvh * G + wave;
-  for (int c = threadIdx.x; c < gamma * dh; c += blockDim.x) {
-    const int key = c / dh, d = c % dh;
+  __shared__ float qs[16][132];
+  __shared__ float ks[16][132];
+  __shared__ float vs[16][132];
+  __shared__ float ps[16][17];
+  const int h = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const int kvh = h / (Hq / Hkv), lane = threadIdx.x;
+  const int d4 = dh / 4, d8 = dh / 8;
+  // k, v: gamma*dh/4 float4 each; q: gamma*dh/8 chunks of 8 bf16 per plane
+#pragma unroll 4
+  for (int c = lane; c < gamma * d4; c += 64) {
+    const int key = c / d4, d = (c % d4) * 4;
     const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * dh + d;
-    ks[key][d] = kb[off];
-    vs[key][d] = vb[off];
+    *(f32x4*)&ks[key][d] = *(const f32x4*)&kb[off];
+    *(f32x4*)&vs[key][d] = *(const f32x4*)&vb[off];
+  }
+#pragma unroll 4
+  for (int c = lane; c < gamma * d8; c += 64) {
+    const int j = c / d8, d = (c % d8) * 8;
+    const size_t off = ((size_t)(b * gamma + j) * Hq + h) * dh + d;
+    const u32x4 hi = ld16(q + off), lo = ld16(q + q_plane + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qs[j][d + 2 * e] = bf2f((uint16_t)(hi[e] & 0xFFFFu)) + bf2f((uint16_t)(lo[e] & 0xFFFFu));
+      qs[j][d + 2 * e + 1] = bf2f((uint16_t)(hi[e] >> 16)) + bf2f((uint16_t)(lo[e] >> 16));
+    }
   }
   __syncthreads();
   const int j = lane >> 2, kg = lane & 3;
   const float sl2 = kLog2e / sqrtf((float)dh);
   float sc[4];
   float mx = -INFINITY;
-  if (j < gamma) {
-    const size_t qo = ((size_t)(b * gamma + j) * Hq + h) * dh;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = kg + 4 * t;
-      sc[t] = -INFINITY;
-      if (key < gamma) {
-        float acc = 0.f;
-        for (int d = 0; d < dh; ++d)
-          acc = fmaf(bf2f(q[qo + d]) + bf2f(q[q_plane + qo + d]), ks[key][d], acc);
-        sc[t] = acc * sl2;
-      }
-      mx = fmaxf(mx, sc[t]);
+  for (int t = 0; t < 4; ++t) {
+    const int key = kg + 4 * t;
+    sc[t] = -INFINITY;
+    if (j < gamma && key < gamma) {
+      float acc = 0.f;
+      for (int d = 0; d < dh; ++d) acc = fmaf(qs[j][d], ks[key][d], acc);
+      sc[t] = acc * sl2;
     }
+    mx = fmaxf(mx, sc[t]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
   float l = 0.f;
-  if (j < gamma) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = kg + 4 * t;
-      const float p = key < gamma ? exp2f(sc[t] - mx) : 0.f;
-      if (key < 16) ps[wave][j][key] = p;
-      l += p;
-    }
+  for (int t = 0; t < 4; ++t) {
+    const int key = kg + 4 * t;
+    const float p = (j < gamma && key < gamma) ? exp2f(sc[t] - mx) : 0.f;
+    ps[j][key] = p;
+    l += p;
   }
   l += __shfl_xor(l, 1, 64);
   l += __shfl_xor(l, 2, 64);
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(512) void k_attn_block(
     const size_t pr = ((size_t)(split * B + b) * Hq + h) * gamma + j;
     for (int d = kg; d < dh; d += 4) {
       float acc = 0.f;
-      for (int key = 0; key < gamma; ++key) acc = fmaf(ps[wave][j][key], vs[key][d], acc);
+      for (int key = 0; key < gamma; ++key) acc = fmaf(ps[j][key], vs[key][d], acc);
       part_o[pr * dh + d] = acc;
     }
     if (kg == 0) {
@@ -322,22 +332,38 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
                                                       const float* __restrict__ part_ml,
                                                       int n_parts, int gamma, int Hq, int dh,
                                                       void* __restrict__ o, size_t o_plane) {
+  // Phase 1: thread s < n_parts fetches split s's (max, sum) -- all at once --
+  // and the group forms the common maximum and the weights 2^(m_s - max).
+  // Phase 2: thread d sums the weighted partial outputs over the splits.
+  __shared__ float wgt[kMaxParts];
+  __shared__ float red[4];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z, d = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_parts; ++s) {
-    const size_t pr = ((size_t)(s * B + b) * Hq + h) * gamma + j;
-    if (part_ml[pr * 2 + 1] > 0.f) M = fmaxf(M, part_ml[pr * 2]);
+  const size_t stride = (size_t)B * Hq * gamma;            // partial rows per split
+  const size_t pr0 = ((size_t)b * Hq + h) * gamma + j;
+  float mx = -INFINITY;
+  for (int s = d; s < n_parts; s += blockDim.x) {
+    if (part_ml[(pr0 + s * stride) * 2 + 1] > 0.f) mx = fmaxf(mx, part_ml[(pr0 + s * stride) * 2]);
   }
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  for (int s = d; s < n_parts; s += blockDim.x) {
+    const float l = part_ml[(pr0 + s * stride) * 2 + 1];
+    wgt[s] = l > 0.f ? exp2f(part_ml[(pr0 + s * stride) * 2] - mx) : 0.f;
+  }
+  __syncthreads();
   float num = 0.f, den = 0.f;
-  for (int s = 0; s < n_parts; ++s) {
-    const size_t pr = ((size_t)(s * B + b) * Hq + h) * gamma + j;
-    const float l = part_ml[pr * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float wgt = exp2f(part_ml[pr * 2] - M);
-    den += wgt * l;
-    if (d < dh) num += wgt * part_o[pr * dh + d];
-  }
   if (d < dh) {
+#pragma unroll 8
+    for (int s = 0; s < n_parts; ++s) {
+      const float ww = wgt[s];
+      if (ww == 0.f) continue;
+      num += ww * part_o[(pr0 + s * stride) * dh + d];
+      den += ww * part_ml[(pr0 + s * stride) * 2 + 1];
+    }
     const float v = den > 0.f ? num / den : 0.f;
     Split<BF16>::store(o, o_plane, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
   }
@@ -349,6 +375,8 @@ AttnPlan plan_attention(int batch, int n_kv_heads, int max_pages, int page_size)
   AttnPlan p;
   const long cap = (long)max_pages * page_size;
   long chunk = (cap * batch * n_kv_heads + 1023) / 1024;
+  const long min_chunk = (cap + kMaxCtxSplits - 1) / kMaxCtxSplits;
+  if (chunk < min_chunk) chunk = min_chunk;
   chunk = ((chunk + 31) / 32) * 32;
   if (chunk < 64) chunk = 64;
   p.chunk = (int)chunk;
@@ -381,7 +409,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
   } else {
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_attn_block, dim3(a.Hkv, a.batch), block, 0, st, (const uint16_t*)a.q,
+  hipLaunchKernelGGL(k_attn_block, dim3(a.Hq, a.batch), dim3(64), 0, st, (const uint16_t*)a.q,
                      a.q_plane, (const float*)a.k, (const float*)a.v, a.gamma, a.Hq, a.Hkv, a.dh,
                      p.n_ctx_splits, a.part_o, a.part_ml);
   return hipGetLastError();

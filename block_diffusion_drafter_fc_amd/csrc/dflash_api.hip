@@ -73,6 +73,7 @@ struct DraftLayout {
   size_t x, y, q, k, v, o, h, part, att_o, att_ml, best, total;
   AttnPlan ap;
   int parts;
+  int groups;   // column groups of the LM-head argmax
 };
 
 DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages) {
@@ -103,7 +104,9 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
   L.parts = bf ? L.ap.n_ctx_splits + 1 : 1;
   L.att_o = take((size_t)L.parts * M * d.Hq * d.dh * 4);
   L.att_ml = take((size_t)L.parts * M * d.Hq * 2 * 4);
-  L.best = take(M * 8);
+  const GemmPlan lm = plan_gemm(bf, (int)M, d.V, d.D, true);
+  L.groups = gemm_argmax_groups(lm, d.V);
+  L.best = take((size_t)L.groups * M * 8);
   L.total = off;
   return L;
 }
@@ -147,6 +150,8 @@ int check_config(const dflash_config* c) {
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f))
     return fail(DFLASH_E_INVAL, "config: rope_theta must be > 0 and rms_eps >= 0");
   if (c->n_layers * 2 > WSEG_MAX) return fail(DFLASH_E_SHAPE, "config: too many layers");
+  if (c->hidden % 4 || c->hidden > 8192)
+    return fail(DFLASH_E_SHAPE, "config: hidden must be a multiple of 4 and at most 8192");
   if (c->dtype == DFLASH_BF16) {
     const int qd = c->n_q_heads * c->head_dim;
     if (c->hidden % 256 || c->intermediate % 256 || qd % 256)
@@ -313,8 +318,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
   uint64_t* best = (uint64_t*)(ws + L.best);
 
   HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
-                      best, m->err, st));
-  HIPCHK(launch_rmsnorm(bf, x, M, d.D, m->w.layer[0].attn_norm, eps, y, y_pl, st));
+                      m->w.layer[0].attn_norm, eps, y, y_pl, m->err, st));
   for (int l = 0; l < d.NL; ++l) {
     const dflash_layer_weights& W = m->w.layer[l];
     WSeg qkv{};
@@ -402,7 +406,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     HIPCHK(hipEventRecord(ev.second, st));
     m->pending.push_back(ev);
   }
-  HIPCHK(launch_argmax_finalize(best, anchor, batch, gamma, block_tokens, st));
+  HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
   return DFLASH_OK;
 }
 

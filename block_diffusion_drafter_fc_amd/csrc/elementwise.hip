@@ -12,22 +12,35 @@ namespace {
 
 constexpr int kRowThreads = 256;
 
+// Row r = b*gamma + j of the block: token (j == 0 ? anchor[b] : mask), its
+// embedding into the fp32 residual x, and y = RMSNorm(x) * g (the first
+// layer's attention norm).
 template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict__ anchor,
                                                        int gamma, int mask_id, int vocab,
                                                        const typename Act<BF16>::T* __restrict__ E,
                                                        int D, float* __restrict__ x,
-                                                       uint64_t* __restrict__ best,
-                                                       uint32_t* err) {
+                                                       const typename Act<BF16>::T* __restrict__ g,
+                                                       float eps, void* __restrict__ y,
+                                                       size_t y_plane, uint32_t* err) {
+  __shared__ float red[16];
   const int r = blockIdx.x, b = r / gamma, j = r % gamma;
   int tok = j == 0 ? anchor[b] : mask_id;
   if (tok < 0 || tok >= vocab) {
     if (threadIdx.x == 0) set_dev_error(err, 4u);
     tok = 0;
   }
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const float v = Act<BF16>::load(E, (size_t)tok * D + d);
+    x[(size_t)r * D + d] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
   for (int d = threadIdx.x; d < D; d += blockDim.x)
-    x[(size_t)r * D + d] = Act<BF16>::load(E, (size_t)tok * D + d);
-  if (threadIdx.x == 0) best[r] = 0;
+    Split<BF16>::store(y, y_plane, (size_t)r * D + d,
+                       Act<BF16>::load(E, (size_t)tok * D + d) * inv * Act<BF16>::load(g, d));
 }
 
 template <bool BF16>
@@ -45,9 +58,14 @@ __global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict
     Split<BF16>::store(y, y_plane, (size_t)blockIdx.x * D + d, xr[d] * inv * Act<BF16>::load(g, d));
 }
 
-// x[r] += sum_s part[s][r]; then y[r] = RMSNorm(x[r]) * g (y optional).
+// x[r] += sum_s part[s][r]; then y[r] = RMSNorm(x[r]) * g.  One workgroup of
+// 1024 threads per row, 4 consecutive columns per thread per pass; the loads
+// of all partial slices are independent, so they are in flight together.
+constexpr int kResThreads = 1024;
+constexpr int kResMaxPass = 2;   // D <= 8192
+
 template <bool BF16>
-__global__ __launch_bounds__(kRowThreads) void k_residual_norm(float* __restrict__ x,
+__global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict__ x,
                                                                const float* __restrict__ part,
                                                                int splits, int M, int D,
                                                                const typename Act<BF16>::T* __restrict__ g,
@@ -56,19 +74,32 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(float* __restrict
   __shared__ float red[16];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * D;
+  f32x4 v[kResMaxPass];
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float add = 0.f;
-    for (int s = 0; s < splits; ++s) add += part[((size_t)s * M + r) * D + d];
-    const float v = xr[d] + add;
-    xr[d] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4;
+    v[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (d < D) {
+      f32x4 add = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int s = 0; s < splits; ++s) add += *(const f32x4*)&part[((size_t)s * M + r) * D + d];
+      v[p] = *(const f32x4*)&xr[d] + add;
+      *(f32x4*)&xr[d] = v[p];
+      ss += v[p][0] * v[p][0] + v[p][1] * v[p][1] + v[p][2] * v[p][2] + v[p][3] * v[p][3];
+    }
   }
-  if (y == nullptr) return;
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Split<BF16>::store(y, y_plane, (size_t)r * D + d, xr[d] * inv * Act<BF16>::load(g, d));
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4;
+    if (d < D)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Split<BF16>::store(y, y_plane, (size_t)r * D + d + e,
+                           v[p][e] * inv * Act<BF16>::load(g, d + e));
+  }
 }
 
 // Sum the QKV partials, rotate q and k (rotate-half form) at position
@@ -124,13 +155,31 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, 
   Split<BF16>::store(h, h_plane, (size_t)r * I + c, sg * up);
 }
 
-__global__ void k_argmax_finalize(const uint64_t* __restrict__ best,
-                                  const int32_t* __restrict__ anchor, int M, int gamma,
-                                  int32_t* __restrict__ block_tokens) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= M) return;
-  const int j = r % gamma;
-  block_tokens[r] = j == 0 ? anchor[r / gamma] : (int32_t)argmax_key_index(best[r]);
+// Row r of the block: the anchor for j == 0, else the column of the largest
+// argmax key of row r over the GEMM's column groups (keys[g][r]).
+__global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restrict__ keys,
+                                                         int groups, int M,
+                                                         const int32_t* __restrict__ anchor,
+                                                         int gamma,
+                                                         int32_t* __restrict__ block_tokens) {
+  __shared__ uint64_t redk[4];
+  const int r = blockIdx.x;
+  uint64_t key = 0;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    const uint64_t k2 = keys[(size_t)g * M + r];
+    key = k2 > key ? k2 : key;
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(key, m);
+    key = o > key ? o : key;
+  }
+  if ((threadIdx.x & 63) == 0) redk[threadIdx.x >> 6] = key;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) key = redk[w] > key ? redk[w] : key;
+    const int j = r % gamma;
+    block_tokens[r] = j == 0 ? anchor[r / gamma] : (int32_t)argmax_key_index(key);
+  }
 }
 
 // c = RMSNorm(sum_s part[s]) * g   (the fused context H_t of each new token)
@@ -299,15 +348,16 @@ __global__ void k_verify_finalize(const uint64_t* __restrict__ best,
 }  // namespace
 
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
-                        int vocab, const void* embed, int D, float* x, uint64_t* best,
-                        uint32_t* err, hipStream_t st) {
+                        int vocab, const void* embed, int D, float* x, const void* g, float eps,
+                        void* y, size_t y_plane, uint32_t* err, hipStream_t st) {
   dim3 grid(batch * gamma);
   if (bf16)
     hipLaunchKernelGGL(k_embed<true>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
-                       vocab, (const uint16_t*)embed, D, x, best, err);
+                       vocab, (const uint16_t*)embed, D, x, (const uint16_t*)g, eps, y, y_plane,
+                       err);
   else
     hipLaunchKernelGGL(k_embed<false>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
-                       vocab, (const float*)embed, D, x, best, err);
+                       vocab, (const float*)embed, D, x, (const float*)g, eps, y, y_plane, err);
   return hipGetLastError();
 }
 
@@ -325,11 +375,12 @@ hipError_t launch_rmsnorm(bool bf16, const float* x, int M, int D, const void* g
 hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int splits, int M, int D,
                                 const void* g, float eps, void* y, size_t y_plane,
                                 hipStream_t st) {
+  if (D % 4 != 0 || D > kResThreads * 4 * kResMaxPass) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(k_residual_norm<true>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
+    hipLaunchKernelGGL(k_residual_norm<true>, dim3(M), dim3(kResThreads), 0, st, x, part, splits,
                        M, D, (const uint16_t*)g, eps, y, y_plane);
   else
-    hipLaunchKernelGGL(k_residual_norm<false>, dim3(M), dim3(kRowThreads), 0, st, x, part, splits,
+    hipLaunchKernelGGL(k_residual_norm<false>, dim3(M), dim3(kResThreads), 0, st, x, part, splits,
                        M, D, (const float*)g, eps, y, y_plane);
   return hipGetLastError();
 }
@@ -358,11 +409,11 @@ hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I,
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_finalize(const uint64_t* best, const int32_t* anchor, int batch, int gamma,
-                                  int32_t* block_tokens, hipStream_t st) {
+hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_t* anchor,
+                                  int batch, int gamma, int32_t* block_tokens, hipStream_t st) {
   const int M = batch * gamma;
-  hipLaunchKernelGGL(k_argmax_finalize, dim3((M + 255) / 256), dim3(256), 0, st, best, anchor, M,
-                     gamma, block_tokens);
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(M), dim3(256), 0, st, best, groups, M, anchor, gamma,
+                     block_tokens);
   return hipGetLastError();
 }
 

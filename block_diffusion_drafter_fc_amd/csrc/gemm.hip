@@ -4,19 +4,20 @@
 //   k_gemm_skinny  bf16, M <= 64 (the block rows of a few sequences).  The
 //                  product is a stream of the weight matrix: each lane loads
 //                  16 contiguous bytes of a weight row straight into the
-//                  B operand of a 16x16x32 bf16 MFMA (no LDS round trip),
-//                  the A operand (activations, L2-resident) is reused across
-//                  NT column tiles, and K is split over the waves of a group
-//                  (LDS reduction in fixed order) and over groups (fp32
-//                  partial slices) so that thousands of waves keep HBM busy.
+//                  B operand of a 16x16x32 bf16 MFMA (no LDS round trip); the
+//                  activations are staged once per workgroup in LDS and
+//                  shared by its 4 waves; K is split over workgroups (fp32
+//                  partial slices) so that about a thousand groups keep HBM
+//                  busy.
 //   k_gemm_tiled   bf16, larger M: 128x128 output tiles, both operands staged
 //                  through double-buffered LDS, 4 waves of 64x64.
 // With SPLIT the activations arrive as two bf16 planes (hi, lo) of an fp32
 // value and every weight fragment meets both: acc += hi*W + lo*W.
 //   k_gemm_f32     fp32 models: one thread per output, plain K loop.
 // All three can end in a fused row argmax (the LM head): the row maximum of
-// the tile is packed with its column into a 64-bit key (value order, then
-// lowest column) and merged with an integer atomic max, which is exact and
+// a group's columns is packed with its column into a 64-bit key (value
+// order, then lowest column) and stored per (group, row); a small kernel
+// takes the maximum key of each row over the groups, which is exact and
 // independent of the order in which groups finish.
 #include "common.h"
 #include "kernels.h"
@@ -47,17 +48,30 @@ DF_DEV uint64_t max16(uint64_t k) {
 }
 
 // ----------------------------------------------------------------------------
-template <int MT, int NT, int U, bool SPLIT>
+// Skinny product.  A workgroup of 4 waves owns 64*NT output columns and one
+// K slice [kbeg, kbeg + kps).  The activations of the slice are staged in
+// LDS in sub-chunks of KC = 32*U columns (both planes, double-buffered) and
+// shared by the 4 waves; each wave streams its own 16*NT weight rows from HBM
+// straight into MFMA B operands (lane (r, g) reads 16 contiguous bytes of
+// row n0 + 16t + r at column k + 32u + 8g).  Keeping the activations out of
+// the load queue matters: loads retire in order, so activation loads issued
+// between weight loads would make every MFMA wait for the slowest stream.
+template <int MT, int NT, int U, bool SPLIT, bool ARGMAX>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
-    int N, int K, int kpw, float* __restrict__ part, uint64_t* __restrict__ best,
+    int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
     float* __restrict__ logits) {
-  extern __shared__ float red[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  constexpr int KC = 32 * U, NP = SPLIT ? 2 : 1, ROWS = 16 * MT;
+  constexpr int CPR = KC / 8;              // 16-byte chunks per activation row
+  constexpr int NCH = ROWS * CPR / 256;    // chunks per thread per plane
+  static_assert(ROWS * CPR % 256 == 0, "sub-chunk must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][ROWS][KC + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * NT;
+  const bool active = n0 < N;
   const int split = blockIdx.y;
-  const int kbeg = (split * W + wave) * kpw;
+  const int kbeg = split * kps;
 
   const uint16_t* bp[NT];
 #pragma unroll
@@ -66,15 +80,18 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
     row = row < N ? row : N - 1;
     bp[t] = seg_row_bf16(w, row, K) + kbeg + lg * 8;
   }
-  const uint16_t* ap[MT];
-  const uint16_t* apl[MT];
+  // activation chunks this thread stages: row r_i, column c_i of a sub-chunk
+  const uint16_t* ag[NCH];
+  int srow[NCH], scol[NCH];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    int row = m * 16 + lr;
-    row = row < M ? row : M - 1;
-    ap[m] = A + (size_t)row * lda + kbeg + lg * 8;
-    apl[m] = SPLIT ? Alo + (size_t)row * lda + kbeg + lg * 8 : ap[m];
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * 256;
+    srow[i] = c / CPR;
+    scol[i] = (c % CPR) * 8;
+    const int r = srow[i] < M ? srow[i] : M - 1;
+    ag[i] = A + (size_t)r * lda + kbeg + scol[i];
   }
+  const size_t lo_off = SPLIT ? (size_t)(Alo - A) : 0;
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -82,75 +99,78 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int iters = kpw / (32 * U);
-  u32x4 bcur[U][NT];
+  // Issue order per sub-chunk: the next activation chunk, then the next
+  // weight batch.  Loads retire in order, so the LDS store of the
+  // activations never waits for weights, and two weight batches per wave
+  // (the one being multiplied and the next) are in flight.
+  u32x4 ra0[NCH], ra1[NCH];
+  u32x4 bc[U][NT], bn[U][NT];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) bcur[u][t] = ld16(bp[t] + u * 32);
-
-  for (int it = 0; it < iters; ++it) {
-    const int kk = it * 32 * U;
-    u32x4 bnxt[U][NT];
-    if (it + 1 < iters) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) bnxt[u][t] = ld16(bp[t] + kk + 32 * U + u * 32);
-    }
-    u32x4 a[U][MT], al[U][MT];
+  for (int i = 0; i < NCH; ++i) {
+    ra0[i] = ld16(ag[i]);
+    if (SPLIT) ra1[i] = ld16(ag[i] + lo_off);
+  }
+  if (active) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        a[u][m] = ld16(ap[m] + kk + u * 32);
-        if (SPLIT) al[u][m] = ld16(apl[m] + kk + u * 32);
+      for (int t = 0; t < NT; ++t) bc[u][t] = ld16(bp[t] + u * 32);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    st16(&As[0][0][srow[i]][scol[i]], ra0[i]);
+    if (SPLIT) st16(&As[0][NP - 1][srow[i]][scol[i]], ra1[i]);
+  }
+  __syncthreads();
+
+  int buf = 0;
+  for (int k = 0; k < kps; k += KC) {
+    const bool more = k + KC < kps;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        ra0[i] = ld16(ag[i] + k + KC);
+        if (SPLIT) ra1[i] = ld16(ag[i] + lo_off + k + KC);
+      }
+      if (active) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) bn[u][t] = ld16(bp[t] + k + KC + u * 32);
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 a = ld16(&As[buf][0][m * 16 + lr][u * 32 + lg * 8]);
+          u32x4 al;
+          if (SPLIT) al = ld16(&As[buf][NP - 1][m * 16 + lr][u * 32 + lg * 8]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            acc[m][t] = mfma_16x16x32(a, bc[u][t], acc[m][t]);
+            if (SPLIT) acc[m][t] = mfma_16x16x32(al, bc[u][t], acc[m][t]);
+          }
+        }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        st16(&As[buf ^ 1][0][srow[i]][scol[i]], ra0[i]);
+        if (SPLIT) st16(&As[buf ^ 1][NP - 1][srow[i]][scol[i]], ra1[i]);
       }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[m][t] = mfma_16x16x32(a[u][m], bcur[u][t], acc[m][t]);
-          if (SPLIT) acc[m][t] = mfma_16x16x32(al[u][m], bcur[u][t], acc[m][t]);
-        }
-    if (it + 1 < iters) {
-#pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bcur[u][t] = bnxt[u][t];
-    }
-  }
-
-  // K split inside the group: waves 1..W-1 hand their sums to wave 0, which
-  // adds them in wave order.
-  constexpr int E = MT * NT * 4;
-  if (W > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            red[((size_t)(wave - 1) * E + (m * NT + t) * 4 + i) * 64 + lane] = acc[m][t][i];
+        for (int t = 0; t < NT; ++t) bc[u][t] = bn[u][t];
     }
     __syncthreads();
-    if (wave == 0) {
-      for (int w2 = 1; w2 < W; ++w2)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[m][t][i] += red[((size_t)(w2 - 1) * E + (m * NT + t) * 4 + i) * 64 + lane];
-    }
+    buf ^= 1;
   }
-  if (wave != 0) return;
 
-  if (best == nullptr) {
+  if (!ARGMAX) {
+    if (!active) return;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -166,6 +186,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
       }
     return;
   }
+  // Row argmax of the group's 64*NT columns: per wave over its columns
+  // (lanes, then tiles), then over the 4 waves in LDS; one key per
+  // (group, row) goes to keys[blockIdx.x][row] -- no atomics.
+  __shared__ uint64_t wkeys[4][ROWS];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -175,7 +199,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int col = n0 + t * 16 + lr;
-        if (col < N) {
+        if (active && col < N) {
           const float v = acc[m][t][i];
           const uint64_t k2 = argmax_key(v, (uint32_t)col);
           key = k2 > key ? k2 : key;
@@ -183,15 +207,22 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         }
       }
       key = max16(key);
-      if (lr == 0 && row < M) atomicMax((unsigned long long*)&best[row], (unsigned long long)key);
+      if (lr == 0) wkeys[wave][row] = key;
     }
+  __syncthreads();
+  if (tid < ROWS && tid < M) {
+    uint64_t key = wkeys[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) key = wkeys[w][tid] > key ? wkeys[w][tid] : key;
+    best[(size_t)blockIdx.x * M + tid] = key;
+  }
 }
 
 // ----------------------------------------------------------------------------
 constexpr int TBM = 128, TBN = 128, TPAD = 8;
 
 // BK = 64 without split, 32 with split (two A planes must fit LDS).
-template <bool SPLIT, int TBK>
+template <bool SPLIT, int TBK, bool ARGMAX>
 __global__ __launch_bounds__(256) void k_gemm_tiled(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
@@ -288,7 +319,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
     __syncthreads();
   }
 
-  if (best == nullptr) {
+  if (!ARGMAX) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -304,11 +335,15 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
       }
     return;
   }
+  // Row argmax of the tile's 128 columns: per wave (lanes, then tiles), then
+  // over the two column halves in LDS; keys[blockIdx.x][row], no atomics.
+  __shared__ uint64_t hkeys[2][TBM];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * 64 + a * 16 + lg * 4 + i;
+      const int rloc = wm * 64 + a * 16 + lg * 4 + i;
+      const int row = m0 + rloc;
       uint64_t key = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -321,8 +356,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
         }
       }
       key = max16(key);
-      if (lr == 0 && row < M) atomicMax((unsigned long long*)&best[row], (unsigned long long)key);
+      if (lr == 0) hkeys[wn][rloc] = key;
     }
+  __syncthreads();
+  if (tid < TBM && m0 + tid < M) {
+    const uint64_t k0 = hkeys[0][tid], k1 = hkeys[1][tid];
+    best[(size_t)blockIdx.x * M + m0 + tid] = k0 > k1 ? k0 : k1;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -347,24 +387,29 @@ __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, in
     uint64_t o = shfl_xor_u64(key, s);
     key = o > key ? o : key;
   }
-  if (threadIdx.x == 0) atomicMax((unsigned long long*)&best[m], (unsigned long long)key);
+  if (threadIdx.x == 0) best[(size_t)blockIdx.x * M + m] = key;
 }
 
 template <int MT, int NT, int U>
 hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda, int M,
                       const WSeg& w, int N, int K, float* part, uint64_t* best, float* logits,
                       hipStream_t st) {
-  dim3 grid((N + 16 * NT - 1) / (16 * NT), p.splits);
-  dim3 block(64 * p.waves);
-  size_t lds = p.waves > 1 ? (size_t)(p.waves - 1) * MT * NT * 4 * 64 * sizeof(float) : 0;
-  if (Alo)
-    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true>), grid, block, lds, st,
-                       (const uint16_t*)A, (const uint16_t*)Alo, lda, M, w, N, K, p.kpw, part,
-                       best, logits);
+  dim3 grid((N + 64 * NT - 1) / (64 * NT), p.splits);
+  dim3 block(256);
+  const uint16_t* a = (const uint16_t*)A;
+  const uint16_t* al = (const uint16_t*)Alo;
+  if (al && best)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true, true>), grid, block, 0, st, a, al, lda, M,
+                       w, N, K, p.kpw, part, best, logits);
+  else if (al)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true, false>), grid, block, 0, st, a, al, lda, M,
+                       w, N, K, p.kpw, part, best, logits);
+  else if (best)
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false, true>), grid, block, 0, st, a, al, lda,
+                       M, w, N, K, p.kpw, part, best, logits);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false>), grid, block, lds, st,
-                       (const uint16_t*)A, (const uint16_t*)nullptr, lda, M, w, N, K, p.kpw,
-                       part, best, logits);
+    hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false, false>), grid, block, 0, st, a, al, lda,
+                       M, w, N, K, p.kpw, part, best, logits);
   return hipGetLastError();
 }
 
@@ -388,23 +433,22 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
   if (M <= 64) {
     p.kind = GEMM_SKINNY;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.nt = ((N / 16) % 2 == 0) ? 2 : 1;
-    p.unroll = p.mt == 1 ? 8 : (p.mt == 2 ? 4 : 2);
-    const int groups = (N + 16 * p.nt - 1) / (16 * p.nt);
-    const int nk = K / (32 * p.unroll);   // loop iterations without any split
-    // Split K until about 2048 waves are in flight, keeping >= 2 iterations
-    // per wave.
-    int T = 1;
-    for (int t = 1; t <= nk; ++t) {
-      if (nk % t) continue;
-      if (nk / t < 2 && t > 1) break;
-      if (argmax && t != 1 && t != 2 && t != 4) continue;   // argmax: one group per tile
-      T = t;
-      if ((long)groups * t >= 2048) break;
+    p.nt = 1;
+    p.unroll = 8 / p.mt;
+    p.waves = 4;
+    const int groups = (N + 64 * p.nt - 1) / (64 * p.nt);
+    const int nk = K / (32 * p.unroll);   // activation sub-chunks along K
+    // Split K across workgroups until about 1024 groups are in flight.
+    int S = 1;
+    if (!argmax) {
+      for (int t = 1; t <= nk; ++t) {
+        if (nk % t) continue;
+        S = t;
+        if ((long)groups * t >= 1024) break;
+      }
     }
-    p.waves = T % 4 == 0 ? 4 : (T % 2 == 0 ? 2 : 1);
-    p.splits = T / p.waves;
-    p.kpw = K / T;
+    p.splits = S;
+    p.kpw = K / S;
     return p;
   }
   p.kind = GEMM_TILED;
@@ -420,6 +464,12 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
   return p;
 }
 
+int gemm_argmax_groups(const GemmPlan& p, int N) {
+  if (p.kind == GEMM_F32) return (N + 63) / 64;
+  if (p.kind == GEMM_TILED) return (N + TBN - 1) / TBN;
+  return (N + 64 * p.nt - 1) / (64 * p.nt);
+}
+
 hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
                        float* logits, hipStream_t st) {
@@ -433,21 +483,26 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
   (void)bf16;
   if (p.kind == GEMM_TILED) {
     dim3 grid((N + TBN - 1) / TBN, (M + TBM - 1) / TBM, p.splits);
-    if (Alo)
-      hipLaunchKernelGGL((k_gemm_tiled<true, 32>), grid, dim3(256), 0, st, (const uint16_t*)A,
-                         (const uint16_t*)Alo, lda, M, w, N, K, p.kpw, part, best, logits);
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* al = (const uint16_t*)Alo;
+    if (al && best)
+      hipLaunchKernelGGL((k_gemm_tiled<true, 32, true>), grid, dim3(256), 0, st, a, al, lda, M, w,
+                         N, K, p.kpw, part, best, logits);
+    else if (al)
+      hipLaunchKernelGGL((k_gemm_tiled<true, 32, false>), grid, dim3(256), 0, st, a, al, lda, M,
+                         w, N, K, p.kpw, part, best, logits);
+    else if (best)
+      hipLaunchKernelGGL((k_gemm_tiled<false, 64, true>), grid, dim3(256), 0, st, a, al, lda, M,
+                         w, N, K, p.kpw, part, best, logits);
     else
-      hipLaunchKernelGGL((k_gemm_tiled<false, 64>), grid, dim3(256), 0, st, (const uint16_t*)A,
-                         (const uint16_t*)nullptr, lda, M, w, N, K, p.kpw, part, best, logits);
+      hipLaunchKernelGGL((k_gemm_tiled<false, 64, false>), grid, dim3(256), 0, st, a, al, lda, M,
+                         w, N, K, p.kpw, part, best, logits);
     return hipGetLastError();
   }
 #define DF_SKINNY(MT, NT, U) \
   if (p.mt == MT && p.nt == NT) return run_skinny<MT, NT, U>(p, A, Alo, lda, M, w, N, K, part, best, logits, st)
-  DF_SKINNY(1, 2, 8);
   DF_SKINNY(1, 1, 8);
-  DF_SKINNY(2, 2, 4);
   DF_SKINNY(2, 1, 4);
-  DF_SKINNY(4, 2, 2);
   DF_SKINNY(4, 1, 2);
 #undef DF_SKINNY
   return hipErrorInvalidValue;

@@ -34,8 +34,10 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax);
 // models, with Alo the lo plane of a split activation (or null when A is an
 // exact bf16 input).  Without `best`: part[s][M][N] (fp32) receives the
 // partial product of split s.  With `best` (argmax mode, splits == 1):
-// best[row] is raised (atomic max) to the argmax key of each row, and
-// logits[M][N] receives the fp32 products when non-null.
+// best[g][row] receives the argmax key of row `row` over the columns of
+// group g (gemm_argmax_groups groups), and logits[M][N] receives the fp32
+// products when non-null.
+int gemm_argmax_groups(const GemmPlan& p, int N);
 hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
                        float* logits, hipStream_t stream);
@@ -68,8 +70,8 @@ hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part
 
 // ---- element-wise and row kernels -----------------------------------------
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
-                        int vocab, const void* embed, int D, float* x, uint64_t* best,
-                        uint32_t* err, hipStream_t stream);
+                        int vocab, const void* embed, int D, float* x, const void* g, float eps,
+                        void* y, size_t y_plane, uint32_t* err, hipStream_t stream);
 // Outputs named y, q, h, c are transient activations: fp32 for fp32 models,
 // split hi/lo bf16 planes for bf16 models (the lo plane starts *_plane
 // elements after the hi plane).
@@ -83,8 +85,10 @@ hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, 
                                size_t q_plane, float* k, float* v, hipStream_t stream);
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
                          size_t h_plane, hipStream_t stream);
-hipError_t launch_argmax_finalize(const uint64_t* best, const int32_t* anchor, int batch, int gamma,
-                                  int32_t* block_tokens, hipStream_t stream);
+// block_tokens[r] = r % gamma == 0 ? anchor[r / gamma] : column of the
+// largest key of row r over best[0..groups)[r].
+hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_t* anchor,
+                                  int batch, int gamma, int32_t* block_tokens, hipStream_t stream);
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
                               float eps, void* c, size_t c_plane, hipStream_t stream);
 hipError_t launch_inject_scatter(bool bf16, const float* part, int splits, int n_tok,
