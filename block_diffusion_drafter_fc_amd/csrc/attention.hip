@@ -8,9 +8,10 @@
 //
 // Split-context (flash-decode) layout: workgroup (s, kvh, b) owns one KV head
 // of one sequence and one slice of keys -- context slice s < n_ctx_splits, or
-// the block's own keys (s == n_ctx_splits, k_attn_block) -- and writes an
+// the block's own keys (s == n_ctx_splits) -- and writes an
 // unnormalised partial (running max in log2 units, sum of weights, weighted
-// values) that k_attn_combine merges in split order.
+// values) that k_attn_combine merges in split order.  Both kinds of slice run
+// in one launch (the block's slice takes a uniform branch).
 //
 // bf16 context kernel: one wave per query head of the KV group, the gamma
 // (<= 16) queries of that head form the N side of 16x16x32 MFMAs.  32 cached
@@ -30,15 +31,101 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxCtxSplits = 256;            // bounded by plan_attention
 constexpr int kMaxParts = kMaxCtxSplits + 1;  // + the block's own keys
 
+// The block's own gamma keys (workgroup s == n_ctx_splits of the same grid):
+// fp32 on the vector ALUs, since the block keys and values are transient fp32
+// values.  Wave w takes query head kvh*G + w; lane = (query j = lane / 4,
+// quarter qd = lane % 4 of the head dimension).  Each lane forms partial
+// dot products over its quarter for all gamma keys; two shuffles complete
+// them, so every lane of a query holds all its scores.
+template <int DH>
+__device__ __forceinline__ void attn_block_keys(
+    const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
+    const float* __restrict__ vb, int gamma, int Hq, int Hkv, int kvh, int b, int B, int split,
+    float* __restrict__ part_o, float* __restrict__ part_ml, float (*ks)[DH + 4],
+    float (*vs)[DH + 4]) {
+  constexpr int QW = DH / 4;   // head dimensions per lane
+  const int G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = kvh * G + wave;
+  for (int c = threadIdx.x; c < gamma * (DH / 4); c += blockDim.x) {
+    const int key = c / (DH / 4), d = (c % (DH / 4)) * 4;
+    const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * DH + d;
+    *(f32x4*)&ks[key][d] = *(const f32x4*)&kb[off];
+    *(f32x4*)&vs[key][d] = *(const f32x4*)&vb[off];
+  }
+  __syncthreads();
+  const int j = lane >> 2, qd = lane & 3;
+  const int jj = j < gamma ? j : 0;
+  float qv[QW];
+  {
+    const size_t off = ((size_t)(b * gamma + jj) * Hq + h) * DH + qd * QW;
+#pragma unroll
+    for (int c = 0; c < QW / 8; ++c) {
+      const u32x4 hi = ld16(q + off + c * 8), lo = ld16(q + q_plane + off + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[c * 8 + 2 * e] = bf2f((uint16_t)(hi[e] & 0xFFFFu)) + bf2f((uint16_t)(lo[e] & 0xFFFFu));
+        qv[c * 8 + 2 * e + 1] = bf2f((uint16_t)(hi[e] >> 16)) + bf2f((uint16_t)(lo[e] >> 16));
+      }
+    }
+  }
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  float sc[16];
+#pragma unroll
+  for (int key = 0; key < 16; ++key) {
+    float acc = 0.f;
+    if (key < gamma) {
+#pragma unroll
+      for (int e = 0; e < QW; ++e) acc = fmaf(qv[e], ks[key][qd * QW + e], acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    sc[key] = key < gamma ? acc * sl2 : -INFINITY;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int key = 1; key < 16; ++key) mx = fmaxf(mx, sc[key]);
+  float l = 0.f;
+#pragma unroll
+  for (int key = 0; key < 16; ++key) {
+    sc[key] = key < gamma ? exp2f(sc[key] - mx) : 0.f;
+    l += sc[key];
+  }
+  if (j < gamma) {
+    const size_t pr = ((size_t)(split * B + b) * Hq + h) * gamma + j;
+#pragma unroll
+    for (int e = 0; e < QW; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int key = 0; key < 16; ++key) acc = fmaf(sc[key], vs[key][qd * QW + e], acc);
+      part_o[pr * DH + qd * QW + e] = acc;
+    }
+    if (qd == 0) {
+      part_ml[pr * 2 + 0] = mx;
+      part_ml[pr * 2 + 1] = l;
+    }
+  }
+}
+
 template <int DH>
 __global__ __launch_bounds__(512) void k_attn_bf16(
-    const uint16_t* __restrict__ q, size_t q_plane, const uint16_t* __restrict__ pages,
-    int n_pages, const int32_t* __restrict__ page_table, int max_pages,
-    const int32_t* __restrict__ ctx_lens, int gamma, int Hq, int Hkv, int layer, int chunk,
+    const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
+    const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
+    int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[32][DH + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][32 + 8];
+  // LDS: the context path uses Ks/Vt, the block path two fp32 key/value tiles.
+  constexpr size_t CTX_LDS = (size_t)32 * (DH + 8) * 2 + (size_t)DH * (32 + 8) * 2;
+  constexpr size_t BLK_LDS = (size_t)2 * 16 * (DH + 4) * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
+  uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])lds;
+  uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (size_t)32 * (DH + 8) * 2);
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  if (s == n_ctx_splits) {
+    attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
+                        (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4));
+    return;
+  }
   const int G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int h = kvh * G + wave;
@@ -166,84 +253,6 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
   }
 }
 
-// The block's own gamma keys (bf16 models): fp32 on the vector ALUs, since
-// the block keys and values are transient fp32 values.  One wave per (query
-// head, sequence): q, k, v of the block are staged in LDS with 16-byte loads
-// that are all in flight together; lane = (query j = lane / 4, key group
-// lane % 4).  Writes the partial of split index `split`.
-__global__ __launch_bounds__(64) void k_attn_block(
-    const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
-    const float* __restrict__ vb, int gamma, int Hq, int Hkv, int dh, int split,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ float qs[16][132];
-  __shared__ float ks[16][132];
-  __shared__ float vs[16][132];
-  __shared__ float ps[16][17];
-  const int h = blockIdx.x, b = blockIdx.y, B = gridDim.y;
-  const int kvh = h / (Hq / Hkv), lane = threadIdx.x;
-  const int d4 = dh / 4, d8 = dh / 8;
-  // k, v: gamma*dh/4 float4 each; q: gamma*dh/8 chunks of 8 bf16 per plane
-#pragma unroll 4
-  for (int c = lane; c < gamma * d4; c += 64) {
-    const int key = c / d4, d = (c % d4) * 4;
-    const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * dh + d;
-    *(f32x4*)&ks[key][d] = *(const f32x4*)&kb[off];
-    *(f32x4*)&vs[key][d] = *(const f32x4*)&vb[off];
-  }
-#pragma unroll 4
-  for (int c = lane; c < gamma * d8; c += 64) {
-    const int j = c / d8, d = (c % d8) * 8;
-    const size_t off = ((size_t)(b * gamma + j) * Hq + h) * dh + d;
-    const u32x4 hi = ld16(q + off), lo = ld16(q + q_plane + off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qs[j][d + 2 * e] = bf2f((uint16_t)(hi[e] & 0xFFFFu)) + bf2f((uint16_t)(lo[e] & 0xFFFFu));
-      qs[j][d + 2 * e + 1] = bf2f((uint16_t)(hi[e] >> 16)) + bf2f((uint16_t)(lo[e] >> 16));
-    }
-  }
-  __syncthreads();
-  const int j = lane >> 2, kg = lane & 3;
-  const float sl2 = kLog2e / sqrtf((float)dh);
-  float sc[4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = kg + 4 * t;
-    sc[t] = -INFINITY;
-    if (j < gamma && key < gamma) {
-      float acc = 0.f;
-      for (int d = 0; d < dh; ++d) acc = fmaf(qs[j][d], ks[key][d], acc);
-      sc[t] = acc * sl2;
-    }
-    mx = fmaxf(mx, sc[t]);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  float l = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = kg + 4 * t;
-    const float p = (j < gamma && key < gamma) ? exp2f(sc[t] - mx) : 0.f;
-    ps[j][key] = p;
-    l += p;
-  }
-  l += __shfl_xor(l, 1, 64);
-  l += __shfl_xor(l, 2, 64);
-  __syncthreads();
-  if (j < gamma) {
-    const size_t pr = ((size_t)(split * B + b) * Hq + h) * gamma + j;
-    for (int d = kg; d < dh; d += 4) {
-      float acc = 0.f;
-      for (int key = 0; key < gamma; ++key) acc = fmaf(ps[j][key], vs[key][d], acc);
-      part_o[pr * dh + d] = acc;
-    }
-    if (kg == 0) {
-      part_ml[pr * 2 + 0] = mx;
-      part_ml[pr * 2 + 1] = l;
-    }
-  }
-}
-
 // fp32 models: one workgroup per (query, head, sequence) over all keys, in
 // chunks of 256 with an online softmax; writes the same partial layout as a
 // single split.
@@ -357,12 +366,16 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   __syncthreads();
   float num = 0.f, den = 0.f;
   if (d < dh) {
-#pragma unroll 8
+    // loads are unconditional (every slot is written: empty splits carry
+    // weight 0 and a stale value that the select drops) so they can be
+    // issued together
+#pragma unroll 16
     for (int s = 0; s < n_parts; ++s) {
       const float ww = wgt[s];
-      if (ww == 0.f) continue;
-      num += ww * part_o[(pr0 + s * stride) * dh + d];
-      den += ww * part_ml[(pr0 + s * stride) * 2 + 1];
+      const float ov = part_o[(pr0 + s * stride) * dh + d];
+      const float lv = part_ml[(pr0 + s * stride) * 2 + 1];
+      num += ww != 0.f ? ww * ov : 0.f;
+      den += ww != 0.f ? ww * lv : 0.f;
     }
     const float v = den > 0.f ? num / den : 0.f;
     Split<BF16>::store(o, o_plane, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
@@ -394,24 +407,23 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
                        a.part_o, a.part_ml, a.err);
     return hipGetLastError();
   }
-  dim3 grid(p.n_ctx_splits, a.Hkv, a.batch);
+  // splits 0 .. n_ctx_splits-1: cached context; split n_ctx_splits: block keys
+  dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
   dim3 block(64 * (a.Hq / a.Hkv));
+  if (a.gamma > 16) return hipErrorInvalidValue;
   if (a.dh == 128) {
     hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
-                       (const uint16_t*)a.pages, a.n_pages, a.page_table, a.max_pages,
-                       a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk, a.part_o, a.part_ml,
-                       a.err);
+                       (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
+                       a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer,
+                       p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
   } else if (a.dh == 64) {
     hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
-                       (const uint16_t*)a.pages, a.n_pages, a.page_table, a.max_pages,
-                       a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk, a.part_o, a.part_ml,
-                       a.err);
+                       (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
+                       a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer,
+                       p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
   } else {
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_attn_block, dim3(a.Hq, a.batch), dim3(64), 0, st, (const uint16_t*)a.q,
-                     a.q_plane, (const float*)a.k, (const float*)a.v, a.gamma, a.Hq, a.Hkv, a.dh,
-                     p.n_ctx_splits, a.part_o, a.part_ml);
   return hipGetLastError();
 }
 

@@ -14,15 +14,15 @@ constexpr int kRowThreads = 256;
 
 // Row r = b*gamma + j of the block: token (j == 0 ? anchor[b] : mask), its
 // embedding into the fp32 residual x, and y = RMSNorm(x) * g (the first
-// layer's attention norm).
+// layer's attention norm).  1024 threads, 4 columns per thread per pass.
 template <bool BF16>
-__global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict__ anchor,
-                                                       int gamma, int mask_id, int vocab,
-                                                       const typename Act<BF16>::T* __restrict__ E,
-                                                       int D, float* __restrict__ x,
-                                                       const typename Act<BF16>::T* __restrict__ g,
-                                                       float eps, void* __restrict__ y,
-                                                       size_t y_plane, uint32_t* err) {
+__global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anchor,
+                                                int gamma, int mask_id, int vocab,
+                                                const typename Act<BF16>::T* __restrict__ E,
+                                                int D, float* __restrict__ x,
+                                                const typename Act<BF16>::T* __restrict__ g,
+                                                float eps, void* __restrict__ y,
+                                                size_t y_plane, uint32_t* err) {
   __shared__ float red[16];
   const int r = blockIdx.x, b = r / gamma, j = r % gamma;
   int tok = j == 0 ? anchor[b] : mask_id;
@@ -30,17 +30,28 @@ __global__ __launch_bounds__(kRowThreads) void k_embed(const int32_t* __restrict
     if (threadIdx.x == 0) set_dev_error(err, 4u);
     tok = 0;
   }
+  float v[2][4];
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    const float v = Act<BF16>::load(E, (size_t)tok * D + d);
-    x[(size_t)r * D + d] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int d = (p * 1024 + threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[p][e] = d < D ? Act<BF16>::load(E, (size_t)tok * D + d + e) : 0.f;
+      ss += v[p][e] * v[p][e];
+    }
+    if (d < D) *(f32x4*)&x[(size_t)r * D + d] = f32x4{v[p][0], v[p][1], v[p][2], v[p][3]};
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Split<BF16>::store(y, y_plane, (size_t)r * D + d,
-                       Act<BF16>::load(E, (size_t)tok * D + d) * inv * Act<BF16>::load(g, d));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int d = (p * 1024 + threadIdx.x) * 4;
+    if (d < D)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Split<BF16>::store(y, y_plane, (size_t)r * D + d + e, v[p][e] * inv * Act<BF16>::load(g, d + e));
+  }
 }
 
 template <bool BF16>
@@ -115,6 +126,7 @@ __global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M
   (void)M;
   const int col = hh * dh + i;
   float a = 0.f, c2 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     a += part[((size_t)s * M + r) * N + col];
     c2 += part[((size_t)s * M + r) * N + col + half];
@@ -146,6 +158,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, 
   const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= I) return;
   float gt = 0.f, up = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float* p = part + ((size_t)s * M + r) * (2 * (size_t)I);
     gt += p[c];
@@ -182,27 +195,39 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restr
   }
 }
 
-// c = RMSNorm(sum_s part[s]) * g   (the fused context H_t of each new token)
+// c = RMSNorm(sum_s part[s]) * g   (the fused context H_t of each new token).
+// Same shape of work as k_residual_norm: 1024 threads per token, 4 columns
+// per thread per pass, all partial loads in flight together.
 template <bool BF16>
-__global__ __launch_bounds__(kRowThreads) void k_inject_norm(const float* __restrict__ part,
+__global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __restrict__ part,
                                                              int splits, int n, int D,
                                                              const typename Act<BF16>::T* __restrict__ g,
                                                              float eps, void* __restrict__ c,
                                                              size_t c_plane) {
   __shared__ float red[16];
-  extern __shared__ float row[];
   const int t = blockIdx.x;
+  f32x4 v[kResMaxPass];
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float u = 0.f;
-    for (int s = 0; s < splits; ++s) u += part[((size_t)s * n + t) * D + d];
-    row[d] = u;
-    ss = fmaf(u, u, ss);
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4;
+    v[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (d < D) {
+#pragma unroll 8
+      for (int s = 0; s < splits; ++s) v[p] += *(const f32x4*)&part[((size_t)s * n + t) * D + d];
+      ss += v[p][0] * v[p][0] + v[p][1] * v[p][1] + v[p][2] * v[p][2] + v[p][3] * v[p][3];
+    }
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += blockDim.x)
-    Split<BF16>::store(c, c_plane, (size_t)t * D + d, row[d] * inv * Act<BF16>::load(g, d));
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4;
+    if (d < D)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Split<BF16>::store(c, c_plane, (size_t)t * D + d + e, v[p][e] * inv * Act<BF16>::load(g, d + e));
+  }
 }
 
 // Token t of the inject batch belongs to sequence b with cu_new[b] <= t <
@@ -237,6 +262,7 @@ __global__ void k_inject_scatter(const float* __restrict__ part, int splits, int
   const size_t N = (size_t)n_layers * 2 * Hkv * dh;
   const size_t col = (size_t)y * dh + i;
   float a = 0.f, c2 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     a += part[((size_t)s * n_tok + t) * N + col];
     c2 += part[((size_t)s * n_tok + t) * N + col + half];
@@ -351,12 +377,13 @@ hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, 
                         int vocab, const void* embed, int D, float* x, const void* g, float eps,
                         void* y, size_t y_plane, uint32_t* err, hipStream_t st) {
   dim3 grid(batch * gamma);
+  if (D % 4 != 0 || D > 8192) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(k_embed<true>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
+    hipLaunchKernelGGL(k_embed<true>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
                        vocab, (const uint16_t*)embed, D, x, (const uint16_t*)g, eps, y, y_plane,
                        err);
   else
-    hipLaunchKernelGGL(k_embed<false>, grid, dim3(kRowThreads), 0, st, anchor, gamma, mask_id,
+    hipLaunchKernelGGL(k_embed<false>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
                        vocab, (const float*)embed, D, x, (const float*)g, eps, y, y_plane, err);
   return hipGetLastError();
 }
@@ -419,12 +446,12 @@ hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_
 
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
                               float eps, void* c, size_t c_plane, hipStream_t st) {
-  const size_t lds = (size_t)D * sizeof(float);
+  if (D % 4 != 0 || D > kResThreads * 4 * kResMaxPass) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(k_inject_norm<true>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n, D,
+    hipLaunchKernelGGL(k_inject_norm<true>, dim3(n), dim3(kResThreads), 0, st, part, splits, n, D,
                        (const uint16_t*)g, eps, c, c_plane);
   else
-    hipLaunchKernelGGL(k_inject_norm<false>, dim3(n), dim3(kRowThreads), lds, st, part, splits, n,
+    hipLaunchKernelGGL(k_inject_norm<false>, dim3(n), dim3(kResThreads), 0, st, part, splits, n,
                        D, (const float*)g, eps, c, c_plane);
   return hipGetLastError();
 }
