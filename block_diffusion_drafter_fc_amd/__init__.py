@@ -14,11 +14,11 @@ import ctypes
 import dataclasses
 
 from . import _abi
-from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DFLASH_BF16, DFLASH_F32, MAX_BLOCK,
-                   MAX_LAYERS, STATE_BYTES)
+from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_XCD, DFLASH_BF16, DFLASH_F32,
+                   MAX_BLOCK, MAX_LAYERS, STATE_BYTES)
 
 __all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy", "load_library",
-           "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "MAX_BLOCK", "MAX_LAYERS"]
+           "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "DEVERR_XCD", "MAX_BLOCK", "MAX_LAYERS"]
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
 GLOBAL_KEYS = ("fc_w", "fc_norm", "embed", "lm_head", "final_norm")

@@ -11,10 +11,10 @@ DFLASH_OK = 0
 STATUS_NAMES = {0: "DFLASH_OK", -1: "DFLASH_E_INVAL", -2: "DFLASH_E_SHAPE", -3: "DFLASH_E_DTYPE",
                 -4: "DFLASH_E_CAPACITY", -5: "DFLASH_E_HIP", -6: "DFLASH_E_DEVICE"}
 DFLASH_F32, DFLASH_BF16 = 0, 1
-DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN = 1, 2, 4
+DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_XCD = 1, 2, 4, 8
 MAX_LAYERS = 16
 MAX_BLOCK = 16
-STATE_BYTES = 256
+STATE_BYTES = 16384
 
 EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_bytes",
             "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",

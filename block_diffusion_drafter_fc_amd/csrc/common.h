@@ -7,6 +7,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define DF_DEV __device__ __forceinline__
 
@@ -17,6 +19,13 @@ DF_DEV uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Two fp32 values -> two bf16 in one word (a in the low half), round to
+// nearest, ties to even: one v_cvt_pk_bf16_f32, equal to f2bf for finite
+// inputs.
+DF_DEV uint32_t pack_bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Round an fp32 value to the nearest bf16 value, kept in fp32.

@@ -16,6 +16,7 @@ struct dflash_model {
   dflash_config cfg;
   dflash_weights w;
   uint32_t* err;   // device error word (in the caller's state buffer)
+  unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
   int device;
   bool bf16;
   bool prof_on;
@@ -69,11 +70,38 @@ size_t part_floats(bool bf16, int M, int N, int K) {
   return (size_t)p.splits * M * N;
 }
 
+// Counters after the error word in the state buffer.
+constexpr size_t kCtrOffset = 256;
+constexpr int kMaxCounters = (int)((DFLASH_STATE_BYTES - kCtrOffset) / 8);
+
+// bf16 models with at most 64 product rows run the fused skinny products
+// (epilogues inside the product kernels); larger M and fp32 models run the
+// plain products followed by separate epilogue kernels.
+bool use_fused(const dflash_model* m, int M) {
+  if (!m->bf16 || M > 64) return false;
+  const dflash_config& c = m->cfg;
+  const int qkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int kvn = 2 * c.n_layers * c.n_kv_heads * c.head_dim;
+  const int tiles[] = {skinny_tiles(SO_QKV, qkv, c.head_dim, c.intermediate),
+                       skinny_tiles(SO_SWIGLU, 2 * c.intermediate, c.head_dim, c.intermediate),
+                       skinny_tiles(SO_RESID, c.hidden, c.head_dim, c.intermediate),
+                       skinny_tiles(SO_KV, kvn, c.head_dim, c.intermediate)};
+  for (int t : tiles)
+    if (t < 0 || t > kMaxCounters) return false;
+  return true;
+}
+
+size_t skinny_part_floats(int M, int N, int K, int out, int dh) {
+  const GemmPlan p = plan_skinny(M, N, K, out, dh);
+  return (size_t)p.splits * M * N;
+}
+
 struct DraftLayout {
-  size_t x, y, q, k, v, o, h, part, att_o, att_ml, best, total;
+  size_t x, y, ss, rope, q, k, v, o, h, part, att_o, att_ml, best, total;
   AttnPlan ap;
   int parts;
   int groups;   // column groups of the LM-head argmax
+  bool fused;
 };
 
 DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages) {
@@ -81,6 +109,7 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
   const bool bf = m->bf16;
   const size_t M = (size_t)B * gamma;
   DraftLayout L{};
+  L.fused = use_fused(m, (int)M);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -89,43 +118,70 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
   };
   // Transient activations take 4 bytes per element: fp32, or two bf16 planes.
   L.x = take(M * d.D * 4);
-  L.y = take(M * d.D * 4);
+  if (!L.fused) L.y = take(M * d.D * 4);
+  L.ss = take(M * std::max(d.D / 64, 1) * 4);
+  if (L.fused) L.rope = take(M * d.dh * 4);   // (cos, sin) per row and dimension pair
   L.q = take(M * d.QD * 4);
   L.k = take(M * d.KVD * 4);
   L.v = take(M * d.KVD * 4);
   L.o = take(M * d.QD * 4);
   L.h = take(M * d.I * 4);
-  size_t pf = part_floats(bf, (int)M, d.QD + 2 * d.KVD, d.D);
-  pf = std::max(pf, part_floats(bf, (int)M, d.D, d.QD));
-  pf = std::max(pf, part_floats(bf, (int)M, 2 * d.I, d.D));
-  pf = std::max(pf, part_floats(bf, (int)M, d.D, d.I));
+  const int Mi = (int)M;
+  size_t pf;
+  if (L.fused) {
+    pf = skinny_part_floats(Mi, d.QD + 2 * d.KVD, d.D, SO_QKV, d.dh);
+    pf = std::max(pf, skinny_part_floats(Mi, d.D, d.QD, SO_RESID, d.dh));
+    pf = std::max(pf, skinny_part_floats(Mi, 2 * d.I, d.D, SO_SWIGLU, d.dh));
+    pf = std::max(pf, skinny_part_floats(Mi, d.D, d.I, SO_RESID, d.dh));
+  } else {
+    pf = part_floats(bf, Mi, d.QD + 2 * d.KVD, d.D);
+    pf = std::max(pf, part_floats(bf, Mi, d.D, d.QD));
+    pf = std::max(pf, part_floats(bf, Mi, 2 * d.I, d.D));
+    pf = std::max(pf, part_floats(bf, Mi, d.D, d.I));
+  }
   L.part = take(pf * 4);
   L.ap = plan_attention(B, d.Hkv, max_pages, m->cfg.page_size);
   L.parts = bf ? L.ap.n_ctx_splits + 1 : 1;
   L.att_o = take((size_t)L.parts * M * d.Hq * d.dh * 4);
   L.att_ml = take((size_t)L.parts * M * d.Hq * 2 * 4);
-  const GemmPlan lm = plan_gemm(bf, (int)M, d.V, d.D, true);
-  L.groups = gemm_argmax_groups(lm, d.V);
+  if (L.fused) {
+    L.groups = (d.V + 63) / 64;
+  } else {
+    const GemmPlan lm = plan_gemm(bf, Mi, d.V, d.D, true);
+    L.groups = gemm_argmax_groups(lm, d.V);
+  }
   L.best = take((size_t)L.groups * M * 8);
   L.total = off;
   return L;
 }
 
 struct InjectLayout {
-  size_t part, c, total;
+  size_t part, c, ss, rope, total;
+  bool fused;
 };
 
 InjectLayout inject_layout(const dflash_model* m, int n_tok) {
   const Dims d = dims_of(m->cfg);
   const bool bf = m->bf16;
   InjectLayout L{};
-  size_t pf = part_floats(bf, n_tok, d.D, d.F);
-  pf = std::max(pf, part_floats(bf, n_tok, 2 * d.NL * d.KVD, d.D));
+  L.fused = use_fused(m, n_tok);
+  size_t pf;
+  if (L.fused) {
+    pf = skinny_part_floats(n_tok, d.D, d.F, SO_STORE_SS, d.dh);
+    pf = std::max(pf, skinny_part_floats(n_tok, 2 * d.NL * d.KVD, d.D, SO_KV, d.dh));
+  } else {
+    pf = part_floats(bf, n_tok, d.D, d.F);
+    pf = std::max(pf, part_floats(bf, n_tok, 2 * d.NL * d.KVD, d.D));
+  }
   size_t off = 0;
   L.part = off;
   off = align256(pf * 4);
   L.c = off;
   off = align256(off + (size_t)n_tok * d.D * 4);
+  L.ss = off;
+  off = align256(off + (size_t)n_tok * std::max(d.D / 64, 1) * 4);
+  L.rope = off;
+  off = align256(off + (size_t)n_tok * d.dh * 4);
   L.total = off;
   return L;
 }
@@ -190,6 +246,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->cfg = *cfg;
   m->w = *w;
   m->err = (uint32_t*)state;
+  m->ctr = (unsigned long long*)((char*)state + kCtrOffset);
   m->device = dev;
   m->bf16 = cfg->dtype == DFLASH_BF16;
   m->prof_on = false;
@@ -255,11 +312,6 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   fc.ptr[0] = m->w.fc_w;
   fc.row_end[0] = d.D;
   fc.n = 1;
-  GemmPlan p = plan_gemm(bf, n_tok, d.D, d.F, false);
-  HIPCHK(launch_gemm(p, bf, hidden, nullptr, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
-  HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c,
-                            c_plane, st));
-
   WSeg kvw{};
   for (int l = 0; l < d.NL; ++l) {
     kvw.ptr[2 * l] = m->w.layer[l].wk;
@@ -269,6 +321,73 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   }
   kvw.n = 2 * d.NL;
   const int Nkv = 2 * d.NL * d.KVD;
+
+  if (L.fused) {
+    // c = W_c f (fp32, with per-tile row sums of squares), then the K/V
+    // product normalises c while staging it and writes the pages itself.
+    float* cx = (float*)c;
+    float* ss = (float*)(ws + L.ss);
+    SkinnyArgs a{};
+    a.A = hidden;
+    a.lda = d.F;
+    a.M = n_tok;
+    a.w = fc;
+    a.N = d.D;
+    a.K = d.F;
+    a.part = part;
+    a.ctr = m->ctr;
+    a.err = m->err;
+    a.dh = d.dh;
+    a.I = d.I;
+    a.x = cx;
+    a.ss_out = ss;
+    float* rope = (float*)(ws + L.rope);
+    a.rope_out = rope;
+    a.rope_rows = n_tok;
+    a.cu_new = cu_new;
+    a.batch = batch;
+    a.ctx_lens = kv->ctx_lens;
+    a.theta = m->cfg.rope_theta;
+    GemmPlan p = plan_skinny(n_tok, d.D, d.F, SO_STORE_SS, d.dh);
+    HIPCHK(launch_skinny(p, SA_BF16, SO_STORE_SS, a, st));
+
+    SkinnyArgs b{};
+    b.A = cx;
+    b.lda = d.D;
+    b.M = n_tok;
+    b.ss_in = ss;
+    b.ss_tiles = d.D / 64;
+    b.gain = m->w.fc_norm;
+    b.eps = m->cfg.rms_eps;
+    b.w = kvw;
+    b.N = Nkv;
+    b.K = d.D;
+    b.part = part;
+    b.ctr = m->ctr;
+    b.err = m->err;
+    b.Hkv = d.Hkv;
+    b.dh = d.dh;
+    b.I = d.I;
+    b.ctx_lens = kv->ctx_lens;
+    b.theta = m->cfg.rope_theta;
+    b.rope = rope;
+    b.pages = kv->pages;
+    b.cu_new = cu_new;
+    b.batch = batch;
+    b.page_table = kv->page_table;
+    b.max_pages = kv->max_pages_per_seq;
+    b.n_pages = kv->n_pages;
+    b.page_size = m->cfg.page_size;
+    p = plan_skinny(n_tok, Nkv, d.D, SO_KV, d.dh);
+    HIPCHK(launch_skinny(p, SA_NORM, SO_KV, b, st));
+    HIPCHK(launch_advance_ctx(kv->ctx_lens, cu_new, batch, st));
+    return DFLASH_OK;
+  }
+
+  GemmPlan p = plan_gemm(bf, n_tok, d.D, d.F, false);
+  HIPCHK(launch_gemm(p, bf, hidden, nullptr, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
+  HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c,
+                            c_plane, st));
   p = plan_gemm(bf, n_tok, Nkv, d.D, false);
   HIPCHK(launch_gemm(p, bf, c, c_lo, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
   HIPCHK(launch_inject_scatter(bf, part, p.splits, n_tok, cu_new, batch, kv->ctx_lens,
@@ -317,8 +436,173 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
   float* att_ml = (float*)(ws + L.att_ml);
   uint64_t* best = (uint64_t*)(ws + L.best);
 
+  float* ss = (float*)(ws + L.ss);
+
+  // LM-head timing events (dflash_profile_enable)
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  auto prof_begin = [&]() -> int {
+    if (!m->prof_on) return DFLASH_OK;
+    if (!m->pool.empty()) {
+      ev = m->pool.back();
+      m->pool.pop_back();
+    } else {
+      HIPCHK(hipEventCreate(&ev.first));
+      HIPCHK(hipEventCreate(&ev.second));
+    }
+    HIPCHK(hipEventRecord(ev.first, st));
+    return DFLASH_OK;
+  };
+  auto prof_end = [&]() -> int {
+    if (!m->prof_on) return DFLASH_OK;
+    HIPCHK(hipEventRecord(ev.second, st));
+    m->pending.push_back(ev);
+    return DFLASH_OK;
+  };
+
+  AttnArgs at{};
+  at.q = q;
+  at.q_plane = q_pl;
+  at.k = k;
+  at.v = v;
+  at.pages = kv->pages;
+  at.n_pages = kv->n_pages;
+  at.max_pages = kv->max_pages_per_seq;
+  at.page_size = m->cfg.page_size;
+  at.page_table = kv->page_table;
+  at.ctx_lens = kv->ctx_lens;
+  at.batch = batch;
+  at.gamma = gamma;
+  at.Hq = d.Hq;
+  at.Hkv = d.Hkv;
+  at.dh = d.dh;
+  at.part_o = att_o;
+  at.part_ml = att_ml;
+  at.err = m->err;
+
+  const int Nqkv = d.QD + 2 * d.KVD;
+  WSeg lm{};
+  lm.ptr[0] = m->w.lm_head;
+  lm.row_end[0] = d.V;
+  lm.n = 1;
+  int rc;
+
+  if (L.fused) {
+    // Every product normalises its input while staging it and finishes its
+    // own epilogue; the residual x carries per-tile row sums of squares ss.
+    float* rope = (float*)(ws + L.rope);
+    HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
+                        nullptr, eps, nullptr, 0, ss, rope, kv->ctx_lens, d.dh,
+                        m->cfg.rope_theta, m->err, st));
+    int ss_tiles = 1;
+    SkinnyArgs base{};
+    base.M = M;
+    base.eps = eps;
+    base.part = part;
+    base.ctr = m->ctr;
+    base.err = m->err;
+    base.gamma = gamma;
+    base.Hq = d.Hq;
+    base.Hkv = d.Hkv;
+    base.dh = d.dh;
+    base.ctx_lens = kv->ctx_lens;
+    base.theta = m->cfg.rope_theta;
+    base.rope = rope;
+    base.I = d.I;
+    for (int l = 0; l < d.NL; ++l) {
+      const dflash_layer_weights& W = m->w.layer[l];
+      SkinnyArgs a = base;
+      a.A = x;
+      a.lda = d.D;
+      a.ss_in = ss;
+      a.ss_tiles = ss_tiles;
+      a.gain = W.attn_norm;
+      a.w = WSeg{};
+      a.w.ptr[0] = W.wq;
+      a.w.ptr[1] = W.wk;
+      a.w.ptr[2] = W.wv;
+      a.w.row_end[0] = d.QD;
+      a.w.row_end[1] = d.QD + d.KVD;
+      a.w.row_end[2] = Nqkv;
+      a.w.n = 3;
+      a.N = Nqkv;
+      a.K = d.D;
+      a.q = q;
+      a.q_plane = q_pl;
+      a.kb = k;
+      a.vb = v;
+      HIPCHK(launch_skinny(plan_skinny(M, Nqkv, d.D, SO_QKV, d.dh), SA_NORM, SO_QKV, a, st));
+
+      at.layer = l;
+      HIPCHK(launch_attention(bf, at, L.ap, st));
+      HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, q_pl,
+                                 st));
+
+      a = base;
+      a.A = o;
+      a.a_plane = q_pl;
+      a.lda = d.QD;
+      a.w.ptr[0] = W.wo;
+      a.w.row_end[0] = d.D;
+      a.w.n = 1;
+      a.N = d.D;
+      a.K = d.QD;
+      a.x = x;
+      a.ss_out = ss;
+      HIPCHK(launch_skinny(plan_skinny(M, d.D, d.QD, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
+      ss_tiles = d.D / 64;
+
+      a = base;
+      a.A = x;
+      a.lda = d.D;
+      a.ss_in = ss;
+      a.ss_tiles = ss_tiles;
+      a.gain = W.mlp_norm;
+      a.w.ptr[0] = W.w_gate;
+      a.w.ptr[1] = W.w_up;
+      a.w.row_end[0] = d.I;
+      a.w.row_end[1] = 2 * d.I;
+      a.w.n = 2;
+      a.N = 2 * d.I;
+      a.K = d.D;
+      a.h = h;
+      a.h_plane = h_pl;
+      HIPCHK(launch_skinny(plan_skinny(M, 2 * d.I, d.D, SO_SWIGLU, d.dh), SA_NORM, SO_SWIGLU, a,
+                           st));
+
+      a = base;
+      a.A = h;
+      a.a_plane = h_pl;
+      a.lda = d.I;
+      a.w.ptr[0] = W.w_down;
+      a.w.row_end[0] = d.D;
+      a.w.n = 1;
+      a.N = d.D;
+      a.K = d.I;
+      a.x = x;
+      a.ss_out = ss;
+      HIPCHK(launch_skinny(plan_skinny(M, d.D, d.I, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
+    }
+    SkinnyArgs a = base;
+    a.A = x;
+    a.lda = d.D;
+    a.ss_in = ss;
+    a.ss_tiles = ss_tiles;
+    a.gain = m->w.final_norm;
+    a.w = lm;
+    a.N = d.V;
+    a.K = d.D;
+    a.keys = best;
+    a.logits = logits;
+    if ((rc = prof_begin()) != DFLASH_OK) return rc;
+    HIPCHK(launch_skinny(plan_skinny(M, d.V, d.D, SO_ARGMAX, d.dh), SA_NORM, SO_ARGMAX, a, st));
+    if ((rc = prof_end()) != DFLASH_OK) return rc;
+    HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
+    return DFLASH_OK;
+  }
+
   HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
-                      m->w.layer[0].attn_norm, eps, y, y_pl, m->err, st));
+                      m->w.layer[0].attn_norm, eps, y, y_pl, nullptr, nullptr, nullptr, d.dh,
+                      m->cfg.rope_theta, m->err, st));
   for (int l = 0; l < d.NL; ++l) {
     const dflash_layer_weights& W = m->w.layer[l];
     WSeg qkv{};
@@ -327,34 +611,14 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     qkv.ptr[2] = W.wv;
     qkv.row_end[0] = d.QD;
     qkv.row_end[1] = d.QD + d.KVD;
-    qkv.row_end[2] = d.QD + 2 * d.KVD;
+    qkv.row_end[2] = Nqkv;
     qkv.n = 3;
-    const int Nqkv = d.QD + 2 * d.KVD;
     GemmPlan p = plan_gemm(bf, M, Nqkv, d.D, false);
     HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, qkv, Nqkv, d.D, part, nullptr, nullptr, st));
     HIPCHK(launch_qkv_epilogue(bf, part, p.splits, M, gamma, d.Hq, d.Hkv, d.dh, kv->ctx_lens,
                                m->cfg.rope_theta, q, q_pl, k, v, st));
-    AttnArgs a{};
-    a.q = q;
-    a.q_plane = q_pl;
-    a.k = k;
-    a.v = v;
-    a.pages = kv->pages;
-    a.n_pages = kv->n_pages;
-    a.max_pages = kv->max_pages_per_seq;
-    a.page_size = m->cfg.page_size;
-    a.page_table = kv->page_table;
-    a.ctx_lens = kv->ctx_lens;
-    a.batch = batch;
-    a.gamma = gamma;
-    a.Hq = d.Hq;
-    a.Hkv = d.Hkv;
-    a.dh = d.dh;
-    a.layer = l;
-    a.part_o = att_o;
-    a.part_ml = att_ml;
-    a.err = m->err;
-    HIPCHK(launch_attention(bf, a, L.ap, st));
+    at.layer = l;
+    HIPCHK(launch_attention(bf, at, L.ap, st));
     HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, q_pl, st));
 
     WSeg wo{};
@@ -385,27 +649,10 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     HIPCHK(launch_residual_norm(bf, x, part, p.splits, M, d.D, g_next, eps, y, y_pl, st));
   }
 
-  WSeg lm{};
-  lm.ptr[0] = m->w.lm_head;
-  lm.row_end[0] = d.V;
-  lm.n = 1;
   const GemmPlan p = plan_gemm(bf, M, d.V, d.D, true);
-  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (m->prof_on) {
-    if (!m->pool.empty()) {
-      ev = m->pool.back();
-      m->pool.pop_back();
-    } else {
-      HIPCHK(hipEventCreate(&ev.first));
-      HIPCHK(hipEventCreate(&ev.second));
-    }
-    HIPCHK(hipEventRecord(ev.first, st));
-  }
+  if ((rc = prof_begin()) != DFLASH_OK) return rc;
   HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st));
-  if (m->prof_on) {
-    HIPCHK(hipEventRecord(ev.second, st));
-    m->pending.push_back(ev);
-  }
+  if ((rc = prof_end()) != DFLASH_OK) return rc;
   HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
   return DFLASH_OK;
 }

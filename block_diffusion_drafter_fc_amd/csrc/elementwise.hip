@@ -13,8 +13,10 @@ namespace {
 constexpr int kRowThreads = 256;
 
 // Row r = b*gamma + j of the block: token (j == 0 ? anchor[b] : mask), its
-// embedding into the fp32 residual x, and y = RMSNorm(x) * g (the first
-// layer's attention norm).  1024 threads, 4 columns per thread per pass.
+// embedding into the fp32 residual x, and either y = RMSNorm(x) * g (the
+// first layer's attention norm) or, when ss is given, only the row's sum of
+// squares ss[r] (the next product normalises while staging x).  1024
+// threads, 4 columns per thread per pass.
 template <bool BF16>
 __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anchor,
                                                 int gamma, int mask_id, int vocab,
@@ -22,9 +24,18 @@ __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anch
                                                 int D, float* __restrict__ x,
                                                 const typename Act<BF16>::T* __restrict__ g,
                                                 float eps, void* __restrict__ y,
-                                                size_t y_plane, uint32_t* err) {
+                                                size_t y_plane, float* __restrict__ ss_out,
+                                                float* __restrict__ rope,
+                                                const int32_t* __restrict__ ctx_lens, int dh,
+                                                float theta, uint32_t* err) {
   __shared__ float red[16];
   const int r = blockIdx.x, b = r / gamma, j = r % gamma;
+  if (rope != nullptr && (int)threadIdx.x < dh / 2) {
+    float cs, sn;
+    rope_cs(ctx_lens[b] + j, threadIdx.x, dh, (double)theta, &cs, &sn);
+    rope[((size_t)r * (dh / 2) + threadIdx.x) * 2] = cs;
+    rope[((size_t)r * (dh / 2) + threadIdx.x) * 2 + 1] = sn;
+  }
   int tok = j == 0 ? anchor[b] : mask_id;
   if (tok < 0 || tok >= vocab) {
     if (threadIdx.x == 0) set_dev_error(err, 4u);
@@ -43,6 +54,10 @@ __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anch
     if (d < D) *(f32x4*)&x[(size_t)r * D + d] = f32x4{v[p][0], v[p][1], v[p][2], v[p][3]};
   }
   ss = block_sum(ss, red);
+  if (ss_out != nullptr) {
+    if (threadIdx.x == 0) ss_out[r] = ss;
+    return;
+  }
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -375,16 +390,19 @@ __global__ void k_verify_finalize(const uint64_t* __restrict__ best,
 
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
                         int vocab, const void* embed, int D, float* x, const void* g, float eps,
-                        void* y, size_t y_plane, uint32_t* err, hipStream_t st) {
+                        void* y, size_t y_plane, float* ss, float* rope, const int32_t* ctx_lens,
+                        int dh, float theta, uint32_t* err, hipStream_t st) {
   dim3 grid(batch * gamma);
-  if (D % 4 != 0 || D > 8192) return hipErrorInvalidValue;
+  if (D % 4 != 0 || D > 8192 || dh > 2048) return hipErrorInvalidValue;
+  if (rope != nullptr && ctx_lens == nullptr) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(k_embed<true>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
                        vocab, (const uint16_t*)embed, D, x, (const uint16_t*)g, eps, y, y_plane,
-                       err);
+                       ss, rope, ctx_lens, dh, theta, err);
   else
     hipLaunchKernelGGL(k_embed<false>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
-                       vocab, (const float*)embed, D, x, (const float*)g, eps, y, y_plane, err);
+                       vocab, (const float*)embed, D, x, (const float*)g, eps, y, y_plane, ss,
+                       rope, ctx_lens, dh, theta, err);
   return hipGetLastError();
 }
 

@@ -42,6 +42,82 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
                        float* logits, hipStream_t stream);
 
+// ---- skinny product with fused epilogues (bf16 models, M <= 64) -----------
+// Activation source of the product.
+enum SkinnyA {
+  SA_SPLIT = 0,  // A: hi plane, A + a_plane: lo plane (transient fp32 activations)
+  SA_BF16 = 1,   // A: exact bf16 input (target hidden states)
+  SA_NORM = 2,   // A: fp32 rows x[M][lda]; the product uses RMSNorm(x) * gain,
+                 // with the row sums of squares taken from ss_in[ss_tiles][M]
+};
+// What happens to the product.  Except for SO_PART and SO_ARGMAX, the K
+// splits of one output tile run on one XCD and the last to finish reduces
+// the fp32 partials (in split order) and applies the epilogue.
+enum SkinnyOut {
+  SO_PART = 0,     // leave the partial slices part[S][M][N]
+  SO_ARGMAX = 1,   // row argmax keys per 64-column group (S == 1)
+  SO_QKV = 2,      // per head: RoPE on q and k; q -> split planes, k and v -> fp32
+  SO_SWIGLU = 3,   // columns [gate | up] -> h = silu(gate) * up, split planes
+  SO_RESID = 4,    // x += product; ss_out[tile][row] = sum over the tile of x^2
+  SO_STORE_SS = 5, // x = product;  ss_out[tile][row] as above
+  SO_KV = 6,       // per head of [K^0 | V^0 | K^1 | ...]: RoPE on K at the token's
+                   // position, store into the paged cache
+};
+
+struct SkinnyArgs {
+  // activations
+  const void* A;
+  size_t a_plane;          // SA_SPLIT: elements from the hi plane to the lo plane
+  int lda, M;
+  const float* ss_in;      // SA_NORM
+  int ss_tiles;
+  const void* gain;        // SA_NORM: [K] bf16
+  float eps;
+  // weights and shape
+  WSeg w;
+  int N, K;
+  // split-K bookkeeping
+  float* part;             // [S][M][N]
+  unsigned long long* ctr; // one arrival counter per output tile, zero between launches
+  uint32_t* err;
+  // SO_ARGMAX
+  uint64_t* keys;          // [ceil(N/64) groups][M]
+  float* logits;           // [M][N] or null
+  // SO_QKV
+  void* q;
+  size_t q_plane;
+  float* kb;
+  float* vb;
+  int gamma, Hq, Hkv, dh;
+  const int32_t* ctx_lens;
+  float theta;
+  const float* rope;       // SO_QKV / SO_KV: (cos, sin) [M][dh/2][2] at each row's position
+  // SO_STORE_SS side job (inject): rope_out[rope_rows][dh/2][2] at the
+  // positions of the new tokens (cu_new, ctx_lens before the advance)
+  float* rope_out;
+  int rope_rows;
+  // SO_SWIGLU (N == 2 I; weight rows [gate; up])
+  void* h;
+  size_t h_plane;
+  int I;
+  // SO_RESID / SO_STORE_SS
+  float* x;
+  float* ss_out;           // [N/64][M]
+  // SO_KV
+  void* pages;
+  const int32_t* cu_new;
+  int batch;
+  const int32_t* page_table;
+  int max_pages, n_pages, page_size;
+};
+// K split and tiling of a fused skinny product.
+GemmPlan plan_skinny(int M, int N, int K, int out, int dh);
+// Output tiles of a fused skinny product (the counters it uses), or -1 if
+// the shape does not fit the epilogue.
+int skinny_tiles(int out, int N, int dh, int I);
+hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs& a,
+                         hipStream_t stream);
+
 // ---- attention ------------------------------------------------------------
 struct AttnPlan {
   int chunk;          // context keys per workgroup (multiple of 32)
@@ -69,9 +145,13 @@ hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part
                                hipStream_t stream);
 
 // ---- element-wise and row kernels -----------------------------------------
+// ss non-null: write the row sums of squares ss[M] instead of y.
+// rope non-null: also write rope[M][dh/2][2] = (cos, sin) of the rotary
+// angles at the position ctx_lens[b] + j of row r = b*gamma + j.
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
                         int vocab, const void* embed, int D, float* x, const void* g, float eps,
-                        void* y, size_t y_plane, uint32_t* err, hipStream_t stream);
+                        void* y, size_t y_plane, float* ss, float* rope, const int32_t* ctx_lens,
+                        int dh, float theta, uint32_t* err, hipStream_t stream);
 // Outputs named y, q, h, c are transient activations: fp32 for fp32 models,
 // split hi/lo bf16 planes for bf16 models (the lo plane starts *_plane
 // elements after the hi plane).

@@ -1,0 +1,588 @@
+// skinny.hip -- bf16 weight-streaming product for M <= 64 rows (the block rows
+// of up to 4 sequences, or up to 64 new context tokens) with the epilogue of
+// the surrounding step fused in.
+//
+// Work split.  Output columns come in groups of 64; a workgroup of 4 waves
+// owns one group and one K slice.  The activations of the slice are staged
+// in LDS in sub-chunks of KC columns (double-buffered) as hi/lo bf16 planes
+// and shared by the 4 waves; each wave streams its own 16 weight rows from
+// HBM straight into 16x16x32 MFMA B operands (16 contiguous bytes per lane).
+// Activation loads are issued before the weight batch (loads retire in
+// order, so the LDS store never waits for weights) and two weight batches
+// per wave are in flight.
+//
+// Activation sources (SkinnyA): split fp32 planes, exact bf16 inputs, or the
+// fp32 residual x normalised on the fly (RMSNorm with the row sums of squares
+// left by the producer of x, times the gain) -- so no separate norm kernel.
+//
+// Fused epilogues (SkinnyOut).  K is split over S workgroups; the groups of
+// one output tile (one head, one [gate|up] pair, or one 64-column group) and
+// all their K splits get workgroup ids congruent mod 8.  The dispatcher
+// places workgroup i on XCD i mod 8, so they meet in that XCD's L2: each
+// finished workgroup waits for its partial stores, adds its arrival to the
+// tile's counter, and the last to arrive drops its L1, sums the partials in
+// split order and applies the epilogue (RoPE, SwiGLU, residual + row sums of
+// squares, K/V page store).  The counter also counts arrivals per XCD (read
+// from the XCC_ID register).  A workgroup away from the tile's home XCD
+// writes its partials back with a device-scope fence; a reducer that saw
+// arrivals from another XCD acquires at device scope; a reducer away from
+// home while home workgroups also wrote (their partials then sit in another
+// L2) raises an error bit.  No workgroup ever waits on another.
+#include "common.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace {
+
+constexpr int kXcds = 8;
+// Workgroups a split-K launch aims for: every fused launch pays a per-
+// workgroup start and publish latency, so about two workgroups per CU with
+// longer K slices beat many short ones (measured on the Qwen3-8B-shaped
+// draft: each product lands within ~0.6 us of its best split).
+constexpr int kWgTarget = 512;
+constexpr int kMaxSplits = 16;
+constexpr int kMaxPer = 63;       // arrivals per tile (6-bit per-XCD fields)
+constexpr int kMaxSsTiles = 128;  // row sum-of-squares pieces (hidden <= 8192)
+constexpr uint32_t kErrXcd = 8u;
+
+DF_DEV unsigned xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu; }
+
+__host__ __device__ inline int tile_groups(int out, int dh) {
+  if (out == SO_QKV || out == SO_KV) return dh / 64;
+  if (out == SO_SWIGLU) return 2;
+  return 1;
+}
+
+DF_DEV uint64_t max16(uint64_t k) {
+  for (int m = 1; m < 16; m <<= 1) {
+    const uint64_t o = shfl_xor_u64(k, m);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+// Weight row of the first column of 64-column group g.  SwiGLU interleaves
+// gate and up groups so that one tile holds both halves of 64 outputs.
+template <int OUT>
+DF_DEV int group_row0(int g, int I) {
+  if (OUT == SO_SWIGLU) return (g & 1) ? I + 64 * (g >> 1) : 64 * (g >> 1);
+  return 64 * g;
+}
+
+// Sums over the S partial slices part[s][M][N] of two 4-column pieces at
+// element offsets o1 and o2 of a slice, in split order.  Loads go out in
+// batches of 8 per piece, so up to 16 are in flight at once.
+DF_DEV void sum_parts2(const float* part, int S, size_t slice, size_t o1, size_t o2, f32x4& s1,
+                       f32x4& s2) {
+  s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s2 = s1;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4 a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        a[j] = *(const f32x4*)&part[(size_t)(s0 + j) * slice + o1];
+        b[j] = *(const f32x4*)&part[(size_t)(s0 + j) * slice + o2];
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        s1 += a[j];
+        s2 += b[j];
+      }
+  }
+}
+
+// Same for one piece.
+DF_DEV f32x4 sum_parts1(const float* part, int S, size_t slice, size_t o) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) a[j] = *(const f32x4*)&part[(size_t)(s0 + j) * slice + o];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) v += a[j];
+  }
+  return v;
+}
+
+// sequence of token t of an inject batch: cu_new[b] <= t < cu_new[b+1]
+DF_DEV int seq_of(const int32_t* cu_new, int batch, int t) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_new[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rotate the pairs (x1[e], x2[e]) = dims (i + e, i + e + dh/2) with the
+// (cos, sin) values cs[2e], cs[2e+1] of one table row.
+DF_DEV void rope4(const float* cs, f32x4& x1, f32x4& x2) {
+  const f32x4 c01 = *(const f32x4*)cs, c23 = *(const f32x4*)(cs + 4);
+  const float c[4] = {c01[0], c01[2], c23[0], c23[2]};
+  const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = x1[e] * c[e] - x2[e] * sn[e], b = x2[e] * c[e] + x1[e] * sn[e];
+    x1[e] = a;
+    x2[e] = b;
+  }
+}
+
+// ------------------------------------------------------------ tile epilogues
+// All run on the 256 threads of the tile's last workgroup.
+
+// x (+)= product over the 64 columns of `tile`; ss_out[tile][row] = sum x^2.
+template <bool ADD>
+DF_DEV void epi_resid(const SkinnyArgs& a, int S, int tile) {
+  const int t = threadIdx.x, r16 = t >> 4, c = (t & 15) * 4;
+  const int col = tile * 64 + c;
+  for (int r0 = 0; r0 < a.M; r0 += 16) {
+    const int row = r0 + r16;
+    float ssq = 0.f;
+    if (row < a.M) {
+      f32x4 v = sum_parts1(a.part, S, (size_t)a.M * a.N, (size_t)row * a.N + col);
+      float* xp = a.x + (size_t)row * a.N + col;
+      if (ADD) v += *(const f32x4*)xp;
+      *(f32x4*)xp = v;
+      ssq = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    for (int m = 1; m < 16; m <<= 1) ssq += __shfl_xor(ssq, m, 64);
+    if ((t & 15) == 0 && row < a.M) a.ss_out[(size_t)tile * a.M + row] = ssq;
+  }
+}
+
+// Head hh of [Q heads | K heads | V heads]: RoPE on q and k at the row's
+// position, q to split planes, k and v to fp32.
+DF_DEV void epi_qkv(const SkinnyArgs& a, int S, int hh) {
+  const int half = a.dh / 2, quads = half / 4;
+  const int c0 = hh * a.dh;
+  for (int task = threadIdx.x; task < a.M * quads; task += blockDim.x) {
+    const int row = task / quads, i = (task % quads) * 4;
+    f32x4 x1, x2;
+    const size_t o = (size_t)row * a.N + c0 + i;
+    sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + half, x1, x2);
+    if (hh < a.Hq + a.Hkv) rope4(a.rope + ((size_t)row * half + i) * 2, x1, x2);
+    if (hh < a.Hq) {
+      const size_t base = ((size_t)row * a.Hq + hh) * a.dh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Split<true>::store(a.q, a.q_plane, base + i + e, x1[e]);
+        Split<true>::store(a.q, a.q_plane, base + i + e + half, x2[e]);
+      }
+    } else {
+      const bool isk = hh < a.Hq + a.Hkv;
+      float* dst = isk ? a.kb : a.vb;
+      const size_t base = ((size_t)row * a.Hkv + (isk ? hh - a.Hq : hh - a.Hq - a.Hkv)) * a.dh;
+      *(f32x4*)&dst[base + i] = x1;
+      *(f32x4*)&dst[base + i + half] = x2;
+    }
+  }
+}
+
+// Tile t: gate columns [64t, 64t+64) (group 2t) and up (group 2t+1).
+DF_DEV void epi_swiglu(const SkinnyArgs& a, int S, int tile) {
+  const int t = threadIdx.x, r16 = t >> 4, c = (t & 15) * 4;
+  for (int r0 = 0; r0 < a.M; r0 += 16) {
+    const int row = r0 + r16;
+    if (row >= a.M) continue;
+    f32x4 g, u;
+    const size_t o = (size_t)row * a.N + (2 * tile) * 64 + c;
+    sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + 64, g, u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = g[e] / (1.0f + expf(-g[e]));
+      Split<true>::store(a.h, a.h_plane, (size_t)row * a.I + tile * 64 + c + e, sg * u[e]);
+    }
+  }
+}
+
+// Head y of [K^0 | V^0 | K^1 | V^1 | ...] for the inject tokens: RoPE on K at
+// the token's position, store bf16 into its page.
+DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
+  const int half = a.dh / 2, quads = half / 4;
+  const int kvh = y % a.Hkv, kv = (y / a.Hkv) % 2, layer = y / (2 * a.Hkv);
+  const int c0 = y * a.dh;
+  for (int task = threadIdx.x; task < a.M * quads; task += blockDim.x) {
+    const int t = task / quads, i = (task % quads) * 4;
+    const int b = seq_of(a.cu_new, a.batch, t);
+    const int pos = a.ctx_lens[b] + (t - a.cu_new[b]);
+    const int pi = pos / a.page_size;
+    if (pos < 0 || pi >= a.max_pages) {
+      if (i == 0) set_dev_error(a.err, 2u);
+      continue;
+    }
+    const int pg = a.page_table[(size_t)b * a.max_pages + pi];
+    if (pg < 0 || pg >= a.n_pages) {
+      if (i == 0) set_dev_error(a.err, 1u);
+      continue;
+    }
+    f32x4 x1, x2;
+    const size_t o = (size_t)t * a.N + c0 + i;
+    sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + half, x1, x2);
+    if (kv == 0) rope4(a.rope + ((size_t)t * half + i) * 2, x1, x2);
+    uint16_t* dst = (uint16_t*)a.pages +
+                    ((((size_t)layer * a.n_pages + pg) * 2 + kv) * a.Hkv + kvh) * a.page_size * a.dh +
+                    (size_t)(pos % a.page_size) * a.dh;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[i + e] = f2bf(x1[e]);
+      dst[i + e + half] = f2bf(x2[e]);
+    }
+  }
+}
+
+// --------------------------------------------------------------- the kernel
+// grid: (n_tiles rounded up to a multiple of 8) * per workgroups of 256
+// threads, per = tile_groups * S.
+template <int MT, int ASRC, int OUT>
+__global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles) {
+  constexpr int U = 8 / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
+  constexpr int NCH = ROWS * CPR / 256;
+  constexpr bool TWO = ASRC != SA_BF16;   // two planes in LDS
+  constexpr int NP = TWO ? 2 : 1;
+  constexpr int LPR = 256 / ROWS;         // threads per row in the norm prologue
+  static_assert(ROWS * CPR % 256 == 0 && 256 % CPR == 0,
+                "sub-chunk must split evenly over 256 threads, same columns per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][ROWS][KC + 8];
+  __shared__ float inv_s[ROWS];
+  __shared__ unsigned long long sh_old;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tg = tile_groups(OUT, a.dh);
+  const int per = tg * S;
+  const int id = blockIdx.x, xcd = id % kXcds, local = id / kXcds;
+  const int tile = (local / per) * kXcds + xcd, member = local % per;
+  if (tile >= n_tiles) return;
+  const int grp = tile * tg + member / S, split = member % S;
+  const int kbeg = split * kps;
+  const int M = a.M, N = a.N, K = a.K;
+  const int vcol0 = grp * 64 + wave * 16;                  // virtual column of the wave
+  const bool active = vcol0 < N;
+  // Weight rows of this wave: base .. base + 15, inside one segment (inner
+  // boundaries are multiples of 16).  The segment lookup is wave-uniform;
+  // rows past the end (a partial last group, or a wave past N) re-read the
+  // last row and their products are discarded.
+  const int nrows = a.w.row_end[a.w.n - 1];
+  const int base = __builtin_amdgcn_readfirstlane(group_row0<OUT>(grp, a.I) + wave * 16);
+  const int rfirst = base < nrows ? base : nrows - 1;
+  int sgi = 0;
+  while (sgi < a.w.n - 1 && rfirst >= a.w.row_end[sgi]) ++sgi;
+  const int st = sgi ? a.w.row_end[sgi - 1] : 0, en = a.w.row_end[sgi];
+  const int wrow = base + lr < en ? base + lr : en - 1;
+  const uint16_t* bp = (const uint16_t*)a.w.ptr[sgi] + (size_t)(wrow - st) * K + kbeg + lg * 8;
+
+  // activation chunks this thread stages per sub-chunk: row srow, column scol
+  int srow[NCH], scol[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * 256;
+    srow[i] = c / CPR;
+    scol[i] = (c % CPR) * 8;
+  }
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 bc[U], bn[U];
+
+  // Raw activation data of one sub-chunk: two 16-byte pieces per chunk (the
+  // hi and lo planes, or 8 fp32 values of x) plus, for SA_NORM, the 8 gains
+  // of the thread's columns (the same for all its chunks).
+  u32x4 r0[NCH], r1[NCH], rg;
+  auto fetch = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int row = srow[i] < M ? srow[i] : M - 1;
+      const int col = kbeg + k + scol[i];
+      if (ASRC == SA_NORM) {
+        const float* xp = (const float*)a.A + (size_t)row * a.lda + col;
+        r0[i] = ld16(xp);
+        r1[i] = ld16(xp + 4);
+        if (i == 0) rg = ld16((const uint16_t*)a.gain + col);
+      } else {
+        const uint16_t* ap = (const uint16_t*)a.A + (size_t)row * a.lda + col;
+        r0[i] = ld16(ap);
+        if (TWO) r1[i] = ld16(ap + a.a_plane);
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (ASRC == SA_NORM) {
+        // y = x * inv * g, split into hi = bf16(y) and lo = bf16(y - hi)
+        const float inv = inv_s[srow[i]];
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xa = __uint_as_float(e < 2 ? r0[i][2 * e] : r1[i][2 * e - 4]);
+          const float xb = __uint_as_float(e < 2 ? r0[i][2 * e + 1] : r1[i][2 * e - 3]);
+          const uint32_t gw = rg[e];
+          const float ya = xa * inv * __uint_as_float(gw << 16);
+          const float yb = xb * inv * __uint_as_float(gw & 0xFFFF0000u);
+          hw[e] = pack_bf2(ya, yb);
+          lw[e] = pack_bf2(ya - __uint_as_float(hw[e] << 16), yb - __uint_as_float(hw[e] & 0xFFFF0000u));
+        }
+        st16(&As[buf][0][srow[i]][scol[i]], u32x4{hw[0], hw[1], hw[2], hw[3]});
+        st16(&As[buf][1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
+      } else {
+        st16(&As[buf][0][srow[i]][scol[i]], r0[i]);
+        if (TWO) st16(&As[buf][NP - 1][srow[i]][scol[i]], r1[i]);
+      }
+    }
+  };
+
+  // Prologue.  Loads retire in order, so they are issued oldest-needed
+  // first: the row sums of squares (SA_NORM), the activations of sub-chunk
+  // 0, then its weights, which stay in flight while the rest is staged.
+  constexpr int Q = kMaxSsTiles / LPR;
+  const int nrm_row = tid / LPR, nrm_j = tid % LPR;
+  float ssv[ASRC == SA_NORM ? Q : 1];
+  if (ASRC == SA_NORM) {
+    // fully unrolled, unpredicated loads (clamped index, masked use): a loop
+    // or a branch here would make the compiler drain the loads in flight
+    const int rr = nrm_row < M ? nrm_row : M - 1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = q * LPR + nrm_j;
+      ssv[q] = a.ss_in[(size_t)(i < a.ss_tiles ? i : a.ss_tiles - 1) * M + rr];
+    }
+  }
+  fetch(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) bc[u] = ld16(bp + u * 32);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ASRC == SA_NORM) {
+    // 1 / rms of each row from the producer's per-tile sums of squares
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) s += ssv[q] * (q * LPR + nrm_j < a.ss_tiles ? 1.f : 0.f);
+    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
+    if (nrm_j == 0) inv_s[nrm_row] = nrm_row < M ? 1.0f / sqrtf(s / (float)K + a.eps) : 0.f;
+    __syncthreads();
+  }
+  stage(0);
+  __syncthreads();
+
+  // One sub-chunk k: if LOAD, issue the next sub-chunk's activation and
+  // weight loads, then run the MFMAs on LDS buffer `buf` with the weights in
+  // `bw` and stage the next activations.  Two weight register sets
+  // alternate, so the batch loading for the next sub-chunk stays in flight
+  // across the barrier, and the MFMAs wait only for their own batch (loads
+  // retire in order).  The loads are not predicated (waves past N read a
+  // clamped row), so the wait counts stay exact.
+  auto step = [&](auto load_tag, int k, int buf, const u32x4* bw, u32x4* bnext) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    if (LOAD) {
+      fetch(k + KC);
+#pragma unroll
+      for (int u = 0; u < U; ++u) bnext[u] = ld16(bp + k + KC + u * 32);
+      __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 av = ld16(&As[buf][0][m * 16 + lr][u * 32 + lg * 8]);
+        acc[m] = mfma_16x16x32(av, bw[u], acc[m]);
+        if (TWO) {
+          const u32x4 al = ld16(&As[buf][NP - 1][m * 16 + lr][u * 32 + lg * 8]);
+          acc[m] = mfma_16x16x32(al, bw[u], acc[m]);
+        }
+      }
+    if (LOAD) {
+      __builtin_amdgcn_sched_barrier(0);   // staging (waits for the activations) after the MFMAs
+      stage(buf ^ 1);
+    }
+    __syncthreads();
+  };
+  using Load = std::integral_constant<bool, true>;
+  using Last = std::integral_constant<bool, false>;
+  const int nsub = kps / KC;   // >= 1
+  int j = 0;
+  for (; j + 2 < nsub; j += 2) {
+    step(Load{}, j * KC, 0, bc, bn);
+    step(Load{}, (j + 1) * KC, 1, bn, bc);
+  }
+  if (nsub - j == 2) {
+    step(Load{}, j * KC, 0, bc, bn);
+    step(Last{}, (j + 1) * KC, 1, bn, bc);
+  } else {
+    step(Last{}, j * KC, 0, bc, bn);
+  }
+
+  if (OUT == SO_ARGMAX) {
+    // per wave over its 16 columns, then over the 4 waves; keys[grp][row]
+    __shared__ uint64_t wkeys[4][ROWS];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+        const int col = vcol0 + lr;
+        uint64_t key = 0;
+        if (active && col < N) {
+          const float v = acc[m][i];
+          key = argmax_key(v, (uint32_t)col);
+          if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
+        }
+        key = max16(key);
+        if (lr == 0) wkeys[wave][row] = key;
+      }
+    __syncthreads();
+    if (tid < ROWS && tid < M) {
+      uint64_t key = wkeys[0][tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) key = wkeys[w][tid] > key ? wkeys[w][tid] : key;
+      a.keys[(size_t)grp * M + tid] = key;
+    }
+    return;
+  }
+
+  if (OUT == SO_STORE_SS && a.rope_out != nullptr) {
+    // Side job for the K/V product that follows: the rotary (cos, sin)
+    // table of the new tokens, entry e = t * dh/2 + i, spread over the
+    // workgroups (numbered densely by tile and member).
+    const int half = a.dh / 2, e = (tile * per + member) * 256 + tid;
+    if (e < a.rope_rows * half) {
+      const int t = e / half, i = e % half;
+      const int b = seq_of(a.cu_new, a.batch, t);
+      float cs, sn;
+      rope_cs(a.ctx_lens[b] + (t - a.cu_new[b]), i, a.dh, (double)a.theta, &cs, &sn);
+      a.rope_out[2 * (size_t)e] = cs;
+      a.rope_out[2 * (size_t)e + 1] = sn;
+    }
+  }
+
+  // partial slice of this group
+  if (active) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+        const int col = vcol0 + lr;
+        if (row < M && col < N) a.part[((size_t)split * M + row) * N + col] = acc[m][i];
+      }
+  }
+  if (OUT == SO_PART) return;
+
+  // Publish the slice and count the arrival: bits 0..15 count all arrivals,
+  // the 6-bit field at 16 + 6x counts those from XCD x.
+  const unsigned xcc = xcc_id();
+  const bool home = xcc == (unsigned)xcd;
+  if (home) __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are in the XCD's L2
+  else __threadfence();                       // write back for readers on other XCDs
+  __syncthreads();
+  const unsigned long long mine = 1ull + (1ull << (16 + 6 * (xcc & 7u)));
+  if (tid == 0) sh_old = atomicAdd(&a.ctr[tile], mine);
+  __syncthreads();
+  const unsigned long long tot = sh_old + mine;
+  if ((int)(tot & 0xFFFFu) != per) return;
+
+  bool foreign = false;   // partials written on another XCD
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x)
+    if ((unsigned)x != (xcc & 7u) && ((tot >> (16 + 6 * x)) & 63u) != 0) foreign = true;
+  if (foreign) {
+    __threadfence();
+    if (!home && ((tot >> (16 + 6 * xcd)) & 63u) != 0 && tid == 0) set_dev_error(a.err, kErrXcd);
+  } else {
+    asm volatile("buffer_inv sc0" ::: "memory");   // drop this CU's L1 copies
+  }
+  if (tid == 0) atomicExch(&a.ctr[tile], 0ull);
+
+  if (OUT == SO_RESID) epi_resid<true>(a, S, tile);
+  if (OUT == SO_STORE_SS) epi_resid<false>(a, S, tile);
+  if (OUT == SO_QKV) epi_qkv(a, S, tile);
+  if (OUT == SO_SWIGLU) epi_swiglu(a, S, tile);
+  if (OUT == SO_KV) epi_kv(a, S, tile);
+}
+
+template <int MT, int ASRC, int OUT>
+hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
+  const int per = tile_groups(OUT, a.dh) * p.splits;
+  const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT>), dim3(padded * per), dim3(256), 0, st, a, p.splits,
+                     p.kpw, n_tiles);
+  return hipGetLastError();
+}
+
+template <int ASRC, int OUT>
+hipError_t run_mt(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
+  if (p.mt == 1) return run<1, ASRC, OUT>(p, a, n_tiles, st);
+  if (p.mt == 2) return run<2, ASRC, OUT>(p, a, n_tiles, st);
+  if (p.mt == 4) return run<4, ASRC, OUT>(p, a, n_tiles, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+GemmPlan plan_skinny(int M, int N, int K, int out, int dh) {
+  GemmPlan p{};
+  p.kind = GEMM_SKINNY;
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.nt = 1;
+  p.unroll = 8 / p.mt;
+  p.waves = 4;
+  const int kc = 32 * p.unroll, nk = K / kc;
+  const int groups = (N + 63) / 64, tg = tile_groups(out, dh);
+  int S = 1;
+  if (out != SO_ARGMAX) {
+    for (int s = 1; s <= nk; ++s) {
+      if (nk % s) continue;
+      if (s > kMaxSplits || tg * s > kMaxPer) break;
+      S = s;
+      if (groups * s >= kWgTarget) break;
+    }
+  }
+  p.splits = S;
+  p.kpw = K / S;
+  return p;
+}
+
+int skinny_tiles(int out, int N, int dh, int I) {
+  if (out == SO_QKV || out == SO_KV) return (dh % 64 || N % dh) ? -1 : N / dh;
+  if (out == SO_SWIGLU) return (N != 2 * I || I % 64) ? -1 : I / 64;
+  if (out == SO_RESID || out == SO_STORE_SS) return N % 64 ? -1 : N / 64;
+  return (N + 63) / 64;
+}
+
+hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs& a,
+                         hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.M > 64 || p.kind != GEMM_SKINNY || p.splits < 1 || p.kpw * p.splits != a.K ||
+      p.kpw % (32 * p.unroll) != 0 || p.unroll * p.mt != 8)
+    return hipErrorInvalidValue;
+  if ((p.mt == 1 && a.M > 16) || (p.mt == 2 && a.M > 32)) return hipErrorInvalidValue;
+  const int n_tiles = skinny_tiles(out, a.N, a.dh, a.I);
+  if (n_tiles < 0) return hipErrorInvalidValue;
+  if (out == SO_ARGMAX && p.splits != 1) return hipErrorInvalidValue;
+  if (tile_groups(out, a.dh) * p.splits > kMaxPer) return hipErrorInvalidValue;
+  if (asrc == SA_NORM && (a.ss_in == nullptr || a.ss_tiles < 1 || a.ss_tiles > kMaxSsTiles ||
+                          a.gain == nullptr))
+    return hipErrorInvalidValue;
+  if ((out == SO_QKV || out == SO_KV) && a.rope == nullptr) return hipErrorInvalidValue;
+  if (out == SO_STORE_SS && a.rope_out != nullptr) {
+    const long long wgs = (long long)n_tiles * tile_groups(out, a.dh) * p.splits;
+    if (a.cu_new == nullptr || a.ctx_lens == nullptr || a.dh % 2 ||
+        (long long)a.rope_rows * (a.dh / 2) > wgs * 256)
+      return hipErrorInvalidValue;
+  }
+#define DF_RUN(A_, O_) \
+  if (asrc == A_ && out == O_) return run_mt<A_, O_>(p, a, n_tiles, st)
+  DF_RUN(SA_NORM, SO_QKV);
+  DF_RUN(SA_SPLIT, SO_RESID);
+  DF_RUN(SA_NORM, SO_SWIGLU);
+  DF_RUN(SA_NORM, SO_ARGMAX);
+  DF_RUN(SA_BF16, SO_STORE_SS);
+  DF_RUN(SA_NORM, SO_KV);
+#undef DF_RUN
+  return hipErrorInvalidValue;
+}

@@ -57,16 +57,21 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_PAGE 1u     /* page-table entry outside [0, n_pages) */
 #define DFLASH_DEVERR_POS 2u      /* position beyond max_pages_per_seq*page_size */
 #define DFLASH_DEVERR_TOKEN 4u    /* anchor token outside [0, vocab) (row uses token 0) */
+#define DFLASH_DEVERR_XCD 8u      /* a split-K reduction ran on a chiplet that could not see
+                                     all partial sums (workgroups were not placed round-robin
+                                     over the 8 XCDs); the call's results are unreliable */
 
 #define DFLASH_MAX_LAYERS 16
 #define DFLASH_MAX_BLOCK 16
-#define DFLASH_STATE_BYTES 256
+#define DFLASH_STATE_BYTES 16384
 
 /* Drafter dimensions.  Constraints checked at model creation:
- *   hidden % 32 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
- *   n_q_heads / n_kv_heads <= 8, intermediate % 32 == 0, n_target_feats >= 1,
- *   1 <= max_block <= DFLASH_MAX_BLOCK, page_size == 16,
- *   0 <= mask_token_id < vocab, n_layers <= DFLASH_MAX_LAYERS. */
+ *   hidden % 4 == 0 and hidden <= 8192, head_dim in {64, 128},
+ *   n_q_heads % n_kv_heads == 0, n_q_heads / n_kv_heads <= 8,
+ *   n_target_feats >= 1, 1 <= max_block <= DFLASH_MAX_BLOCK, page_size == 16,
+ *   0 <= mask_token_id < vocab, n_layers <= DFLASH_MAX_LAYERS;
+ *   bf16 models also need hidden, intermediate and n_q_heads * head_dim to
+ *   be multiples of 256. */
 typedef struct {
   int32_t hidden;          /* D */
   int32_t n_layers;        /* draft layers (5 for the Qwen3-8B-shaped drafter) */
@@ -133,8 +138,11 @@ typedef struct dflash_model dflash_model;   /* opaque host handle */
 /* Create a model handle.  cfg and w are [host] structs; the weight pointers
  * are device pointers the caller keeps alive for the handle's lifetime.
  * state: device buffer of DFLASH_STATE_BYTES bytes owned by the caller (it
- * holds the sticky device error word); it is cleared here (synchronously).
- * The handle binds to the device current at creation. */
+ * holds the sticky device error word and the arrival counters of the split-K
+ * reductions, which every call leaves at zero); it is cleared here
+ * (synchronously).  The handle binds to the device current at creation.
+ * Calls that share a handle must be ordered (one stream, or streams joined
+ * by events): concurrent calls on one handle race on its counters. */
 int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void* state,
                         dflash_model** out /* [host] */);
 void dflash_model_destroy(dflash_model* model);
