@@ -16,6 +16,16 @@ oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload qwen3-8b-bs1|qwen3-8b-bs32|qwen3-8b-long|wide-8layer|tiny-fp32]
+
+HBM traffic of the LM-head kernel (the "traffic" field) comes from rocprofv3
+counter runs summarised into profiles/lm_head_traffic_<workload>.json:
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D3 -o c -- python3 bench.py --copy-calibration
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d D4 -o c -- python3 bench.py --copy-calibration
+  python3 bench.py --counter-summary D1 D2 D3 D4
+The copy of known size calibrates each counter (bytes per counted KiB); the
+record carries a hash of the kernel sources and is ignored once they change.
 """
 from __future__ import annotations
 
@@ -33,6 +43,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/s & draft tokens/s (block 16, Qwen3-8B-shaped, bs 1/32); %HBM peak"
+LM_KERNEL = {"bf16-skinny": "k_skinny<1, 2, 1>"}   # LM head at M <= 16 rows: norm-staged, argmax
+COPY_BYTES = 1 << 30                               # calibration copy size
+KERNEL_SOURCES = ("block_diffusion_drafter_fc_amd/csrc/skinny.hip",
+                  "block_diffusion_drafter_fc_amd/csrc/common.h",
+                  "block_diffusion_drafter_fc_amd/csrc/kernels.h")
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
@@ -267,6 +282,98 @@ def cpu_baseline(s, w_host, budget_s=15.0):
                       f"sequence with a {L}-token synthetic context, {dt:.1f} s"}
 
 
+# ------------------------------------------------------------ HBM counters
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"lm_head_traffic_{workload}.json")
+
+
+def copy_calibration(reps: int = 5):
+    """A plain device-to-device copy of COPY_BYTES, reps times (calibrates
+    the HBM byte counters: the copy reads and writes exactly COPY_BYTES)."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no counter_collection.csv under {d}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                key = (fn, r["Dispatch_Id"])
+                e = per.setdefault(key, {"name": r["Kernel_Name"], "value": 0.0})
+                e["value"] += float(r["Counter_Value"])
+    return list(per.values())
+
+
+def counter_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the LM-head kernel,
+    scaled by what the same counters read for the calibration copy."""
+    kname = LM_KERNEL["bf16-skinny"]
+
+    def mean_for(rows, pred):
+        v = [r["value"] for r in rows if pred(r)]
+        if not v:
+            sys.exit("no matching dispatches in the counter files")
+        return float(np.mean(v)), len(v)
+
+    def copy_kib(d):
+        # the calibration copies: the largest dispatches of a copy kernel
+        rows = [r for r in _counter_rows(d) if "copy" in r["name"].lower()]
+        if not rows:
+            sys.exit(f"no copy dispatches in {d}")
+        top = max(r["value"] for r in rows)
+        return mean_for(rows, lambda r: r["value"] >= 0.5 * top)[0]
+
+    f_kib, nf = mean_for(_counter_rows(fetch_dir), lambda r: kname in r["name"])
+    w_kib, nw = mean_for(_counter_rows(write_dir), lambda r: kname in r["name"])
+    cf_kib, cw_kib = copy_kib(cfetch_dir), copy_kib(cwrite_dir)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    rec = {"workload": workload, "kernel": kname, "source_sha256_16": kernel_source_hash(),
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "dispatches": [nf, nw],
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "traffic_bytes_per_launch": int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale))}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
+def recorded_traffic(workload: str):
+    """Counter-derived HBM bytes per LM-head launch, if recorded for the
+    current kernel sources; else None."""
+    try:
+        with open(traffic_path(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,7 +382,17 @@ def main():
     ap.add_argument("--workload", default="qwen3-8b-bs1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the counter-calibration copy")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="summarise rocprofv3 --pmc output directories into profiles/")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the DFlash hot path here is built for and timed on a "
               f"single MI355X (sequences shard across GPUs with no exchange); --gpus {args.gpus} "
@@ -333,11 +450,11 @@ def main():
                        "tflops": round(flops / (res["draft_only_ms"] * 1e-3) / 1e12, 2)},
         "replay_accept_match": res["replay_ok"],
         "prefill": {"tokens": res["prefill_tokens"], "s": round(res["prefill_s"], 4)},
-        "roofline": {"kernel": "LM head + fused argmax (k_gemm_skinny, argmax epilogue)",
+        "roofline": {"kernel": "LM head: final RMSNorm staged + bf16 MFMA + argmax (k_skinny)",
                      "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_ms": round(lm_avg_ms, 5), "launches": res["lm_count"],
-                     "bytes_per_launch": lm_bytes, "traffic": None},
+                     "bytes_per_launch": lm_bytes, "traffic": recorded_traffic(s.name)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(s, w_host, args.cpu_budget)
