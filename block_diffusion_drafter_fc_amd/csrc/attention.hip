@@ -29,6 +29,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxCtxSplits = 256;            // bounded by plan_attention
+constexpr int kMaxChunk = 1024;               // context keys per workgroup (64 pages)
 constexpr int kMaxParts = kMaxCtxSplits + 1;  // + the block's own keys
 
 // The block's own gamma keys (workgroup s == n_ctx_splits of the same grid):
@@ -107,27 +108,35 @@ __device__ __forceinline__ void attn_block_keys(
   }
 }
 
-template <int DH>
+// Context path.  A tile is 32 keys: P = 32*DH/8 sixteen-byte pieces of K
+// and as many of V.  Each thread moves NPT pieces of each per tile (piece
+// c = tid + i*T, T = 64*G threads; pieces past P re-read the last one and are
+// not stored).  The split's page-table slice is read once into LDS; up to PF
+// tiles of K/V loads are in flight in a register ring while earlier tiles
+// are scored, and the LDS tiles are double-buffered, so a tile costs one
+// barrier.  Loads are never predicated (keys past the end are clamped and
+// masked at the store), which keeps the compiler's wait counts exact.
+template <int DH, int NPT, int PF>
 __global__ __launch_bounds__(512) void k_attn_bf16(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
     const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
     int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err) {
-  // LDS: the context path uses Ks/Vt, the block path two fp32 key/value tiles.
-  constexpr size_t CTX_LDS = (size_t)32 * (DH + 8) * 2 + (size_t)DH * (32 + 8) * 2;
+  constexpr int P = 32 * DH / 8;
+  constexpr size_t KS_B = (size_t)32 * (DH + 8) * 2, VT_B = (size_t)DH * (32 + 8) * 2;
+  constexpr size_t CTX_LDS = 2 * (KS_B + VT_B);
   constexpr size_t BLK_LDS = (size_t)2 * 16 * (DH + 4) * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
-  uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])lds;
-  uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (size_t)32 * (DH + 8) * 2);
+  __shared__ int pg_s[64];
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
   if (s == n_ctx_splits) {
     attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
                         (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4));
     return;
   }
-  const int G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int G = Hq / Hkv, T = 64 * G, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int h = kvh * G + wave;
   const int L = ctx_lens[b];
   const int kbeg = s * chunk;
@@ -153,39 +162,76 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
       qlo[i] = lr < gamma ? ld16(qp + q_plane + i * 32) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  // page-table slice of this split: pages kbeg/16 .. (kend-1)/16, at most
+  // 64 (splits start at multiples of 16 keys), read by wave 0 in one pass
+  const int pg0 = kbeg >> 4, npg = ((kend - 1) >> 4) - pg0 + 1;
+  if (wave == 0) {
+    const int pi = pg0 + (lane < npg ? lane : npg - 1);
+    int pg = page_table[(size_t)b * max_pages + (pi < max_pages ? pi : max_pages - 1)];
+    const bool bad = pi >= max_pages || pg < 0 || pg >= n_pages;
+    if (bad && lane < npg) set_dev_error(err, pi < max_pages ? 1u : 2u);
+    pg_s[lane] = bad ? -1 : pg;
+  }
+  __syncthreads();   // pg_s
+
+  const size_t head_stride = (size_t)16 * DH;            // one page of one head
+  const size_t kv_stride = (size_t)Hkv * head_stride;     // K part -> V part
+  const uint16_t* lpages = pages + ((size_t)layer * n_pages * 2 * Hkv + kvh) * head_stride;
+  const int ntile = (kend - kbeg + 31) >> 5;
+  // piece i of this thread: key row kr[i] of the tile, dimension offset
+  // d8[i].  Consecutive lanes take consecutive keys, so each transposed V
+  // store (one dimension, 32 keys) fills 64 contiguous bytes of a Vt row and
+  // the two half-waves land 32 banks apart: no LDS bank conflicts.
+  int kr[NPT], d8[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    int c = tid + i * T;
+    c = c < P ? c : P - 1;
+    kr[i] = c % 32;
+    d8[i] = (c / 32) * 8;
+  }
+  u32x4 rk[PF][NPT], rv[PF][NPT];
+  auto issue = [&](int t, u32x4* k, u32x4* v) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      int key = kbeg + t * 32 + kr[i];
+      key = key < kend ? key : kend - 1;
+      const int pg = pg_s[(key >> 4) - pg0];
+      const uint16_t* base = lpages + (size_t)(pg < 0 ? 0 : pg) * 2 * kv_stride +
+                             (size_t)(key & 15) * DH + d8[i];
+      k[i] = ld16(base);
+      v[i] = ld16(base + kv_stride);
+    }
+  };
+  auto store = [&](int t, const u32x4* k, const u32x4* v) {
+    uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])(lds + (t & 1) * (KS_B + VT_B));
+    uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (t & 1) * (KS_B + VT_B) + KS_B);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      // (a piece past P was clamped to piece P-1: it stores the same bytes)
+      const int key = kbeg + t * 32 + kr[i];
+      const int kc = key < kend ? key : kend - 1;
+      const bool ok = (key < kend) & (pg_s[(kc >> 4) - pg0] >= 0);   // no short circuit: no branch
+      const u32x4 vk = ok ? k[i] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vv = ok ? v[i] : u32x4{0u, 0u, 0u, 0u};
+      st16(&Ks[kr[i]][d8[i]], vk);
+      const uint16_t* ve = (const uint16_t*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[d8[i] + e][kr[i]] = ve[e];
+    }
+  };
+
   f32x4 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = kLog2e / sqrtf((float)DH);
   const int ra = 8 * (lr >> 2) + (lr & 3), rb = ra + 4;
-  const size_t head_stride = (size_t)16 * DH;            // one page of one head
-  const size_t kv_stride = (size_t)Hkv * head_stride;     // K part -> V part
 
-  for (int t0 = kbeg; t0 < kend; t0 += 32) {
-    for (int c = threadIdx.x; c < 32 * (DH / 8); c += blockDim.x) {
-      const int kr = c / (DH / 8), d8 = (c % (DH / 8)) * 8;
-      const int key = t0 + kr;
-      u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < kend) {
-        const int pi = key >> 4;
-        const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
-        if (pg >= 0 && pg < n_pages) {
-          const uint16_t* base = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
-                                 (size_t)(key & 15) * DH + d8;
-          vk = ld16(base);
-          vv = ld16(base + kv_stride);
-        } else if (d8 == 0) {
-          set_dev_error(err, pi < max_pages ? 1u : 2u);
-        }
-      }
-      st16(&Ks[kr][d8], vk);
-      const uint16_t* ve = (const uint16_t*)&vv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[d8 + e][kr] = ve[e];
-    }
-    __syncthreads();
-
+  auto score = [&](int t) {
+    const int t0 = kbeg + t * 32;
+    uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])(lds + (t & 1) * (KS_B + VT_B));
+    uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (t & 1) * (KS_B + VT_B) + KS_B);
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -212,23 +258,18 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = exp2f(m_run - m_new);
-    uint16_t pb[8], pl[8];
+    uint32_t pw[4], lw[4];
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = exp2f(sv[e] - m_new);
-      pb[e] = f2bf(pe);
-      pl[e] = f2bf(pe - bf2f(pb[e]));
-      psum += pe;
+    for (int e = 0; e < 4; ++e) {
+      const float pa = exp2f(sv[2 * e] - m_new), pb = exp2f(sv[2 * e + 1] - m_new);
+      pw[e] = pack_bf2(pa, pb);
+      lw[e] = pack_bf2(pa - __uint_as_float(pw[e] << 16), pb - __uint_as_float(pw[e] & 0xFFFF0000u));
+      psum += pa + pb;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    u32x4 pop, plo;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pop[e] = (uint32_t)pb[2 * e] | ((uint32_t)pb[2 * e + 1] << 16);
-      plo[e] = (uint32_t)pl[2 * e] | ((uint32_t)pl[2 * e + 1] << 16);
-    }
+    const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]}, plo = {lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       o[d] *= alpha;
@@ -236,7 +277,32 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
       o[d] = mfma_16x16x32(vt, pop, o[d]);
       o[d] = mfma_16x16x32(vt, plo, o[d]);
     }
-    __syncthreads();
+  };
+
+  // prologue: tiles 0 .. PF-1 in flight (tiles past the end re-read the
+  // split's last key and are never stored)
+  // (scheduling barriers keep the tiles' loads in issue order, so waiting for
+  // the oldest tile never waits for the younger ones)
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    issue(j, rk[j], rv[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Whole groups of PF steps, none of them conditional (a skipped step would
+  // make the compiler assume its loads might be missing and wait longer).
+  // Steps past the last tile see only masked keys and add exactly nothing:
+  // tile 0 always holds a key, so the running maximum is finite by then.
+  for (int t0 = 0; t0 < ntile; t0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int t = t0 + j;
+      store(t, rk[j], rv[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(t + PF, rk[j], rv[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      score(t);
+    }
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -382,6 +448,29 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   }
 }
 
+template <int DH, int NPT, int PF>
+hipError_t run_ctx1(const AttnArgs& a, const AttnPlan& p, dim3 grid, dim3 block, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_bf16<DH, NPT, PF>), grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
+                     (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
+                     a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk,
+                     p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+  return hipGetLastError();
+}
+
+// Pieces per thread NPT = ceil(32*DH/8 / (64*G)); the prefetch depth PF
+// keeps the load ring at <= 64 VGPRs.
+template <int DH>
+hipError_t run_ctx(const AttnArgs& a, const AttnPlan& p, dim3 grid, dim3 block, hipStream_t st) {
+  const int P = 32 * DH / 8, T = (int)block.x;
+  switch ((P + T - 1) / T) {
+    case 1: return run_ctx1<DH, 1, 4>(a, p, grid, block, st);
+    case 2: return run_ctx1<DH, 2, 4>(a, p, grid, block, st);
+    case 3: return run_ctx1<DH, 3, 2>(a, p, grid, block, st);
+    case 4: return run_ctx1<DH, 4, 2>(a, p, grid, block, st);
+    default: return run_ctx1<DH, 8, 1>(a, p, grid, block, st);
+  }
+}
+
 }  // namespace
 
 AttnPlan plan_attention(int batch, int n_kv_heads, int max_pages, int page_size) {
@@ -390,8 +479,8 @@ AttnPlan plan_attention(int batch, int n_kv_heads, int max_pages, int page_size)
   long chunk = (cap * batch * n_kv_heads + 1023) / 1024;
   const long min_chunk = (cap + kMaxCtxSplits - 1) / kMaxCtxSplits;
   if (chunk < min_chunk) chunk = min_chunk;
-  chunk = ((chunk + 31) / 32) * 32;
-  if (chunk < 64) chunk = 64;
+  chunk = ((chunk + 127) / 128) * 128;   // whole groups of 4 tiles
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   p.chunk = (int)chunk;
   p.n_ctx_splits = (int)((cap + chunk - 1) / chunk);
   if (p.n_ctx_splits < 1) p.n_ctx_splits = 1;
@@ -410,21 +499,12 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
   // splits 0 .. n_ctx_splits-1: cached context; split n_ctx_splits: block keys
   dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
   dim3 block(64 * (a.Hq / a.Hkv));
-  if (a.gamma > 16) return hipErrorInvalidValue;
-  if (a.dh == 128) {
-    hipLaunchKernelGGL(k_attn_bf16<128>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
-                       (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
-                       a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer,
-                       p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
-  } else if (a.dh == 64) {
-    hipLaunchKernelGGL(k_attn_bf16<64>, grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
-                       (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
-                       a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer,
-                       p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err);
-  } else {
+  if (a.gamma > 16 || p.chunk > kMaxChunk || p.chunk % 128 || p.n_ctx_splits > kMaxCtxSplits ||
+      a.page_size != 16)
     return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.dh == 128) return run_ctx<128>(a, p, grid, block, st);
+  if (a.dh == 64) return run_ctx<64>(a, p, grid, block, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
