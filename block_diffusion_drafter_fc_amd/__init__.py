@@ -116,7 +116,7 @@ class Drafter:
     embed, lm_head, final_norm and l{i}.{attn_norm, wq, wk, wv, wo, mlp_norm,
     w_gate, w_up, w_down})."""
 
-    def __init__(self, cfg: DrafterConfig, weights: dict):
+    def __init__(self, cfg: DrafterConfig, weights: dict, pack: bool = True):
         import torch
         self.lib = _abi.load()
         self.cfg = cfg
@@ -138,6 +138,14 @@ class Drafter:
         _check(self.lib.dflash_model_create(ctypes.byref(self._c_cfg), ctypes.byref(w),
                                             ctypes.c_void_p(self.state.data_ptr()), ctypes.byref(h)))
         self.handle = h
+        self.packed = None
+        nbytes = self.lib.dflash_packed_weight_bytes(self.handle)
+        if pack and nbytes:
+            # weights in matrix-core tile order for the <= 64-row products
+            self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            _check(self.lib.dflash_pack_weights(self.handle, ctypes.c_void_p(self.packed.data_ptr()),
+                                                nbytes, ctypes.c_void_p(stream)))
 
     def close(self):
         if getattr(self, "handle", None):

@@ -17,6 +17,7 @@ MAX_BLOCK = 16
 STATE_BYTES = 16384
 
 EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_bytes",
+            "dflash_packed_weight_bytes", "dflash_pack_weights",
             "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
             "dflash_profile_read"]
@@ -69,6 +70,10 @@ def load(path: str = LIB_PATH):
     lib.dflash_model_destroy.restype = None
     lib.dflash_workspace_bytes.argtypes = [vp, i32, i32, i32, i32]
     lib.dflash_workspace_bytes.restype = sz
+    lib.dflash_packed_weight_bytes.argtypes = [vp]
+    lib.dflash_packed_weight_bytes.restype = sz
+    lib.dflash_pack_weights.argtypes = [vp, vp, sz, vp]
+    lib.dflash_pack_weights.restype = ctypes.c_int
     lib.dflash_inject_ctx.argtypes = [vp, P(KV), vp, vp, i32, i32, vp, sz, vp]
     lib.dflash_inject_ctx.restype = ctypes.c_int
     lib.dflash_draft_block.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp, sz, vp]

@@ -17,6 +17,7 @@ struct dflash_model {
   dflash_weights w;
   uint32_t* err;   // device error word (in the caller's state buffer)
   unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
+  const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
   int device;
   bool bf16;
   bool prof_on;
@@ -94,6 +95,80 @@ bool use_fused(const dflash_model* m, int M) {
 size_t skinny_part_floats(int M, int N, int K, int out, int dh) {
   const GemmPlan p = plan_skinny(M, N, K, out, dh);
   return (size_t)p.splits * M * N;
+}
+
+// Weight matrices of the fused products, as row-stacked segments.
+WSeg seg1(const void* p, int rows) {
+  WSeg w{};
+  w.ptr[0] = p;
+  w.row_end[0] = rows;
+  w.n = 1;
+  return w;
+}
+WSeg wseg_qkv(const dflash_model* m, int l) {
+  const Dims d = dims_of(m->cfg);
+  const dflash_layer_weights& W = m->w.layer[l];
+  WSeg w{};
+  w.ptr[0] = W.wq;
+  w.ptr[1] = W.wk;
+  w.ptr[2] = W.wv;
+  w.row_end[0] = d.QD;
+  w.row_end[1] = d.QD + d.KVD;
+  w.row_end[2] = d.QD + 2 * d.KVD;
+  w.n = 3;
+  return w;
+}
+WSeg wseg_gu(const dflash_model* m, int l) {
+  const Dims d = dims_of(m->cfg);
+  WSeg w{};
+  w.ptr[0] = m->w.layer[l].w_gate;
+  w.ptr[1] = m->w.layer[l].w_up;
+  w.row_end[0] = d.I;
+  w.row_end[1] = 2 * d.I;
+  w.n = 2;
+  return w;
+}
+WSeg wseg_kv(const dflash_model* m) {   // [W_K^0; W_V^0; W_K^1; ...]
+  const Dims d = dims_of(m->cfg);
+  WSeg w{};
+  for (int l = 0; l < d.NL; ++l) {
+    w.ptr[2 * l] = m->w.layer[l].wk;
+    w.ptr[2 * l + 1] = m->w.layer[l].wv;
+    w.row_end[2 * l] = (2 * l + 1) * d.KVD;
+    w.row_end[2 * l + 1] = (2 * l + 2) * d.KVD;
+  }
+  w.n = 2 * d.NL;
+  return w;
+}
+
+// Element offsets of each product's packed weights.
+struct PackLayout {
+  size_t fc, kv, lm, qkv[DFLASH_MAX_LAYERS], o[DFLASH_MAX_LAYERS], gu[DFLASH_MAX_LAYERS],
+      down[DFLASH_MAX_LAYERS], total;
+};
+PackLayout pack_layout(const dflash_model* m) {
+  const Dims d = dims_of(m->cfg);
+  PackLayout P{};
+  size_t off = 0;
+  auto take = [&](int N, int K) {
+    const size_t o = off;
+    off += (packed_elems(N, K) + 127) / 128 * 128;   // 256-byte aligned
+    return o;
+  };
+  P.fc = take(d.D, d.F);
+  P.kv = take(2 * d.NL * d.KVD, d.D);
+  P.lm = take(d.V, d.D);
+  for (int l = 0; l < d.NL; ++l) {
+    P.qkv[l] = take(d.QD + 2 * d.KVD, d.D);
+    P.o[l] = take(d.D, d.QD);
+    P.gu[l] = take(2 * d.I, d.D);
+    P.down[l] = take(d.D, d.I);
+  }
+  P.total = off;
+  return P;
+}
+const uint16_t* packed_at(const dflash_model* m, size_t off) {
+  return m->packed ? m->packed + off : nullptr;
 }
 
 struct DraftLayout {
@@ -247,6 +322,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->w = *w;
   m->err = (uint32_t*)state;
   m->ctr = (unsigned long long*)((char*)state + kCtrOffset);
+  m->packed = nullptr;
   m->device = dev;
   m->bf16 = cfg->dtype == DFLASH_BF16;
   m->prof_on = false;
@@ -283,6 +359,36 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t 
   return need;
 }
 
+size_t dflash_packed_weight_bytes(const dflash_model* m) {
+  if (!m || !m->bf16) return 0;
+  return pack_layout(m).total * 2;
+}
+
+int dflash_pack_weights(dflash_model* m, void* packed, size_t bytes, void* stream) {
+  if (!m || !packed) return fail(DFLASH_E_INVAL, "pack_weights: null argument");
+  if (!m->bf16) return fail(DFLASH_E_DTYPE, "pack_weights: only bf16 models use packed weights");
+  if (((uintptr_t)packed & 255) != 0)
+    return fail(DFLASH_E_INVAL, "pack_weights: buffer must be 256-byte aligned");
+  const PackLayout P = pack_layout(m);
+  if (bytes < P.total * 2)
+    return fail(DFLASH_E_CAPACITY, "pack_weights: buffer %zu bytes < %zu needed", bytes,
+                P.total * 2);
+  const Dims d = dims_of(m->cfg);
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t* out = (uint16_t*)packed;
+  HIPCHK(launch_pack(seg1(m->w.fc_w, d.D), d.D, d.F, 0, out + P.fc, st));
+  HIPCHK(launch_pack(wseg_kv(m), 2 * d.NL * d.KVD, d.D, 0, out + P.kv, st));
+  HIPCHK(launch_pack(seg1(m->w.lm_head, d.V), d.V, d.D, 0, out + P.lm, st));
+  for (int l = 0; l < d.NL; ++l) {
+    HIPCHK(launch_pack(wseg_qkv(m, l), d.QD + 2 * d.KVD, d.D, 0, out + P.qkv[l], st));
+    HIPCHK(launch_pack(seg1(m->w.layer[l].wo, d.D), d.D, d.QD, 0, out + P.o[l], st));
+    HIPCHK(launch_pack(wseg_gu(m, l), 2 * d.I, d.D, d.I, out + P.gu[l], st));
+    HIPCHK(launch_pack(seg1(m->w.layer[l].w_down, d.D), d.D, d.I, 0, out + P.down[l], st));
+  }
+  m->packed = out;
+  return DFLASH_OK;
+}
+
 int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hidden,
                       const int32_t* cu_new, int32_t batch, int32_t n_tok, void* workspace,
                       size_t ws_bytes, void* stream) {
@@ -308,19 +414,10 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   const size_t c_plane = (size_t)n_tok * d.D;
   const void* c_lo = bf ? (const void*)((const uint16_t*)c + c_plane) : nullptr;
 
-  WSeg fc{};
-  fc.ptr[0] = m->w.fc_w;
-  fc.row_end[0] = d.D;
-  fc.n = 1;
-  WSeg kvw{};
-  for (int l = 0; l < d.NL; ++l) {
-    kvw.ptr[2 * l] = m->w.layer[l].wk;
-    kvw.ptr[2 * l + 1] = m->w.layer[l].wv;
-    kvw.row_end[2 * l] = (2 * l + 1) * d.KVD;
-    kvw.row_end[2 * l + 1] = (2 * l + 2) * d.KVD;
-  }
-  kvw.n = 2 * d.NL;
+  const WSeg fc = seg1(m->w.fc_w, d.D);
+  const WSeg kvw = wseg_kv(m);
   const int Nkv = 2 * d.NL * d.KVD;
+  const PackLayout PL = pack_layout(m);
 
   if (L.fused) {
     // c = W_c f (fp32, with per-tile row sums of squares), then the K/V
@@ -332,6 +429,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     a.lda = d.F;
     a.M = n_tok;
     a.w = fc;
+    a.packed = packed_at(m, PL.fc);
     a.N = d.D;
     a.K = d.F;
     a.part = part;
@@ -360,6 +458,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     b.gain = m->w.fc_norm;
     b.eps = m->cfg.rms_eps;
     b.w = kvw;
+    b.packed = packed_at(m, PL.kv);
     b.N = Nkv;
     b.K = d.D;
     b.part = part;
@@ -480,10 +579,8 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
   at.err = m->err;
 
   const int Nqkv = d.QD + 2 * d.KVD;
-  WSeg lm{};
-  lm.ptr[0] = m->w.lm_head;
-  lm.row_end[0] = d.V;
-  lm.n = 1;
+  const WSeg lm = seg1(m->w.lm_head, d.V);
+  const PackLayout PL = pack_layout(m);
   int rc;
 
   if (L.fused) {
@@ -516,14 +613,8 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
       a.ss_in = ss;
       a.ss_tiles = ss_tiles;
       a.gain = W.attn_norm;
-      a.w = WSeg{};
-      a.w.ptr[0] = W.wq;
-      a.w.ptr[1] = W.wk;
-      a.w.ptr[2] = W.wv;
-      a.w.row_end[0] = d.QD;
-      a.w.row_end[1] = d.QD + d.KVD;
-      a.w.row_end[2] = Nqkv;
-      a.w.n = 3;
+      a.w = wseg_qkv(m, l);
+      a.packed = packed_at(m, PL.qkv[l]);
       a.N = Nqkv;
       a.K = d.D;
       a.q = q;
@@ -541,9 +632,8 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
       a.A = o;
       a.a_plane = q_pl;
       a.lda = d.QD;
-      a.w.ptr[0] = W.wo;
-      a.w.row_end[0] = d.D;
-      a.w.n = 1;
+      a.w = seg1(W.wo, d.D);
+      a.packed = packed_at(m, PL.o[l]);
       a.N = d.D;
       a.K = d.QD;
       a.x = x;
@@ -557,11 +647,8 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
       a.ss_in = ss;
       a.ss_tiles = ss_tiles;
       a.gain = W.mlp_norm;
-      a.w.ptr[0] = W.w_gate;
-      a.w.ptr[1] = W.w_up;
-      a.w.row_end[0] = d.I;
-      a.w.row_end[1] = 2 * d.I;
-      a.w.n = 2;
+      a.w = wseg_gu(m, l);
+      a.packed = packed_at(m, PL.gu[l]);
       a.N = 2 * d.I;
       a.K = d.D;
       a.h = h;
@@ -573,9 +660,8 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
       a.A = h;
       a.a_plane = h_pl;
       a.lda = d.I;
-      a.w.ptr[0] = W.w_down;
-      a.w.row_end[0] = d.D;
-      a.w.n = 1;
+      a.w = seg1(W.w_down, d.D);
+      a.packed = packed_at(m, PL.down[l]);
       a.N = d.D;
       a.K = d.I;
       a.x = x;
@@ -589,6 +675,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     a.ss_tiles = ss_tiles;
     a.gain = m->w.final_norm;
     a.w = lm;
+    a.packed = packed_at(m, PL.lm);
     a.N = d.V;
     a.K = d.D;
     a.keys = best;

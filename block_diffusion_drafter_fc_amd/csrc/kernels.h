@@ -75,6 +75,7 @@ struct SkinnyArgs {
   float eps;
   // weights and shape
   WSeg w;
+  const uint16_t* packed;  // the same weights in MFMA tile order (launch_pack), or null
   int N, K;
   // split-K bookkeeping
   float* part;             // [S][M][N]
@@ -117,6 +118,13 @@ GemmPlan plan_skinny(int M, int N, int K, int out, int dh);
 int skinny_tiles(int out, int N, int dh, int I);
 hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs& a,
                          hipStream_t stream);
+// Weights of one fused product in MFMA tile order: the product's virtual rows
+// (swiglu_I > 0: gate/up 64-row groups interleaved) padded to a multiple of
+// 16, 16 x 32 tiles of 1 KB with lane l holding row l % 16, columns 8 (l / 16)
+// .. + 7 of the tile.  packed_elems(N, K) bf16 elements.
+size_t packed_elems(int N, int K);
+hipError_t launch_pack(const WSeg& w, int N, int K, int swiglu_I, uint16_t* out,
+                       hipStream_t stream);
 
 // ---- attention ------------------------------------------------------------
 struct AttnPlan {

@@ -239,7 +239,7 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 // --------------------------------------------------------------- the kernel
 // grid: (n_tiles rounded up to a multiple of 8) * per workgroups of 256
 // threads, per = tile_groups * S.
-template <int MT, int ASRC, int OUT>
+template <int MT, int ASRC, int OUT, bool PACKED>
 __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles) {
   constexpr int U = 8 / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
@@ -264,18 +264,35 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   const int M = a.M, N = a.N, K = a.K;
   const int vcol0 = grp * 64 + wave * 16;                  // virtual column of the wave
   const bool active = vcol0 < N;
-  // Weight rows of this wave: base .. base + 15, inside one segment (inner
-  // boundaries are multiples of 16).  The segment lookup is wave-uniform;
-  // rows past the end (a partial last group, or a wave past N) re-read the
-  // last row and their products are discarded.
-  const int nrows = a.w.row_end[a.w.n - 1];
-  const int base = __builtin_amdgcn_readfirstlane(group_row0<OUT>(grp, a.I) + wave * 16);
-  const int rfirst = base < nrows ? base : nrows - 1;
-  int sgi = 0;
-  while (sgi < a.w.n - 1 && rfirst >= a.w.row_end[sgi]) ++sgi;
-  const int st = sgi ? a.w.row_end[sgi - 1] : 0, en = a.w.row_end[sgi];
-  const int wrow = base + lr < en ? base + lr : en - 1;
-  const uint16_t* bp = (const uint16_t*)a.w.ptr[sgi] + (size_t)(wrow - st) * K + kbeg + lg * 8;
+  // Weight rows of this wave: virtual rows vcol0 .. vcol0 + 15.
+  //  Plain layout: rows of the segments, 16 contiguous bytes per lane at
+  //  column k + 32u + 8 lg (inner segment boundaries are multiples of 16; the
+  //  segment lookup is wave-uniform).  Packed layout: 16-row x 32-column
+  //  tiles of 1 KB in lane order, the product's virtual rows in order, so a
+  //  lane's piece of block kb is 16 bytes at tile (rows/16, kb) + 16 * lane.
+  // Rows past the end (a partial last group, or a wave past N) re-read the
+  // last row (group) and their products are discarded.
+  const uint16_t* bp;
+  int bstride;   // elements from one 32-column block to the next
+  if (PACKED) {
+    const int rg_last = (N + 15) / 16 - 1;
+    int rg = __builtin_amdgcn_readfirstlane(vcol0 / 16);
+    rg = rg < rg_last ? rg : rg_last;
+    bp = a.packed + ((size_t)rg * (K / 32) + kbeg / 32) * 512 + lane * 8;
+    bstride = 512;
+  } else {
+    const int nrows = a.w.row_end[a.w.n - 1];
+    const int base = __builtin_amdgcn_readfirstlane(group_row0<OUT>(grp, a.I) + wave * 16);
+    const int rfirst = base < nrows ? base : nrows - 1;
+    int sgi = 0;
+    while (sgi < a.w.n - 1 && rfirst >= a.w.row_end[sgi]) ++sgi;
+    const int st = sgi ? a.w.row_end[sgi - 1] : 0, en = a.w.row_end[sgi];
+    const int wrow = base + lr < en ? base + lr : en - 1;
+    bp = (const uint16_t*)a.w.ptr[sgi] + (size_t)(wrow - st) * K + kbeg + lg * 8;
+    bstride = 32;
+  }
+  // weights of block u of the sub-chunk at column k of the slice
+  auto wload = [&](int k, int u) { return ld16(bp + (size_t)(k / 32 + u) * bstride); };
 
   // activation chunks this thread stages per sub-chunk: row srow, column scol
   int srow[NCH], scol[NCH];
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   }
   fetch(0);
 #pragma unroll
-  for (int u = 0; u < U; ++u) bc[u] = ld16(bp + u * 32);
+  for (int u = 0; u < U; ++u) bc[u] = wload(0, u);
   __builtin_amdgcn_sched_barrier(0);
   if (ASRC == SA_NORM) {
     // 1 / rms of each row from the producer's per-tile sums of squares
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
     if (LOAD) {
       fetch(k + KC);
 #pragma unroll
-      for (int u = 0; u < U; ++u) bnext[u] = ld16(bp + k + KC + u * 32);
+      for (int u = 0; u < U; ++u) bnext[u] = wload(k + KC, u);
       __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
     }
 #pragma unroll
@@ -509,8 +526,12 @@ template <int MT, int ASRC, int OUT>
 hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
   const int per = tile_groups(OUT, a.dh) * p.splits;
   const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT>), dim3(padded * per), dim3(256), 0, st, a, p.splits,
-                     p.kpw, n_tiles);
+  if (a.packed != nullptr)
+    hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true>), dim3(padded * per), dim3(256), 0, st, a,
+                       p.splits, p.kpw, n_tiles);
+  else
+    hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, false>), dim3(padded * per), dim3(256), 0, st, a,
+                       p.splits, p.kpw, n_tiles);
   return hipGetLastError();
 }
 
@@ -522,7 +543,49 @@ hipError_t run_mt(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream
   return hipErrorInvalidValue;
 }
 
+// Pack the virtual rows [0, N) of a product's weight matrix (segments w;
+// with swiglu_I > 0 the gate/up interleave of 64-row groups) into 16-row x
+// 32-column tiles of 1 KB in MFMA lane order: 16-byte unit u = 64 t + l of
+// tile t = rg * K/32 + kb holds row 16 rg + l % 16, columns 32 kb + 8 (l / 16)
+// .. + 7.  Rows N .. 16 ceil(N/16) - 1 are zero.
+__global__ __launch_bounds__(256) void k_pack(WSeg w, int N, int K, int swiglu_I,
+                                             uint16_t* __restrict__ out, size_t units) {
+  const int kbs = K / 32;
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = u / 64;
+    const int l = (int)(u % 64), kb = (int)(t % kbs);
+    const int vrow = (int)(t / kbs) * 16 + l % 16, col = kb * 32 + (l / 16) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (vrow < N) {
+      int row = vrow;
+      if (swiglu_I > 0) {
+        const int g = vrow / 64;
+        row = ((g & 1) ? swiglu_I + 64 * (g >> 1) : 64 * (g >> 1)) + vrow % 64;
+      }
+      int sg = 0;
+      while (sg < w.n - 1 && row >= w.row_end[sg]) ++sg;
+      const int st = sg ? w.row_end[sg - 1] : 0;
+      v = ld16((const uint16_t*)w.ptr[sg] + (size_t)(row - st) * K + col);
+    }
+    st16(out + u * 8, v);
+  }
+}
+
 }  // namespace
+
+size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16 * 16) * (size_t)K; }
+
+hipError_t launch_pack(const WSeg& w, int N, int K, int swiglu_I, uint16_t* out, hipStream_t st) {
+  if (N <= 0 || K % 32 || w.n < 1 || w.row_end[w.n - 1] < (swiglu_I > 0 ? 2 * swiglu_I : N))
+    return hipErrorInvalidValue;
+  if (swiglu_I > 0 && (N != 2 * swiglu_I || swiglu_I % 64)) return hipErrorInvalidValue;
+  const size_t units = packed_elems(N, K) / 8;
+  const size_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, st,
+                     w, N, K, swiglu_I, out, units);
+  return hipGetLastError();
+}
 
 GemmPlan plan_skinny(int M, int N, int K, int out, int dh) {
   GemmPlan p{};

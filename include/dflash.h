@@ -154,6 +154,24 @@ void dflash_model_destroy(dflash_model* model);
 size_t dflash_workspace_bytes(const dflash_model* model, int32_t max_batch, int32_t max_block,
                               int32_t max_new_tokens, int32_t max_pages_per_seq);
 
+/* Packed weights (bf16 models).  The products with at most 64 rows (block
+ * rows of up to 4 sequences, or up to 64 injected tokens) stream their
+ * weights faster from a copy in matrix-core tile order: for each product,
+ * its rows in the order the kernel walks them, padded to a multiple of 16,
+ * cut into 16-row x 32-column tiles of 1 KB whose 16-byte pieces sit in the
+ * order of the lanes that consume them, so every weight load of a wave
+ * reads 1 KB of contiguous memory.
+ *   dflash_packed_weight_bytes: size of that copy (0 for fp32 models).
+ *   dflash_pack_weights: fills `packed` [device, caller-owned, 256-byte
+ *     aligned, >= dflash_packed_weight_bytes] from the model's weights on
+ *     `stream` and makes the model use it from then on; calls on other
+ *     streams must be ordered after the packing.  The caller keeps the
+ *     buffer alive for the handle's lifetime, and the original weights too
+ *     (the other paths read them).  Returns DFLASH_E_DTYPE for fp32 models,
+ *     DFLASH_E_CAPACITY if `bytes` is too small. */
+size_t dflash_packed_weight_bytes(const dflash_model* model);
+int dflash_pack_weights(dflash_model* model, void* packed, size_t bytes, void* stream);
+
 /* Context injection (summary page: "Target Hidden States Supply the Missing
  * Context", eq. H_t = RMSNorm(W_c [H^(l1); ...; H^(lm)]), and "Per-Layer K/V
  * Injection Prevents Context Dilution", K_i = [W_i^K H_t; ...],

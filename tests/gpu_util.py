@@ -54,12 +54,13 @@ def drafter_config(s: Shape, max_block=None):
                          rms_eps=s.eps)
 
 
-def make_drafter(s: Shape, weights_np: dict | None = None):
-    """(Drafter, host weights) with device copies of the seeded weights."""
+def make_drafter(s: Shape, weights_np: dict | None = None, pack: bool = True):
+    """(Drafter, host weights) with device copies of the seeded weights; bf16
+    models get packed weights unless pack is False."""
     from block_diffusion_drafter_fc_amd import Drafter
     w = weights_np if weights_np is not None else make_weights(s)
     dev = {k: to_dev(v, s.bf16) for k, v in w.items()}
-    return Drafter(drafter_config(s), dev), w, dev
+    return Drafter(drafter_config(s), dev, pack=pack), w, dev
 
 
 class PagedCache:

@@ -6,7 +6,8 @@ token must be the oracle's argmax unless the oracle's top-2 gap there is
 below that tolerance.
 
 Covers: the five workloads (the batch-32, long-context and wide ones on
-sampled sequences), every GEMM path (1, 2, 4 row tiles and the tiled kernel),
+sampled sequences), every GEMM path (1, 2, 4 row tiles and the tiled kernel,
+packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
 one, determinism, batch invariance, and the device error word."""
 import numpy as np
@@ -64,10 +65,11 @@ def check_seq(s, model, dense, L, anchor, gamma, gpu_block, gpu_logits):
     return err, tolerated
 
 
-def run_case(s, ctx_lens, gamma, sample=None, weights=None):
-    log(f"draft {s.name}: batch {len(ctx_lens)} block {gamma} contexts {list(ctx_lens)[:8]}")
+def run_case(s, ctx_lens, gamma, sample=None, weights=None, pack=True):
+    log(f"draft {s.name}: batch {len(ctx_lens)} block {gamma} contexts {list(ctx_lens)[:8]}"
+        f"{'' if pack else ' (unpacked weights)'}")
     w = weights if weights is not None else make_weights(s)
-    drafter, w, _ = make_drafter(s, w)
+    drafter, w, _ = make_drafter(s, w, pack=pack)
     pps = pages_for(max(ctx_lens))
     cache, kv, dense = setup_cache(s, ctx_lens, pps)
     anc = anchors(s, len(ctx_lens), tag=f"draft.anchor.{gamma}")
@@ -115,6 +117,12 @@ def test_draft_mini_bf16_paths_and_ragged_contexts(ctx):
     # skinny product, then the tiled product; contexts include 0, non-multiples
     # of 16 and of 32, and several context splits.
     run_case(MINI, ctx, 16)
+
+
+@pytest.mark.parametrize("ctx", [[37], [5, 0, 129]])
+def test_draft_mini_bf16_unpacked_weights(ctx):
+    # the row-major weight path of the skinny products (no packed copy)
+    run_case(MINI, ctx, 16, pack=False)
 
 
 @pytest.mark.parametrize("gamma", [1, 7])
