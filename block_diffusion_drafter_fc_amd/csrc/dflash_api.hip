@@ -17,6 +17,8 @@ struct dflash_model {
   dflash_weights w;
   uint32_t* err;   // device error word (in the caller's state buffer)
   unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
+  unsigned long long* amax;  // LM-head argmax slots and their counter (same buffer)
+  unsigned long long* actr;
   const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
   int device;
   bool bf16;
@@ -71,8 +73,12 @@ size_t part_floats(bool bf16, int M, int N, int K) {
   return (size_t)p.splits * M * N;
 }
 
-// Counters after the error word in the state buffer.
-constexpr size_t kCtrOffset = 256;
+// State buffer: the error word, then the LM-head argmax slots [8 XCDs][64
+// rows] and their arrival counter, then one arrival counter per output tile
+// of a fused product.  Every call leaves all of them at zero.
+constexpr size_t kAmaxOffset = 256;
+constexpr size_t kActrOffset = kAmaxOffset + 8 * 64 * 8;
+constexpr size_t kCtrOffset = kActrOffset + 256;
 constexpr int kMaxCounters = (int)((DFLASH_STATE_BYTES - kCtrOffset) / 8);
 
 // bf16 models with at most 64 product rows run the fused skinny products
@@ -219,13 +225,11 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
   L.parts = bf ? L.ap.n_ctx_splits + 1 : 1;
   L.att_o = take((size_t)L.parts * M * d.Hq * d.dh * 4);
   L.att_ml = take((size_t)L.parts * M * d.Hq * 2 * 4);
-  if (L.fused) {
-    L.groups = (d.V + 63) / 64;
-  } else {
+  if (!L.fused) {   // the fused LM head merges its keys in the state buffer
     const GemmPlan lm = plan_gemm(bf, Mi, d.V, d.D, true);
     L.groups = gemm_argmax_groups(lm, d.V);
+    L.best = take((size_t)L.groups * M * 8);
   }
-  L.best = take((size_t)L.groups * M * 8);
   L.total = off;
   return L;
 }
@@ -322,6 +326,8 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->w = *w;
   m->err = (uint32_t*)state;
   m->ctr = (unsigned long long*)((char*)state + kCtrOffset);
+  m->amax = (unsigned long long*)((char*)state + kAmaxOffset);
+  m->actr = (unsigned long long*)((char*)state + kActrOffset);
   m->packed = nullptr;
   m->device = dev;
   m->bf16 = cfg->dtype == DFLASH_BF16;
@@ -678,12 +684,14 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     a.packed = packed_at(m, PL.lm);
     a.N = d.V;
     a.K = d.D;
-    a.keys = best;
+    a.amax = m->amax;
+    a.actr = m->actr;
+    a.anchor = anchor;
+    a.block_tokens = block_tokens;
     a.logits = logits;
     if ((rc = prof_begin()) != DFLASH_OK) return rc;
     HIPCHK(launch_skinny(plan_skinny(M, d.V, d.D, SO_ARGMAX, d.dh), SA_NORM, SO_ARGMAX, a, st));
     if ((rc = prof_end()) != DFLASH_OK) return rc;
-    HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
     return DFLASH_OK;
   }
 

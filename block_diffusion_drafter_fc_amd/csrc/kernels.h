@@ -81,8 +81,13 @@ struct SkinnyArgs {
   float* part;             // [S][M][N]
   unsigned long long* ctr; // one arrival counter per output tile, zero between launches
   uint32_t* err;
-  // SO_ARGMAX
-  uint64_t* keys;          // [ceil(N/64) groups][M]
+  // SO_ARGMAX: row argmax keys merged into amax[8 XCDs][64] (zero between
+  // launches); the last workgroup writes block_tokens[M] (row r = b*gamma + j:
+  // anchor[b] for j == 0, else the argmax column) and re-zeroes amax and actr
+  unsigned long long* amax;
+  unsigned long long* actr;
+  const int32_t* anchor;
+  int32_t* block_tokens;
   float* logits;           // [M][N] or null
   // SO_QKV
   void* q;
@@ -120,8 +125,9 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
                          hipStream_t stream);
 // Weights of one fused product in MFMA tile order: the product's virtual rows
 // (swiglu_I > 0: gate/up 64-row groups interleaved) padded to a multiple of
-// 16, 16 x 32 tiles of 1 KB with lane l holding row l % 16, columns 8 (l / 16)
-// .. + 7 of the tile.  packed_elems(N, K) bf16 elements.
+// 64, 16 x 32 tiles of 1 KB with lane l holding row l % 16, columns 8 (l / 16)
+// .. + 7 of the tile, ordered [64-row group][32-column block][16-row group].
+// packed_elems(N, K) bf16 elements.
 size_t packed_elems(int N, int K);
 hipError_t launch_pack(const WSeg& w, int N, int K, int swiglu_I, uint16_t* out,
                        hipStream_t stream);

@@ -268,18 +268,17 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   //  Plain layout: rows of the segments, 16 contiguous bytes per lane at
   //  column k + 32u + 8 lg (inner segment boundaries are multiples of 16; the
   //  segment lookup is wave-uniform).  Packed layout: 16-row x 32-column
-  //  tiles of 1 KB in lane order, the product's virtual rows in order, so a
-  //  lane's piece of block kb is 16 bytes at tile (rows/16, kb) + 16 * lane.
+  //  tiles of 1 KB in lane order, the product's virtual rows in order, the
+  //  four tiles of a 64-row group adjacent per 32-column block.
   // Rows past the end (a partial last group, or a wave past N) re-read the
   // last row (group) and their products are discarded.
   const uint16_t* bp;
   int bstride;   // elements from one 32-column block to the next
   if (PACKED) {
-    const int rg_last = (N + 15) / 16 - 1;
-    int rg = __builtin_amdgcn_readfirstlane(vcol0 / 16);
-    rg = rg < rg_last ? rg : rg_last;
-    bp = a.packed + ((size_t)rg * (K / 32) + kbeg / 32) * 512 + lane * 8;
-    bstride = 512;
+    // [64-row group][32-column block][wave][1 KB tile]: the four waves of a
+    // workgroup read 4 adjacent KB per block (rows padded to 64 with zeros)
+    bp = a.packed + (((size_t)grp * (K / 32) + kbeg / 32) * 4 + wave) * 512 + lane * 8;
+    bstride = 4 * 512;
   } else {
     const int nrows = a.w.row_end[a.w.n - 1];
     const int base = __builtin_amdgcn_readfirstlane(group_row0<OUT>(grp, a.I) + wave * 16);
@@ -435,7 +434,11 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   }
 
   if (OUT == SO_ARGMAX) {
-    // per wave over its 16 columns, then over the 4 waves; keys[grp][row]
+    // Row argmax keys (ordered value bits | inverted column): per wave over
+    // its 16 columns, then over the 4 waves, then a 64-bit atomic max into
+    // this XCD's slot of the row.  The last workgroup to arrive reads the 8
+    // slots of every row (device-scope atomic loads), writes the block
+    // tokens, and re-zeroes the slots and the counter for the next launch.
     __shared__ uint64_t wkeys[4][ROWS];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -453,12 +456,32 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
         if (lr == 0) wkeys[wave][row] = key;
       }
     __syncthreads();
+    const unsigned slot = xcc_id() & 7u;
     if (tid < ROWS && tid < M) {
       uint64_t key = wkeys[0][tid];
 #pragma unroll
       for (int w = 1; w < 4; ++w) key = wkeys[w][tid] > key ? wkeys[w][tid] : key;
-      a.keys[(size_t)grp * M + tid] = key;
+      atomicMax(&a.amax[slot * 64 + tid], (unsigned long long)key);
     }
+    __builtin_amdgcn_s_waitcnt(0);   // the atomics are performed
+    __syncthreads();
+    if (tid == 0) sh_old = atomicAdd(a.actr, 1ull);
+    __syncthreads();
+    if (sh_old != (unsigned long long)(n_tiles - 1)) return;
+    if (tid < M) {
+      uint64_t key = 0;
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) {
+        const uint64_t k2 = __hip_atomic_load(&a.amax[x * 64 + tid], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        key = k2 > key ? k2 : key;
+      }
+      const int j = tid % a.gamma;
+      a.block_tokens[tid] = j == 0 ? a.anchor[tid / a.gamma] : (int32_t)argmax_key_index(key);
+    }
+    __syncthreads();
+    for (int i = tid; i < kXcds * 64; i += 256) atomicExch(&a.amax[i], 0ull);
+    if (tid == 0) atomicExch(a.actr, 0ull);
     return;
   }
 
@@ -545,23 +568,25 @@ hipError_t run_mt(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream
 
 // Pack the virtual rows [0, N) of a product's weight matrix (segments w;
 // with swiglu_I > 0 the gate/up interleave of 64-row groups) into 16-row x
-// 32-column tiles of 1 KB in MFMA lane order: 16-byte unit u = 64 t + l of
-// tile t = rg * K/32 + kb holds row 16 rg + l % 16, columns 32 kb + 8 (l / 16)
-// .. + 7.  Rows N .. 16 ceil(N/16) - 1 are zero.
+// 32-column tiles of 1 KB in MFMA lane order, ordered [64-row group g]
+// [32-column block kb][16-row group w of the 64][tile]: 16-byte unit u =
+// 64 t + l of tile t = (g * K/32 + kb) * 4 + w holds row 64 g + 16 w + l % 16,
+// columns 32 kb + 8 (l / 16) .. + 7.  Rows N .. 64 ceil(N/64) - 1 are zero.
 __global__ __launch_bounds__(256) void k_pack(WSeg w, int N, int K, int swiglu_I,
                                              uint16_t* __restrict__ out, size_t units) {
   const int kbs = K / 32;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
        u += (size_t)gridDim.x * blockDim.x) {
     const size_t t = u / 64;
-    const int l = (int)(u % 64), kb = (int)(t % kbs);
-    const int vrow = (int)(t / kbs) * 16 + l % 16, col = kb * 32 + (l / 16) * 8;
+    const int l = (int)(u % 64), wv = (int)(t % 4), kb = (int)((t / 4) % kbs);
+    const int g = (int)(t / 4 / kbs);
+    const int vrow = g * 64 + wv * 16 + l % 16, col = kb * 32 + (l / 16) * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (vrow < N) {
       int row = vrow;
       if (swiglu_I > 0) {
-        const int g = vrow / 64;
-        row = ((g & 1) ? swiglu_I + 64 * (g >> 1) : 64 * (g >> 1)) + vrow % 64;
+        const int gg = vrow / 64;
+        row = ((gg & 1) ? swiglu_I + 64 * (gg >> 1) : 64 * (gg >> 1)) + vrow % 64;
       }
       int sg = 0;
       while (sg < w.n - 1 && row >= w.row_end[sg]) ++sg;
@@ -574,7 +599,7 @@ __global__ __launch_bounds__(256) void k_pack(WSeg w, int N, int K, int swiglu_I
 
 }  // namespace
 
-size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16 * 16) * (size_t)K; }
+size_t packed_elems(int N, int K) { return (size_t)((N + 63) / 64 * 64) * (size_t)K; }
 
 hipError_t launch_pack(const WSeg& w, int N, int K, int swiglu_I, uint16_t* out, hipStream_t st) {
   if (N <= 0 || K % 32 || w.n < 1 || w.row_end[w.n - 1] < (swiglu_I > 0 ? 2 * swiglu_I : N))
@@ -626,7 +651,9 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
   if ((p.mt == 1 && a.M > 16) || (p.mt == 2 && a.M > 32)) return hipErrorInvalidValue;
   const int n_tiles = skinny_tiles(out, a.N, a.dh, a.I);
   if (n_tiles < 0) return hipErrorInvalidValue;
-  if (out == SO_ARGMAX && p.splits != 1) return hipErrorInvalidValue;
+  if (out == SO_ARGMAX && (p.splits != 1 || a.amax == nullptr || a.actr == nullptr ||
+                           a.anchor == nullptr || a.block_tokens == nullptr || a.gamma < 1))
+    return hipErrorInvalidValue;
   if (tile_groups(out, a.dh) * p.splits > kMaxPer) return hipErrorInvalidValue;
   if (asrc == SA_NORM && (a.ss_in == nullptr || a.ss_tiles < 1 || a.ss_tiles > kMaxSsTiles ||
                           a.gain == nullptr))

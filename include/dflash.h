@@ -138,8 +138,9 @@ typedef struct dflash_model dflash_model;   /* opaque host handle */
 /* Create a model handle.  cfg and w are [host] structs; the weight pointers
  * are device pointers the caller keeps alive for the handle's lifetime.
  * state: device buffer of DFLASH_STATE_BYTES bytes owned by the caller (it
- * holds the sticky device error word and the arrival counters of the split-K
- * reductions, which every call leaves at zero); it is cleared here
+ * holds the sticky device error word, the LM-head argmax slots and the
+ * arrival counters of the split-K reductions, which every call leaves at
+ * zero); it is cleared here
  * (synchronously).  The handle binds to the device current at creation.
  * Calls that share a handle must be ordered (one stream, or streams joined
  * by events): concurrent calls on one handle race on its counters. */
@@ -157,10 +158,11 @@ size_t dflash_workspace_bytes(const dflash_model* model, int32_t max_batch, int3
 /* Packed weights (bf16 models).  The products with at most 64 rows (block
  * rows of up to 4 sequences, or up to 64 injected tokens) stream their
  * weights faster from a copy in matrix-core tile order: for each product,
- * its rows in the order the kernel walks them, padded to a multiple of 16,
+ * its rows in the order the kernel walks them, padded to a multiple of 64,
  * cut into 16-row x 32-column tiles of 1 KB whose 16-byte pieces sit in the
- * order of the lanes that consume them, so every weight load of a wave
- * reads 1 KB of contiguous memory.
+ * order of the lanes that consume them, stored [64-row group][32-column
+ * block][16-row group]; every weight load of a wave reads 1 KB of contiguous
+ * memory and the four waves of a workgroup read 4 adjacent KB.
  *   dflash_packed_weight_bytes: size of that copy (0 for fp32 models).
  *   dflash_pack_weights: fills `packed` [device, caller-owned, 256-byte
  *     aligned, >= dflash_packed_weight_bytes] from the model's weights on

@@ -1,8 +1,9 @@
 """Packed weights (dflash_pack_weights) against the layout the header defines:
 for every fused product, its rows in kernel order (gate/up: 64-row groups of
-gate and up alternating), padded to a multiple of 16 with zeros, cut into
+gate and up alternating), padded to a multiple of 64 with zeros, cut into
 16-row x 32-column tiles of 512 bf16, in which 16-byte piece l holds row
-l % 16 and columns 8 (l // 16) .. + 7 of the tile.  The products follow one
+l % 16 and columns 8 (l // 16) .. + 7 of the tile, the tiles ordered
+[64-row group][32-column block][16-row group].  The products follow one
 another in the order fc, K/V of all layers, LM head, then per layer QKV, O,
 gate/up, down, each starting at a multiple of 128 elements.  Bit-exact."""
 import numpy as np
@@ -19,11 +20,11 @@ MINI = Shape("mini-bf16-pack", 512, 2, 4, 2, 128, 768, 1000, 16, 1, True, seed=9
 def tiles(rows):
     """rows [N][K] uint16 -> packed uint16 vector of the defined tile order."""
     N, K = rows.shape
-    Np = (N + 15) // 16 * 16
+    Np = (N + 63) // 64 * 64
     pad = np.zeros((Np, K), np.uint16)
     pad[:N] = rows
-    # [rg][r][kb][g][8] -> [rg][kb][g][r][8]  (piece l = 16 g + r)
-    t = pad.reshape(Np // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+    # [g][w][r][kb][q][8] -> [g][kb][w][q][r][8]   (piece l = 16 q + r)
+    t = pad.reshape(Np // 64, 4, 16, K // 32, 4, 8).transpose(0, 3, 1, 4, 2, 5)
     return t.reshape(-1)
 
 
