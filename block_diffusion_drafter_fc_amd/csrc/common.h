@@ -77,6 +77,9 @@ DF_DEV f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 DF_DEV u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+// Streaming load of data read once per launch (weights): the non-temporal
+// hint keeps it from displacing reused lines in the caches.
+DF_DEV u32x4 ld16_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 DF_DEV void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
 // Order-preserving map of an fp32 value onto uint32 (finite inputs).

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bc[u][t] = ld16(bp[t] + u * 32);
+      for (int t = 0; t < NT; ++t) bc[u][t] = ld16_stream(bp[t] + u * 32);
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) bn[u][t] = ld16(bp[t] + k + KC + u * 32);
+          for (int t = 0; t < NT; ++t) bn[u][t] = ld16_stream(bp[t] + k + KC + u * 32);
       }
     }
     if (active) {

@@ -36,11 +36,13 @@
 namespace {
 
 constexpr int kXcds = 8;
-// Workgroups a split-K launch aims for: every fused launch pays a per-
-// workgroup start and publish latency, so about two workgroups per CU with
-// longer K slices beat many short ones (measured on the Qwen3-8B-shaped
-// draft: each product lands within ~0.6 us of its best split).
-constexpr int kWgTarget = 512;
+// Workgroups a split-K launch aims for: every workgroup pays a start and
+// publish latency, so fewer workgroups with longer K slices beat many short
+// ones.  Measured with packed weights on the Qwen3-8B-shaped draft and inject
+// (M <= 16): QKV, O, down and the fc were fastest at ~256-384 workgroups
+// (S = 4), SwiGLU and K/V products at 640-768 (S = 2 and 4).
+constexpr int kWgTarget = 256;
+constexpr int kWgTargetPaired = 640;   // SO_SWIGLU, SO_KV
 constexpr int kMaxSplits = 16;
 constexpr int kMaxPer = 63;       // arrivals per tile (6-bit per-XCD fields)
 constexpr int kMaxSsTiles = 128;  // row sum-of-squares pieces (hidden <= 8192)
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
     bstride = 32;
   }
   // weights of block u of the sub-chunk at column k of the slice
-  auto wload = [&](int k, int u) { return ld16(bp + (size_t)(k / 32 + u) * bstride); };
+  auto wload = [&](int k, int u) { return ld16_stream(bp + (size_t)(k / 32 + u) * bstride); };
 
   // activation chunks this thread stages per sub-chunk: row srow, column scol
   int srow[NCH], scol[NCH];
@@ -627,7 +629,7 @@ GemmPlan plan_skinny(int M, int N, int K, int out, int dh) {
       if (nk % s) continue;
       if (s > kMaxSplits || tg * s > kMaxPer) break;
       S = s;
-      if (groups * s >= kWgTarget) break;
+      if (groups * s >= ((out == SO_SWIGLU || out == SO_KV) ? kWgTargetPaired : kWgTarget)) break;
     }
   }
   p.splits = S;
