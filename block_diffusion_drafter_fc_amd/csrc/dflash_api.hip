@@ -19,6 +19,7 @@ struct dflash_model {
   unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
   unsigned long long* amax;  // LM-head argmax slots and their counter (same buffer)
   unsigned long long* actr;
+  uint32_t* qhint;           // workgroup -> XCD rotation of the last split-K launch (same buffer)
   const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
   int device;
   bool bf16;
@@ -73,9 +74,11 @@ size_t part_floats(bool bf16, int M, int N, int K) {
   return (size_t)p.splits * M * N;
 }
 
-// State buffer: the error word, then the LM-head argmax slots [8 XCDs][64
-// rows] and their arrival counter, then one arrival counter per output tile
-// of a fused product.  Every call leaves all of them at zero.
+// State buffer: the error word; at 128 the workgroup -> XCD rotation the last
+// split-K launch observed; then the LM-head argmax slots [8 XCDs][64 rows]
+// and their arrival counter, then one arrival counter per output tile of a
+// fused product.  Every call leaves the slots and counters at zero.
+constexpr size_t kQhintOffset = 128;
 constexpr size_t kAmaxOffset = 256;
 constexpr size_t kActrOffset = kAmaxOffset + 8 * 64 * 8;
 constexpr size_t kCtrOffset = kActrOffset + 256;
@@ -328,6 +331,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->ctr = (unsigned long long*)((char*)state + kCtrOffset);
   m->amax = (unsigned long long*)((char*)state + kAmaxOffset);
   m->actr = (unsigned long long*)((char*)state + kActrOffset);
+  m->qhint = (uint32_t*)((char*)state + kQhintOffset);
   m->packed = nullptr;
   m->device = dev;
   m->bf16 = cfg->dtype == DFLASH_BF16;
@@ -440,6 +444,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     a.K = d.F;
     a.part = part;
     a.ctr = m->ctr;
+    a.qhint = m->qhint;
     a.err = m->err;
     a.dh = d.dh;
     a.I = d.I;
@@ -469,6 +474,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     b.K = d.D;
     b.part = part;
     b.ctr = m->ctr;
+    b.qhint = m->qhint;
     b.err = m->err;
     b.Hkv = d.Hkv;
     b.dh = d.dh;
@@ -602,6 +608,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     base.eps = eps;
     base.part = part;
     base.ctr = m->ctr;
+    base.qhint = m->qhint;
     base.err = m->err;
     base.gamma = gamma;
     base.Hq = d.Hq;

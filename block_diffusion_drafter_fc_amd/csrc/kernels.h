@@ -81,6 +81,7 @@ struct SkinnyArgs {
   float* part;             // [S][M][N]
   unsigned long long* ctr; // one arrival counter per output tile, zero between launches
   uint32_t* err;
+  uint32_t* qhint;         // workgroup -> XCD rotation seen by the previous launch (or null)
   // SO_ARGMAX: row argmax keys merged into amax[8 XCDs][64] (zero between
   // launches); the last workgroup writes block_tokens[M] (row r = b*gamma + j:
   // anchor[b] for j == 0, else the argmax column) and re-zeroes amax and actr

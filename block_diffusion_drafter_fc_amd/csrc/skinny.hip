@@ -22,8 +22,12 @@
 // finished workgroup waits for its partial stores, adds its arrival to the
 // tile's counter, and the last to arrive drops its L1, sums the partials in
 // split order and applies the epilogue (RoPE, SwiGLU, residual + row sums of
-// squares, K/V page store).  The counter also counts arrivals per XCD (read
-// from the XCC_ID register).  A workgroup away from the tile's home XCD
+// squares, K/V page store).  The dispatcher's round robin starts at an XCD
+// that is fixed per hardware queue (not always XCD 0 once a process has
+// several streams), so each launch takes the rotation workgroup 0 saw in the
+// previous launch (a word of the state buffer) as the expected placement.
+// The counter also counts arrivals per XCD (read from the XCC_ID register).
+// A workgroup away from the tile's home XCD
 // writes its partials back with a device-scope fence; a reducer that saw
 // arrivals from another XCD acquires at device scope; a reducer away from
 // home while home workgroups also wrote (their partials then sit in another
@@ -261,6 +265,8 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   const int id = blockIdx.x, xcd = id % kXcds, local = id / kXcds;
   const int tile = (local / per) * kXcds + xcd, member = local % per;
   if (tile >= n_tiles) return;
+  // queue rotation of the workgroup -> XCD placement (see the publish step)
+  const unsigned rot = (OUT != SO_ARGMAX && a.qhint != nullptr) ? (*a.qhint & 7u) : 0u;
   const int grp = tile * tg + member / S, split = member % S;
   const int kbeg = split * kps;
   const int M = a.M, N = a.N, K = a.K;
@@ -516,9 +522,13 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   if (OUT == SO_PART) return;
 
   // Publish the slice and count the arrival: bits 0..15 count all arrivals,
-  // the 6-bit field at 16 + 6x counts those from XCD x.
+  // the 6-bit field at 16 + 6x counts those from XCD x.  Workgroup i is
+  // expected on XCD (i + rot) mod 8, rot being the rotation that workgroup 0
+  // of the previous launch observed (it is fixed per hardware queue).
   const unsigned xcc = xcc_id();
-  const bool home = xcc == (unsigned)xcd;
+  const unsigned homex = (unsigned)(xcd + rot) & 7u;
+  const bool home = xcc == homex;
+  if (blockIdx.x == 0 && tid == 0 && a.qhint != nullptr) *a.qhint = (xcc - (unsigned)xcd) & 7u;
   if (home) __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are in the XCD's L2
   else __threadfence();                       // write back for readers on other XCDs
   __syncthreads();
@@ -534,7 +544,7 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
     if ((unsigned)x != (xcc & 7u) && ((tot >> (16 + 6 * x)) & 63u) != 0) foreign = true;
   if (foreign) {
     __threadfence();
-    if (!home && ((tot >> (16 + 6 * xcd)) & 63u) != 0 && tid == 0) set_dev_error(a.err, kErrXcd);
+    if (!home && ((tot >> (16 + 6 * homex)) & 63u) != 0 && tid == 0) set_dev_error(a.err, kErrXcd);
   } else {
     asm volatile("buffer_inv sc0" ::: "memory");   // drop this CU's L1 copies
   }

@@ -140,7 +140,8 @@ typedef struct dflash_model dflash_model;   /* opaque host handle */
  * state: device buffer of DFLASH_STATE_BYTES bytes owned by the caller (it
  * holds the sticky device error word, the LM-head argmax slots and the
  * arrival counters of the split-K reductions, which every call leaves at
- * zero); it is cleared here
+ * zero, and the workgroup placement the last split-K launch observed); it is
+ * cleared here
  * (synchronously).  The handle binds to the device current at creation.
  * Calls that share a handle must be ordered (one stream, or streams joined
  * by events): concurrent calls on one handle race on its counters. */
