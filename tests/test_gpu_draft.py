@@ -163,7 +163,7 @@ def test_draft_on_other_streams_is_bit_identical():
     ctx = [33, 250, 7]
     drafter, kv, anc, blk, lg, pps = run_case(s, ctx, 16, weights=w)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    for st in streams + streams[::-1]:
+    for st in (streams + streams[::-1]) * 3:
         with torch.cuda.stream(st):
             b2, l2 = gpu_draft(drafter, kv, anc, 16, pps)
         assert np.array_equal(blk, b2) and np.array_equal(lg, l2)
