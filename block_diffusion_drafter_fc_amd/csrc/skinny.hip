@@ -42,10 +42,12 @@ namespace {
 constexpr int kXcds = 8;
 // Workgroups a split-K launch aims for: every workgroup pays a start and
 // publish latency, so fewer workgroups with longer K slices beat many short
-// ones.  Measured with packed weights on the Qwen3-8B-shaped draft and inject
-// (M <= 16): QKV, O, down and the fc were fastest at ~256-384 workgroups
-// (S = 4), SwiGLU and K/V products at 640-768 (S = 2 and 4).
+// ones.  Measured with packed weights and streaming loads on the
+// Qwen3-8B-shaped draft and inject (M <= 16): O, down and the fc were
+// fastest at 256 workgroups (S = 4), QKV at 192 (S = 2), SwiGLU and K/V at
+// 640-768 (S = 2 and 4).
 constexpr int kWgTarget = 256;
+constexpr int kWgTargetQkv = 192;
 constexpr int kWgTargetPaired = 640;   // SO_SWIGLU, SO_KV
 constexpr int kMaxSplits = 16;
 constexpr int kMaxPer = 63;       // arrivals per tile (6-bit per-XCD fields)
@@ -639,7 +641,10 @@ GemmPlan plan_skinny(int M, int N, int K, int out, int dh) {
       if (nk % s) continue;
       if (s > kMaxSplits || tg * s > kMaxPer) break;
       S = s;
-      if (groups * s >= ((out == SO_SWIGLU || out == SO_KV) ? kWgTargetPaired : kWgTarget)) break;
+      const int target = (out == SO_SWIGLU || out == SO_KV) ? kWgTargetPaired
+                         : out == SO_QKV                      ? kWgTargetQkv
+                                                              : kWgTarget;
+      if (groups * s >= target) break;
     }
   }
   p.splits = S;
