@@ -16,6 +16,7 @@ oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload qwen3-8b-bs1|qwen3-8b-bs32|qwen3-8b-long|wide-8layer|tiny-fp32]
+                       [--block-sweep 4,8,10,16]
 
 HBM traffic of the LM-head kernel (the "traffic" field) comes from rocprofv3
 counter runs summarised into profiles/lm_head_traffic_<workload>.json:
@@ -374,6 +375,38 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def block_sweep(s, gammas, steps, warmup):
+    """Draft cost against block size on one workload: each block size gets
+    its own seeded steps (planted accepted lengths within the block), the
+    same context, weights and shapes otherwise.  Proposals per block are
+    gamma - 1 (the anchor is given)."""
+    import dataclasses
+    rows = []
+    for gamma in gammas:
+        if not 2 <= gamma <= 16:
+            sys.exit(f"block size {gamma} outside 2..16")
+        sg = dataclasses.replace(s, block=gamma)
+        res, _ = run_gpu(sg, steps, warmup)
+        wl = res["wl"]
+        B = wl.B
+        timed = range(warmup, warmup + steps)
+        draft_bytes = float(np.mean([algorithmic_bytes(sg, wl.L_at[k], int(wl.n_new[k].sum()), B,
+                                                       gamma)["draft"] for k in timed]))
+        blocks_per_s = B * steps / res["elapsed"]
+        d_ms = res["draft_only_ms"]
+        rows.append({"block": gamma,
+                     "step_blocks_per_s": round(blocks_per_s, 2),
+                     "step_tokens_per_s": round(blocks_per_s * (gamma - 1), 1),
+                     "draft_ms": round(d_ms, 4),
+                     "draft_blocks_per_s": round(B * 1e3 / d_ms, 2),
+                     "draft_tokens_per_s": round(B * 1e3 / d_ms * (gamma - 1), 1),
+                     "draft_hbm_frac": round(draft_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "replay_accept_match": res["replay_ok"]})
+        log(f"block {gamma}: draft {d_ms:.4f} ms, step {blocks_per_s:.1f} blocks/s")
+    print(json.dumps({"block_sweep": rows, "workload": s.name, "batch": s.batch,
+                      "steps": steps, "warmup": warmup, "dtype": s.dtype}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +419,8 @@ def main():
                     help="only run the counter-calibration copy")
     ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarise rocprofv3 --pmc output directories into profiles/")
+    ap.add_argument("--block-sweep", default=None, metavar="G1,G2,...",
+                    help="time the step at each block size instead (one JSON line)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -403,6 +438,9 @@ def main():
     if args.workload not in by_name:
         sys.exit(f"unknown workload {args.workload}; one of {sorted(by_name)}")
     s = by_name[args.workload]
+    if args.block_sweep:
+        block_sweep(s, [int(g) for g in args.block_sweep.split(",")], args.steps, args.warmup)
+        return
 
     res, w_host = run_gpu(s, args.steps, args.warmup)
     wl = res["wl"]

@@ -6,7 +6,7 @@ token must be the oracle's argmax unless the oracle's top-2 gap there is
 below that tolerance.
 
 Covers: the five workloads (the batch-32, long-context and wide ones on
-sampled sequences), every GEMM path (1, 2, 4 row tiles and the tiled kernel,
+sampled sequences), block sizes 4, 8 and 10 at the batch-1 Qwen3-8B shape, every GEMM path (1, 2, 4 row tiles and the tiled kernel,
 packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
 one, determinism, batch invariance, other streams, and the device error
@@ -22,6 +22,16 @@ pytestmark = pytest.mark.gpu
 
 MINI = Shape("mini-bf16", 512, 2, 4, 2, 128, 768, 1000, 16, 1, True, seed=991)
 MINI_F32 = Shape("mini-f32", 256, 2, 4, 2, 64, 768, 1001, 5, 1, False, seed=992)
+
+
+_C2_WEIGHTS = []
+
+
+def _c2_weights():
+    # generated once per session: the Qwen3-8B-shaped weights take seconds
+    if not _C2_WEIGHTS:
+        _C2_WEIGHTS.append(make_weights(CONFIGS[2]))
+    return _C2_WEIGHTS[0]
 
 
 def pages_for(L_max, extra=2):
@@ -91,7 +101,14 @@ def test_draft_tiny_fp32_workload():
 
 def test_draft_qwen3_8b_batch1_workload():
     s = CONFIGS[2]
-    run_case(s, context_lengths(s), s.block)
+    run_case(s, context_lengths(s), s.block, weights=_c2_weights())
+
+
+@pytest.mark.parametrize("gamma", [4, 8, 10])
+def test_draft_qwen3_8b_batch1_block_sizes(gamma):
+    # the block-size sweep's shapes: fewer mask positions, same weights
+    s = CONFIGS[2]
+    run_case(s, context_lengths(s), gamma, weights=_c2_weights())
 
 
 def test_draft_qwen3_8b_batch32_workload_sampled():
