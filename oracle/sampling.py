@@ -17,7 +17,9 @@ Readings where the page leaves a step open (listed in the design doc):
     the row that predicts position k (as in the greedy rule).
   * "Kept with probability a" means kept iff u_k < a for an input uniform u_k
     in [0, 1); the comparison is made as u_k * p^d < p^t.
-  * The residual distribution is max(0, p^t - p^d), normalised.
+  * The residual distribution is max(0, p^t - p^d), normalised.  When it has
+    no mass (the two rows agree and the proposal has probability zero under
+    both, so the check could not keep it), the correction is drawn from p^t.
   * A draw from a discrete distribution r with uniform u is the smallest
     token v whose cumulative mass exceeds u * sum(r).
   * The drafter draws x_k by Gumbel-max: x_k = argmax_v (logit_k(v) + g),
@@ -61,16 +63,18 @@ def draw_counter(seq: int, pos: int, tok: np.ndarray) -> np.ndarray:
             | np.asarray(tok, dtype=np.uint64)) + np.uint64(1)
 
 
-def uniform24(seed: int, n: np.ndarray) -> np.ndarray:
-    """Uniforms in (0, 1) from the top 24 bits of the SplitMix64 outputs:
-    (bits + 1/2) / 2^24, exact in fp32 and fp64."""
-    bits = _splitmix64_vec(seed, n) >> np.uint64(40)
-    return (bits.astype(np.float64) + 0.5) / float(1 << 24)
+def uniform23(seed: int, n: np.ndarray) -> np.ndarray:
+    """Uniforms in (0, 1) from the top 23 bits of the SplitMix64 outputs:
+    (bits + 1/2) / 2^23.  The numerator 2 * bits + 1 has at most 24
+    significant bits, so every value is exact in fp32 as well as in fp64 and
+    the largest one stays below 1."""
+    bits = _splitmix64_vec(seed, n) >> np.uint64(41)
+    return (bits.astype(np.float64) + 0.5) / float(1 << 23)
 
 
 def gumbel(seed: int, seq: int, pos: int, vocab: int) -> np.ndarray:
     """Gumbel noise -log(-log(w)) for every token of one block position."""
-    w = uniform24(seed, draw_counter(seq, pos, np.arange(vocab, dtype=np.uint64)))
+    w = uniform23(seed, draw_counter(seq, pos, np.arange(vocab, dtype=np.uint64)))
     return -np.log(-np.log(w))
 
 
@@ -119,7 +123,7 @@ def verify_stochastic(block, draft_logits, target_logits, uniforms):
             out[k - 1] = x
             continue
         resid = np.maximum(pt[k - 1] - pd[k], 0.0)
-        out[k - 1] = draw(resid, float(uniforms[0]))
+        out[k - 1] = draw(resid if resid.sum() > 0.0 else pt[k - 1], float(uniforms[0]))
         return k, out, k - 1
     out[gamma - 1] = draw(pt[gamma - 1], float(uniforms[0]))
     return gamma, out, gamma - 1

@@ -20,12 +20,21 @@ def test_splitmix64_reference_outputs():
         6457827717110365317, 3203168211198807973, 9817491932198370423]
 
 
-def test_uniform24_and_vector_generator_agree_with_scalar():
+def test_uniform23_and_vector_generator_agree_with_scalar():
     n = np.array([1, 2, 3, 1 << 40, (5 << 40) | (3 << 32) | 77], dtype=np.uint64)
-    u = S.uniform24(99, n)
+    u = S.uniform23(99, n)
     for i, c in enumerate(n):
-        assert u[i] == ((S.splitmix64(99, int(c)) >> 40) + 0.5) / 2 ** 24
+        assert u[i] == ((S.splitmix64(99, int(c)) >> 41) + 0.5) / 2 ** 23
     assert np.all((u > 0) & (u < 1))
+
+
+def test_uniforms_are_exact_in_fp32_and_below_one():
+    # the extreme numerators of (bits + 1/2) / 2^23 survive a cast to fp32
+    for bits in (0, 1, (1 << 22) + 1, (1 << 23) - 2, (1 << 23) - 1):
+        u = (bits + 0.5) / 2 ** 23
+        assert float(np.float32(u)) == u and np.float32(u) < np.float32(1.0)
+    u = S.uniform23(7, np.arange(1, 20001, dtype=np.uint64))
+    assert np.array_equal(u.astype(np.float32).astype(np.float64), u)
 
 
 def _chi2_pvalue(counts, probs):
@@ -138,6 +147,22 @@ def test_proposal_the_target_excludes_is_always_rejected():
         tg[0, block[1]] = -2000.0                    # p_t(x_1) = 0
         tau, out, acc = S.verify_stochastic(block, draft, tg, rng.random(gamma))
         assert tau == 1 and acc == 0 and out[0] != block[1]
+
+
+def test_rejection_with_an_empty_residual_draws_from_the_target():
+    # equal rows and a proposal both give probability zero: the check
+    # rejects it and the residual has no mass, so the target row decides
+    rng = np.random.default_rng(17)
+    gamma, V = 3, 6
+    target = _random_logits(rng, gamma, V)
+    target[0, 4] = -2000.0
+    draft = np.vstack([target[:1], target[:-1]])
+    block = np.array([1, 4, 2], dtype=np.int32)
+    for u0 in (0.05, 0.5, 0.95):
+        u = np.array([u0, 0.3, 0.3])
+        tau, out, acc = S.verify_stochastic(block, draft, target, u)
+        assert tau == 1 and acc == 0
+        assert out[0] == S.draw(S.softmax(target[0]), u0) and out[0] != 4
 
 
 def test_residual_draw_uses_only_the_positive_part():
