@@ -17,7 +17,8 @@ from . import _abi
 from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_XCD, DFLASH_BF16, DFLASH_F32,
                    MAX_BLOCK, MAX_LAYERS, STATE_BYTES)
 
-__all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy", "load_library",
+__all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy",
+           "verify_stochastic", "verify_stochastic_workspace_bytes", "load_library",
            "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "DEVERR_XCD", "MAX_BLOCK", "MAX_LAYERS"]
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
@@ -183,6 +184,20 @@ class Drafter:
             _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)))
 
+    def draft_sampled(self, kv: KVCache, anchor, block_size, seed, block_tokens, logits,
+                      workspace, stream=None):
+        """dflash_draft_block_sampled: proposals drawn by Gumbel-max from the
+        drafter's logits with the counter stream of `seed` (logits required)."""
+        import torch
+        if logits is None:
+            raise ValueError("draft_sampled: logits are required")
+        _check(self.lib.dflash_draft_block_sampled(
+            self.handle, ctypes.byref(kv.c), _dev_ptr(anchor, "anchor", torch.int32),
+            int(anchor.numel()), int(block_size), int(seed) & ((1 << 64) - 1),
+            _dev_ptr(block_tokens, "block_tokens", torch.int32),
+            _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32(0)
         rc = self.lib.dflash_device_error(self.handle, _stream(stream), ctypes.byref(code))
@@ -219,4 +234,35 @@ def verify_greedy(block_tokens, target_logits, accept_len, out_tokens, workspace
         dt, int(B), int(gamma), int(target_logits.shape[-1]),
         _dev_ptr(accept_len, "accept_len", torch.int32), _dev_ptr(out_tokens, "out_tokens", torch.int32),
         _dev_ptr(target_argmax, "target_argmax", torch.int32), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def verify_stochastic_workspace_bytes(batch, block_size, vocab) -> int:
+    n = _abi.load().dflash_verify_stochastic_workspace_bytes(int(batch), int(block_size), int(vocab))
+    if n == 0:
+        raise DFlashError(-1, "verify_stochastic_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def verify_stochastic(block_tokens, draft_logits, target_logits, uniforms, accept_len, out_tokens,
+                      workspace, stream=None):
+    """Lossless verification through dflash_verify_stochastic.  block_tokens
+    int32 [B][gamma]; draft_logits fp32 and target_logits bf16 or fp32
+    [B][gamma][V]; uniforms fp32 [B][gamma]."""
+    import torch
+    lib = _abi.load()
+    if target_logits.dtype == torch.bfloat16:
+        dt = DFLASH_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = DFLASH_F32
+    else:
+        raise ValueError("target_logits must be bf16 or fp32")
+    B, gamma = block_tokens.shape
+    _check(lib.dflash_verify_stochastic(
+        _dev_ptr(block_tokens, "block_tokens", torch.int32),
+        _dev_ptr(draft_logits, "draft_logits", torch.float32),
+        _dev_ptr(target_logits, "target_logits"), dt,
+        _dev_ptr(uniforms, "uniforms", torch.float32), int(B), int(gamma),
+        int(target_logits.shape[-1]), _dev_ptr(accept_len, "accept_len", torch.int32),
+        _dev_ptr(out_tokens, "out_tokens", torch.int32), _dev_ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -19,6 +19,8 @@ STATE_BYTES = 16384
 EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_bytes",
             "dflash_packed_weight_bytes", "dflash_pack_weights",
             "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",
+            "dflash_draft_block_sampled", "dflash_verify_stochastic_workspace_bytes",
+            "dflash_verify_stochastic",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
             "dflash_profile_read"]
 
@@ -80,6 +82,14 @@ def load(path: str = LIB_PATH):
     lib.dflash_draft_block.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_verify_greedy.restype = ctypes.c_int
+    lib.dflash_draft_block_sampled.argtypes = [vp, P(KV), vp, i32, i32, ctypes.c_uint64, vp, vp,
+                                               vp, sz, vp]
+    lib.dflash_draft_block_sampled.restype = ctypes.c_int
+    lib.dflash_verify_stochastic_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.dflash_verify_stochastic_workspace_bytes.restype = sz
+    lib.dflash_verify_stochastic.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp, sz,
+                                             vp]
+    lib.dflash_verify_stochastic.restype = ctypes.c_int
     lib.dflash_last_error.argtypes = []
     lib.dflash_last_error.restype = ctypes.c_char_p
     lib.dflash_device_error.argtypes = [vp, vp, P(i32)]

@@ -94,6 +94,28 @@ DF_DEV uint64_t argmax_key(float v, uint32_t idx) {
 }
 DF_DEV uint32_t argmax_key_index(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu); }
 
+// n-th output (n >= 1) of the SplitMix64 generator started at seed (Steele,
+// Lea and Flood, "Fast splittable pseudorandom number generators", 2014):
+// the state advances by the golden-ratio constant and goes through the
+// generator's finaliser.
+DF_DEV uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Gumbel noise -log(-log(w)) of the drafter's draw at (sequence, block
+// position, token): w = (top 23 bits of output n + 1/2) / 2^23 with counter
+// n = (seq << 40 | pos << 32 | token) + 1.  2 * bits + 1 < 2^24, so w is
+// exact in fp32 and never reaches 1.
+DF_DEV float gumbel_noise(uint64_t seed, uint32_t seq, uint32_t pos, uint32_t tok) {
+  const uint64_t n = (((uint64_t)seq << 40) | ((uint64_t)pos << 32) | tok) + 1ull;
+  const uint32_t bits = (uint32_t)(splitmix64_at(seed, n) >> 41);
+  const float w = (float)(2u * bits + 1u) * (1.0f / 16777216.0f);
+  return -logf(-logf(w));
+}
+
 DF_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
   lo = __shfl_xor(lo, m, 64);

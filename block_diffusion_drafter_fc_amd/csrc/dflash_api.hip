@@ -509,9 +509,10 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   return DFLASH_OK;
 }
 
-int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_t* anchor,
-                       int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
-                       void* workspace, size_t ws_bytes, void* stream) {
+// One draft pass; dr.on turns the LM head's argmax into a Gumbel-max draw.
+static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t* anchor,
+                      int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
+                      void* workspace, size_t ws_bytes, void* stream, const DrawArgs& dr) {
   dflash_model* m = const_cast<dflash_model*>(mc);
   if (!m || !kv || !anchor || !block_tokens || !workspace)
     return fail(DFLASH_E_INVAL, "draft_block: null argument");
@@ -696,6 +697,7 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
     a.anchor = anchor;
     a.block_tokens = block_tokens;
     a.logits = logits;
+    a.draw = dr;
     if ((rc = prof_begin()) != DFLASH_OK) return rc;
     HIPCHK(launch_skinny(plan_skinny(M, d.V, d.D, SO_ARGMAX, d.dh), SA_NORM, SO_ARGMAX, a, st));
     if ((rc = prof_end()) != DFLASH_OK) return rc;
@@ -753,10 +755,32 @@ int dflash_draft_block(const dflash_model* mc, const dflash_kv* kv, const int32_
 
   const GemmPlan p = plan_gemm(bf, M, d.V, d.D, true);
   if ((rc = prof_begin()) != DFLASH_OK) return rc;
-  HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st));
+  HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st,
+                     dr));
   if ((rc = prof_end()) != DFLASH_OK) return rc;
   HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
   return DFLASH_OK;
+}
+
+int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                       int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  return draft_impl(m, kv, anchor, batch, gamma, block_tokens, logits, workspace, ws_bytes,
+                    stream, DrawArgs{});
+}
+
+int dflash_draft_block_sampled(const dflash_model* m, const dflash_kv* kv,
+                               const int32_t* anchor, int32_t batch, int32_t gamma,
+                               uint64_t seed, int32_t* block_tokens, float* logits,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  if (!logits)
+    return fail(DFLASH_E_INVAL, "draft_block_sampled: the drafter logits are required");
+  DrawArgs dr{};
+  dr.on = 1;
+  dr.gamma = gamma;
+  dr.seed = seed;
+  return draft_impl(m, kv, anchor, batch, gamma, block_tokens, logits, workspace, ws_bytes,
+                    stream, dr);
 }
 
 int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
@@ -776,6 +800,39 @@ int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
   HIPCHK(launch_verify(logits_dtype == DFLASH_BF16, block_tokens, target_logits, batch, gamma,
                        vocab, (uint64_t*)workspace, accept_len, out_tokens, target_argmax,
                        (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+size_t dflash_verify_stochastic_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab) {
+  if (batch < 1 || gamma < 1 || vocab < 1) return 0;
+  return verify_sampled_ws_bytes(batch, gamma, vocab);
+}
+
+int dflash_verify_stochastic(const int32_t* block_tokens, const float* draft_logits,
+                             const void* target_logits, int32_t logits_dtype,
+                             const float* uniforms, int32_t batch, int32_t gamma, int32_t vocab,
+                             int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (!block_tokens || !draft_logits || !target_logits || !uniforms || !accept_len ||
+      !out_tokens || !workspace)
+    return fail(DFLASH_E_INVAL, "verify_stochastic: null argument");
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
+    return fail(DFLASH_E_DTYPE, "verify_stochastic: unknown logits dtype %d", logits_dtype);
+  if (batch < 1 || gamma < 1 || vocab < 1)
+    return fail(DFLASH_E_INVAL, "verify_stochastic: batch, block_size and vocab must be >= 1");
+  if (gamma > kMaxVerifyBlock || (int64_t)batch * gamma > 65535)
+    return fail(DFLASH_E_CAPACITY,
+                "verify_stochastic: block_size %d > %d or batch * block_size > 65535", gamma,
+                kMaxVerifyBlock);
+  if (((uintptr_t)workspace & 15) != 0)
+    return fail(DFLASH_E_INVAL, "verify_stochastic: workspace must be 16-byte aligned");
+  const size_t need = verify_sampled_ws_bytes(batch, gamma, vocab);
+  if (ws_bytes < need)
+    return fail(DFLASH_E_CAPACITY, "verify_stochastic: workspace %zu bytes < %zu needed",
+                ws_bytes, need);
+  HIPCHK(launch_verify_sampled(logits_dtype == DFLASH_BF16, block_tokens, target_logits,
+                               draft_logits, uniforms, batch, gamma, vocab, workspace,
+                               accept_len, out_tokens, (hipStream_t)stream));
   return DFLASH_OK;
 }
 

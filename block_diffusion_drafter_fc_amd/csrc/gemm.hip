@@ -60,7 +60,7 @@ template <int MT, int NT, int U, bool SPLIT, bool ARGMAX>
 __global__ __launch_bounds__(256) void k_gemm_skinny(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, DrawArgs dr) {
   constexpr int KC = 32 * U, NP = SPLIT ? 2 : 1, ROWS = 16 * MT;
   constexpr int CPR = KC / 8;              // 16-byte chunks per activation row
   constexpr int NCH = ROWS * CPR / 256;    // chunks per thread per plane
@@ -201,7 +201,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(
         const int col = n0 + t * 16 + lr;
         if (active && col < N) {
           const float v = acc[m][t][i];
-          const uint64_t k2 = argmax_key(v, (uint32_t)col);
+          const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
+                                                               (uint32_t)(row % dr.gamma), (uint32_t)col)
+                                            : v;
+          const uint64_t k2 = argmax_key(kv, (uint32_t)col);
           key = k2 > key ? k2 : key;
           if (logits != nullptr && row < M) logits[(size_t)row * N + col] = v;
         }
@@ -226,7 +229,7 @@ template <bool SPLIT, int TBK, bool ARGMAX>
 __global__ __launch_bounds__(256) void k_gemm_tiled(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, DrawArgs dr) {
   constexpr int NP = SPLIT ? 2 : 1;               // A planes
   constexpr int CPR = TBK / 8;                    // 16-byte chunks per tile row
   constexpr int NCH = TBM * CPR / 256;            // chunks per thread per operand
@@ -350,7 +353,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
         const int col = n0 + wn * 64 + b * 16 + lr;
         if (col < N) {
           const float v = acc[a][b][i];
-          const uint64_t k2 = argmax_key(v, (uint32_t)col);
+          const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
+                                                               (uint32_t)(row % dr.gamma), (uint32_t)col)
+                                            : v;
+          const uint64_t k2 = argmax_key(kv, (uint32_t)col);
           key = k2 > key ? k2 : key;
           if (logits != nullptr && row < M) logits[(size_t)row * N + col] = v;
         }
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, int lda, int M,
                                                  WSeg w, int N, int K, float* __restrict__ part,
                                                  uint64_t* __restrict__ best,
-                                                 float* __restrict__ logits) {
+                                                 float* __restrict__ logits, DrawArgs dr) {
   const int n = blockIdx.x * 64 + threadIdx.x, m = blockIdx.y;
   float acc = 0.f;
   if (n < N) {
@@ -381,7 +387,10 @@ __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, in
     if (n < N) part[(size_t)m * N + n] = acc;
     return;
   }
-  uint64_t key = n < N ? argmax_key(acc, (uint32_t)n) : 0;
+  const float kv = dr.on ? acc + gumbel_noise(dr.seed, (uint32_t)(m / dr.gamma), (uint32_t)(m % dr.gamma),
+                                              (uint32_t)n)
+                        : acc;
+  uint64_t key = n < N ? argmax_key(kv, (uint32_t)n) : 0;
   if (n < N && logits != nullptr) logits[(size_t)m * N + n] = acc;
   for (int s = 1; s < 64; s <<= 1) {
     uint64_t o = shfl_xor_u64(key, s);
@@ -393,23 +402,23 @@ __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, in
 template <int MT, int NT, int U>
 hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda, int M,
                       const WSeg& w, int N, int K, float* part, uint64_t* best, float* logits,
-                      hipStream_t st) {
+                      hipStream_t st, const DrawArgs& dr) {
   dim3 grid((N + 64 * NT - 1) / (64 * NT), p.splits);
   dim3 block(256);
   const uint16_t* a = (const uint16_t*)A;
   const uint16_t* al = (const uint16_t*)Alo;
   if (al && best)
     hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true, true>), grid, block, 0, st, a, al, lda, M,
-                       w, N, K, p.kpw, part, best, logits);
+                       w, N, K, p.kpw, part, best, logits, dr);
   else if (al)
     hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, true, false>), grid, block, 0, st, a, al, lda, M,
-                       w, N, K, p.kpw, part, best, logits);
+                       w, N, K, p.kpw, part, best, logits, dr);
   else if (best)
     hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false, true>), grid, block, 0, st, a, al, lda,
-                       M, w, N, K, p.kpw, part, best, logits);
+                       M, w, N, K, p.kpw, part, best, logits, dr);
   else
     hipLaunchKernelGGL((k_gemm_skinny<MT, NT, U, false, false>), grid, block, 0, st, a, al, lda,
-                       M, w, N, K, p.kpw, part, best, logits);
+                       M, w, N, K, p.kpw, part, best, logits, dr);
   return hipGetLastError();
 }
 
@@ -472,12 +481,13 @@ int gemm_argmax_groups(const GemmPlan& p, int N) {
 
 hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
-                       float* logits, hipStream_t st) {
+                       float* logits, hipStream_t st, const DrawArgs& dr) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (dr.on && (best == nullptr || dr.gamma < 1)) return hipErrorInvalidValue;
   if (p.kind == GEMM_F32) {
     dim3 grid((N + 63) / 64, M);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, st, (const float*)A, lda, M, w, N, K, part,
-                       best, logits);
+                       best, logits, dr);
     return hipGetLastError();
   }
   (void)bf16;
@@ -487,20 +497,20 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
     const uint16_t* al = (const uint16_t*)Alo;
     if (al && best)
       hipLaunchKernelGGL((k_gemm_tiled<true, 32, true>), grid, dim3(256), 0, st, a, al, lda, M, w,
-                         N, K, p.kpw, part, best, logits);
+                         N, K, p.kpw, part, best, logits, dr);
     else if (al)
       hipLaunchKernelGGL((k_gemm_tiled<true, 32, false>), grid, dim3(256), 0, st, a, al, lda, M,
-                         w, N, K, p.kpw, part, best, logits);
+                         w, N, K, p.kpw, part, best, logits, dr);
     else if (best)
       hipLaunchKernelGGL((k_gemm_tiled<false, 64, true>), grid, dim3(256), 0, st, a, al, lda, M,
-                         w, N, K, p.kpw, part, best, logits);
+                         w, N, K, p.kpw, part, best, logits, dr);
     else
       hipLaunchKernelGGL((k_gemm_tiled<false, 64, false>), grid, dim3(256), 0, st, a, al, lda, M,
-                         w, N, K, p.kpw, part, best, logits);
+                         w, N, K, p.kpw, part, best, logits, dr);
     return hipGetLastError();
   }
 #define DF_SKINNY(MT, NT, U) \
-  if (p.mt == MT && p.nt == NT) return run_skinny<MT, NT, U>(p, A, Alo, lda, M, w, N, K, part, best, logits, st)
+  if (p.mt == MT && p.nt == NT) return run_skinny<MT, NT, U>(p, A, Alo, lda, M, w, N, K, part, best, logits, st, dr)
   DF_SKINNY(1, 1, 8);
   DF_SKINNY(2, 1, 4);
   DF_SKINNY(4, 1, 2);

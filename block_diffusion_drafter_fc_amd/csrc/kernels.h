@@ -16,6 +16,14 @@ struct WSeg {
 
 enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2 };
 
+// Sampled drafting: the LM head's row argmax becomes a Gumbel-max draw over
+// logit + gumbel_noise(seed, row / gamma, row % gamma, column).
+struct DrawArgs {
+  int on;
+  int gamma;
+  unsigned long long seed;
+};
+
 struct GemmPlan {
   int kind;
   int mt;      // skinny: 16-row tiles of M per wave (1, 2 or 4)
@@ -40,7 +48,7 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax);
 int gemm_argmax_groups(const GemmPlan& p, int N);
 hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
-                       float* logits, hipStream_t stream);
+                       float* logits, hipStream_t stream, const DrawArgs& draw = DrawArgs{});
 
 // ---- skinny product with fused epilogues (bf16 models, M <= 64) -----------
 // Activation source of the product.
@@ -90,6 +98,7 @@ struct SkinnyArgs {
   const int32_t* anchor;
   int32_t* block_tokens;
   float* logits;           // [M][N] or null
+  DrawArgs draw;           // SO_ARGMAX: draw instead of argmax (draw.gamma = gamma)
   // SO_QKV
   void* q;
   size_t q_plane;
@@ -197,3 +206,16 @@ hipError_t launch_verify(bool bf16, const int32_t* block_tokens, const void* tar
                          int gamma, int vocab, uint64_t* best, int32_t* accept_len,
                          int32_t* out_tokens, int32_t* target_argmax, hipStream_t stream);
 hipError_t launch_clear_word(uint32_t* word, hipStream_t stream);
+
+// ---- lossless verification of sampled blocks ------------------------------
+constexpr int kMaxVerifyBlock = 64;
+// Workspace of launch_verify_sampled: 16 * ceil(vocab / 4096) *
+// (2 * batch * gamma + 256 * batch) bytes, 16-byte aligned.
+size_t verify_sampled_ws_bytes(int batch, int gamma, int vocab);
+// draft [batch][gamma][vocab] fp32 (row 0 unused), target [batch][gamma][vocab]
+// (bf16 or fp32), uniforms [batch][gamma]; writes accept_len [batch] and
+// out_tokens [batch][gamma] (-1 past the accepted length).
+hipError_t launch_verify_sampled(bool bf16, const int32_t* block_tokens, const void* target,
+                                 const float* draft, const float* uniforms, int batch, int gamma,
+                                 int vocab, void* workspace, int32_t* accept_len,
+                                 int32_t* out_tokens, hipStream_t stream);

@@ -459,7 +459,10 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
         uint64_t key = 0;
         if (active && col < N) {
           const float v = acc[m][i];
-          key = argmax_key(v, (uint32_t)col);
+          const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
+                                                        (uint32_t)(row % a.gamma), (uint32_t)col)
+                                     : v;
+          key = argmax_key(kv, (uint32_t)col);
           if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
         }
         key = max16(key);

@@ -228,6 +228,55 @@ int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* target_argmax,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* Sampled block draft: dflash_draft_block with each proposal drawn from
+ * the drafter's distribution instead of taken as its argmax (the lossless
+ * rule of the summary page's section "The Target Verifier Remains the
+ * Correctness Anchor" checks proposals drawn from p_d).  The draw is
+ * Gumbel-max at temperature 1:
+ *   d_j = lowest-index argmax over v of logits[b][j][v] + g(seed, b, j, v),
+ *   g = -log(-log(w)), w = (2 * (z >> 41) + 1) / 2^24, z the n-th output of
+ *   SplitMix64 started at `seed` (Steele, Lea and Flood 2014) with
+ *   n = (b << 40 | j << 32 | v) + 1, evaluated in fp32.
+ * The noise depends only on (seed, b, j, v): pass a fresh seed per call.
+ *   logits [batch][gamma][V] fp32 out, required (the verifier needs p_d).
+ * Everything else as dflash_draft_block; DFLASH_E_INVAL for NULL logits. */
+int dflash_draft_block_sampled(const dflash_model* model, const dflash_kv* kv,
+                               const int32_t* anchor, int32_t batch, int32_t block_size,
+                               uint64_t seed, int32_t* block_tokens, float* logits,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Lossless (stochastic) verification of a sampled block (summary page,
+ * section "The Target Verifier Remains the Correctness Anchor": proposal
+ * x_k is kept with probability min(1, p_t(x_k) / p_d(x_k)); the first
+ * rejection is corrected from the residual distribution and the rest of
+ * the block dropped; a block kept whole earns a bonus token).
+ *   block_tokens  [batch][gamma]: [anchor, x_1, ..., x_{gamma-1}]
+ *   draft_logits  [batch][gamma][vocab] fp32: row k gives p_d of x_k (row 0
+ *                 is not read), as written by dflash_draft_block_sampled
+ *   target_logits [batch][gamma][vocab] in logits_dtype: row j gives p_t of
+ *                 the token after block[0..j]
+ *   uniforms      [batch][gamma] fp32 in [0, 1): uniforms[b][k] decides x_k,
+ *                 uniforms[b][0] draws the correction or the bonus token
+ * p_d and p_t are softmax rows at temperature 1, evaluated in fp64.  x_k
+ * (k = 1, 2, ...) is kept while u_k * p_d[k](x_k) < p_t[k-1](x_k); a token
+ * outside [0, vocab) is never kept.  At the first rejection k:
+ * accept_len = k and out_tokens = [x_1 .. x_{k-1}, r, -1 ...] with r drawn
+ * from max(0, p_t[k-1] - p_d[k]) (from p_t[k-1] when that has no mass);
+ * with no rejection accept_len = gamma and the last token is drawn from
+ * p_t[gamma-1].  A draw from weights w with uniform u is the smallest token
+ * v whose running sum of w exceeds u * sum(w).
+ *   workspace  device, 16-byte aligned, at least
+ *              dflash_verify_stochastic_workspace_bytes(batch, gamma, vocab)
+ *              = 16 * ceil(vocab / 4096) * (2 * batch * gamma + 256 * batch)
+ * Limits: gamma <= 64 and batch * gamma <= 65535 (DFLASH_E_CAPACITY).
+ * Inputs are read only; rows of NaN logits give unspecified tokens. */
+size_t dflash_verify_stochastic_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab);
+int dflash_verify_stochastic(const int32_t* block_tokens, const float* draft_logits,
+                             const void* target_logits, int32_t logits_dtype,
+                             const float* uniforms, int32_t batch, int32_t block_size,
+                             int32_t vocab, int32_t* accept_len, int32_t* out_tokens,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* dflash_last_error(void);
 

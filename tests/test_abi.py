@@ -89,3 +89,41 @@ def test_verify_rejects_bad_arguments(lib):
     assert call(args(V=0)) == -1
     assert call(args(wsb=2 * 16 * 8 - 1)) == -4
     assert b"workspace" in lib.dflash_last_error()
+
+
+def test_sampled_draft_requires_logits(lib):
+    kv = _abi.KV(FAKE.value, 1, 1, FAKE.value, FAKE.value)
+    assert lib.dflash_draft_block_sampled(FAKE, ctypes.byref(kv), FAKE, 1, 16, 7, FAKE, None,
+                                          FAKE, 1 << 30, None) == -1
+    assert b"logits" in lib.dflash_last_error()
+    assert lib.dflash_draft_block_sampled(None, ctypes.byref(kv), FAKE, 1, 16, 7, FAKE, FAKE,
+                                          FAKE, 1 << 30, None) == -1
+
+
+def test_stochastic_verify_workspace_formula(lib):
+    f = lib.dflash_verify_stochastic_workspace_bytes
+    assert f(1, 16, 151936) == 16 * 38 * (2 * 16 + 256)
+    assert f(32, 16, 151936) == 16 * 38 * (2 * 32 * 16 + 256 * 32)
+    assert f(3, 5, 4096) == 16 * 1 * (2 * 15 + 768) and f(3, 5, 4097) == 16 * 2 * (2 * 15 + 768)
+    assert f(0, 16, 100) == 0 and f(1, 0, 100) == 0 and f(1, 16, 0) == 0
+
+
+def test_stochastic_verify_rejects_bad_arguments(lib):
+    need = lib.dflash_verify_stochastic_workspace_bytes(2, 16, 100)
+    args = lambda **kw: dict(dict(block=FAKE, d=FAKE, tgt=FAKE, dt=_abi.DFLASH_BF16, u=FAKE, B=2,
+                                  g=16, V=100, acc=FAKE, out=FAKE, ws=FAKE, wsb=need), **kw)
+
+    def call(a):
+        return lib.dflash_verify_stochastic(a["block"], a["d"], a["tgt"], a["dt"], a["u"], a["B"],
+                                            a["g"], a["V"], a["acc"], a["out"], a["ws"], a["wsb"],
+                                            None)
+    for k in ("block", "d", "tgt", "u", "acc", "out", "ws"):
+        assert call(args(**{k: None})) == -1, k
+    assert call(args(dt=5)) == -3
+    assert call(args(B=0)) == -1 and call(args(g=0)) == -1 and call(args(V=0)) == -1
+    assert call(args(g=65)) == -4
+    assert call(args(B=4096)) == -4
+    assert call(args(ws=ctypes.c_void_p(0x1008))) == -1
+    assert b"aligned" in lib.dflash_last_error()
+    assert call(args(wsb=need - 1)) == -4
+    assert b"workspace" in lib.dflash_last_error()
