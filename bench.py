@@ -141,9 +141,14 @@ def to_dev(a, bf16):
     return t.to("cuda")
 
 
-def run_gpu(s, steps, warmup):
+def run_gpu(s, steps, warmup, sampled=False):
+    """Time `steps` whole steps.  sampled: the draft draws its proposals
+    (fresh seed per step, logits written) and the verification is the
+    lossless stochastic one with seeded uniforms."""
     import torch
-    from block_diffusion_drafter_fc_amd import (Drafter, DrafterConfig, KVCache, verify_greedy)
+    from block_diffusion_drafter_fc_amd import (Drafter, DrafterConfig, KVCache, verify_greedy,
+                                                verify_stochastic,
+                                                verify_stochastic_workspace_bytes)
     from synth import Gen
     from synth.configs import hidden_states, make_weights, page_pool
 
@@ -213,10 +218,30 @@ def run_gpu(s, steps, warmup):
         tgt.append(to_dev(t, s.bf16))
     log(f"inputs of {S} steps resident ({time.time() - t0:.1f}s)")
 
+    if sampled:
+        logits = torch.empty((B, gamma, s.vocab), dtype=torch.float32, device="cuda")
+        uni = [torch.from_numpy(g.uniform(f"bench.u.{k}", B * gamma).astype(np.float32)
+                                .reshape(B, gamma)).cuda() for k in range(S)]
+        vws = torch.empty(verify_stochastic_workspace_bytes(B, gamma, s.vocab), dtype=torch.uint8,
+                          device="cuda")
+        seed0 = 0x5EED_0000_0000_0000
+
+        def draft_call(k):
+            drafter.draft_sampled(kv, anc[k], gamma, seed0 + k, blk[k], logits, ws)
+
+        def verify_call(k):
+            verify_stochastic(blk[k], logits, tgt[k], uni[k], acc[k], out[k], vws)
+    else:
+        def draft_call(k):
+            drafter.draft(kv, anc[k], gamma, blk[k], ws)
+
+        def verify_call(k):
+            verify_greedy(blk[k], tgt[k], acc[k], out[k], ws)
+
     def step(k):
         drafter.inject(kv, hid[k], cus[k], ws)
-        drafter.draft(kv, anc[k], gamma, blk[k], ws)
-        verify_greedy(blk[k], tgt[k], acc[k], out[k], ws)
+        draft_call(k)
+        verify_call(k)
 
     ctx.copy_(L0_dev)
     for k in range(warmup):
@@ -243,12 +268,21 @@ def run_gpu(s, steps, warmup):
     torch.cuda.synchronize()
     td = time.perf_counter()
     for k in range(n_draft):
-        drafter.draft(kv, anc[k], gamma, blk[k], ws)
+        draft_call(k)
     torch.cuda.synchronize()
     draft_only_ms = (time.perf_counter() - td) * 1e3 / n_draft
+    # verification alone, on the last drafted block of each step
+    torch.cuda.synchronize()
+    tv = time.perf_counter()
+    for k in range(n_draft):
+        verify_call(k)
+    torch.cuda.synchronize()
+    verify_only_ms = (time.perf_counter() - tv) * 1e3 / n_draft
+    taus = np.stack([acc[k].cpu().numpy() for k in range(warmup, S)])
 
     res = dict(elapsed=elapsed, steps=steps, warmup=warmup, lm_ms=lm_ms, lm_count=lm_count,
                replay_ok=replay_ok, draft_only_ms=draft_only_ms, prefill_s=prefill_s,
+               verify_only_ms=verify_only_ms, mean_tau=float(taus.mean()),
                prefill_tokens=prefill_tokens, wl=wl)
     drafter.close()
     return res, w_host
@@ -407,6 +441,30 @@ def block_sweep(s, gammas, steps, warmup):
                       "steps": steps, "warmup": warmup, "dtype": s.dtype}), flush=True)
 
 
+def sampled_bench(s, steps, warmup):
+    """The step with sampled drafting and lossless verification, next to the
+    greedy step on the same inputs (one JSON line)."""
+    rows = {}
+    for mode in ("greedy", "sampled"):
+        res, _ = run_gpu(s, steps, warmup, sampled=mode == "sampled")
+        wl = res["wl"]
+        B, gamma = wl.B, wl.gamma
+        rows[mode] = {"step_ms": round(res["elapsed"] * 1e3 / steps, 4),
+                      "step_blocks_per_s": round(B * steps / res["elapsed"], 2),
+                      "draft_ms": round(res["draft_only_ms"], 4),
+                      "verify_ms": round(res["verify_only_ms"], 4),
+                      "mean_accept_len": round(res["mean_tau"], 3)}
+        log(f"{mode}: {rows[mode]}")
+    elem = 2 if s.bf16 else 4
+    v_bytes = B * gamma * s.vocab * elem + B * (gamma - 1) * s.vocab * 4
+    rows["sampled"]["verify_logit_bytes"] = v_bytes
+    rows["sampled"]["verify_hbm_frac"] = round(
+        v_bytes / (rows["sampled"]["verify_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    print(json.dumps({"sampled_vs_greedy": rows, "workload": s.name, "batch": s.batch,
+                      "block": s.block, "steps": steps, "warmup": warmup, "dtype": s.dtype}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,6 +477,8 @@ def main():
                     help="only run the counter-calibration copy")
     ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="summarise rocprofv3 --pmc output directories into profiles/")
+    ap.add_argument("--sampled", action="store_true",
+                    help="time the sampled-draft + lossless-verify step next to the greedy one")
     ap.add_argument("--block-sweep", default=None, metavar="G1,G2,...",
                     help="time the step at each block size instead (one JSON line)")
     args = ap.parse_args()
@@ -438,6 +498,9 @@ def main():
     if args.workload not in by_name:
         sys.exit(f"unknown workload {args.workload}; one of {sorted(by_name)}")
     s = by_name[args.workload]
+    if args.sampled:
+        sampled_bench(s, args.steps, args.warmup)
+        return
     if args.block_sweep:
         block_sweep(s, [int(g) for g in args.block_sweep.split(",")], args.steps, args.warmup)
         return

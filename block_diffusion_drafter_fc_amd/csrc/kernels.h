@@ -209,8 +209,8 @@ hipError_t launch_clear_word(uint32_t* word, hipStream_t stream);
 
 // ---- lossless verification of sampled blocks ------------------------------
 constexpr int kMaxVerifyBlock = 64;
-// Workspace of launch_verify_sampled: 16 * ceil(vocab / 4096) *
-// (2 * batch * gamma + 256 * batch) bytes, 16-byte aligned.
+// Workspace of launch_verify_sampled: 16 * (ceil(vocab / 4096) *
+// (4 * batch * gamma + 256 * batch) + batch) bytes, 16-byte aligned.
 size_t verify_sampled_ws_bytes(int batch, int gamma, int vocab);
 // draft [batch][gamma][vocab] fp32 (row 0 unused), target [batch][gamma][vocab]
 // (bf16 or fp32), uniforms [batch][gamma]; writes accept_len [batch] and

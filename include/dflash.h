@@ -257,7 +257,9 @@ int dflash_draft_block_sampled(const dflash_model* model, const dflash_kv* kv,
  *                 the token after block[0..j]
  *   uniforms      [batch][gamma] fp32 in [0, 1): uniforms[b][k] decides x_k,
  *                 uniforms[b][0] draws the correction or the bonus token
- * p_d and p_t are softmax rows at temperature 1, evaluated in fp64.  x_k
+ * p_d and p_t are softmax rows at temperature 1; every decision is the
+ * one their fp64 values give (fp32 normalisers decide where the margin is
+ * wide, fp64 ones everywhere else).  x_k
  * (k = 1, 2, ...) is kept while u_k * p_d[k](x_k) < p_t[k-1](x_k); a token
  * outside [0, vocab) is never kept.  At the first rejection k:
  * accept_len = k and out_tokens = [x_1 .. x_{k-1}, r, -1 ...] with r drawn
@@ -267,7 +269,8 @@ int dflash_draft_block_sampled(const dflash_model* model, const dflash_kv* kv,
  * v whose running sum of w exceeds u * sum(w).
  *   workspace  device, 16-byte aligned, at least
  *              dflash_verify_stochastic_workspace_bytes(batch, gamma, vocab)
- *              = 16 * ceil(vocab / 4096) * (2 * batch * gamma + 256 * batch)
+ *              = 16 * (ceil(vocab / 4096) * (4 * batch * gamma + 256 * batch)
+ *                + batch)
  * Limits: gamma <= 64 and batch * gamma <= 65535 (DFLASH_E_CAPACITY).
  * Inputs are read only; rows of NaN logits give unspecified tokens. */
 size_t dflash_verify_stochastic_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab);

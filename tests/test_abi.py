@@ -102,9 +102,10 @@ def test_sampled_draft_requires_logits(lib):
 
 def test_stochastic_verify_workspace_formula(lib):
     f = lib.dflash_verify_stochastic_workspace_bytes
-    assert f(1, 16, 151936) == 16 * 38 * (2 * 16 + 256)
-    assert f(32, 16, 151936) == 16 * 38 * (2 * 32 * 16 + 256 * 32)
-    assert f(3, 5, 4096) == 16 * 1 * (2 * 15 + 768) and f(3, 5, 4097) == 16 * 2 * (2 * 15 + 768)
+    assert f(1, 16, 151936) == 16 * (38 * (4 * 16 + 256) + 1)
+    assert f(32, 16, 151936) == 16 * (38 * (4 * 32 * 16 + 256 * 32) + 32)
+    assert f(3, 5, 4096) == 16 * (1 * (4 * 15 + 768) + 3)
+    assert f(3, 5, 4097) == 16 * (2 * (4 * 15 + 768) + 3)
     assert f(0, 16, 100) == 0 and f(1, 0, 100) == 0 and f(1, 16, 0) == 0
 
 

@@ -114,6 +114,8 @@ def compare_stochastic(blocks, draft, target, u, bf16, max_tolerated=1):
         if acc[b] == tau and np.array_equal(out[b], o):
             continue
         m = decision_margin(blocks[b], d64[b], t64[b], u64[b])
+        log(f"  seq {b}: gpu tau {acc[b]} {out[b].tolist()} vs oracle {tau} {o.tolist()}, "
+            f"margin {m:.3e}")
         assert m < 1e-10, f"seq {b}: gpu tau {acc[b]} {out[b]} vs oracle {tau} {o}, margin {m:.3e}"
         tolerated += 1
     assert tolerated <= max_tolerated
@@ -137,6 +139,31 @@ def test_stochastic_verify_matches_oracle(B, gamma, V, bf16):
     log(f"  accepted lengths {np.bincount(taus, minlength=gamma + 1)[1:].tolist()}")
     if gamma > 1 and B >= 4:
         assert len(set(taus.tolist())) > 1      # the inputs reach more than one outcome
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_stochastic_verify_decisions_near_the_boundary(bf16):
+    # uniforms planted a relative 1e-6 below or above p_t / p_d of one
+    # proposal per sequence: inside the margin where fp32 normalisers could
+    # decide wrongly, far outside fp64 rounding, so the outcome is fixed
+    B, gamma, V = 12, 8, 5000
+    blocks, draft, target, u = make_inputs(4321 + bf16, B, gamma, V, bf16)
+    pd = S.softmax(draft.astype(np.float64))
+    pt = S.softmax(host64(target, bf16))
+    planted = 0
+    for b in range(B):
+        for k in range(1, gamma):
+            x = blocks[b, k]
+            ratio = pt[b, k - 1, x] / pd[b, k, x]
+            if ratio < 0.9:
+                side = 1.0 - 1e-6 if b % 2 == 0 else 1.0 + 1e-6
+                u[b, 1:k] = 0.0                      # keep the proposals before it
+                u[b, k] = np.float32(ratio * side)
+                planted += 1
+                break
+    assert planted >= 8
+    taus, acc, out = compare_stochastic(blocks, draft, target, u, bf16, max_tolerated=0)
+    log(f"  near-boundary accepted lengths {acc.tolist()}")
 
 
 def test_stochastic_verify_out_of_range_proposals_are_rejected():
