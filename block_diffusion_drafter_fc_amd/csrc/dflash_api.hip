@@ -69,9 +69,16 @@ Dims dims_of(const dflash_config& c) {
   return d;
 }
 
+// Partial-slice floats of a plain product with at most M rows: the split
+// count depends on M (whole rounds of workgroups), so S * M * N is not
+// monotone in M; the workspace covers every row count up to M.
 size_t part_floats(bool bf16, int M, int N, int K) {
-  const GemmPlan p = plan_gemm(bf16, M, N, K, false);
-  return (size_t)p.splits * M * N;
+  size_t best = 0;
+  for (int m = M > 64 ? 65 : 1; m <= M; ++m) {
+    const GemmPlan p = plan_gemm(bf16, m, N, K, false);
+    best = std::max(best, (size_t)p.splits * m * N);
+  }
+  return best;
 }
 
 // State buffer: the error word; at 128 the workgroup -> XCD rotation the last

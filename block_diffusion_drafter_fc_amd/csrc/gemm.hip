@@ -372,6 +372,194 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 }
 
 // ----------------------------------------------------------------------------
+// Large product (M > 64): 128 x 256 output tiles, 4 waves of 64 x 128 (wide
+// in N, so that the two activation planes share every weight fragment read
+// from LDS), K in steps of 32 through a ring of 4 LDS stages.
+//
+// Loads go straight from global memory to LDS (global_load_lds_dwordx4: lane
+// l of a wave writes its 16 bytes at the instruction's LDS base + 16 l), so
+// no registers stage the tiles and three steps of loads stay in flight.  A
+// stage holds the tile rows back to back, 64 bytes each: the A planes' 128
+// rows each, then the 256 weight rows.  The four 16-byte chunks of row R sit
+// XOR-swizzled (chunk c at slot c ^ ((R >> 1) & 3)), so the 16 rows a
+// fragment read touches land in distinct banks; a load block of 16 rows
+// (1 KB, one wave instruction) fetches the chunks in swizzled order.
+constexpr int GBM = 128, GBN = 256, GBK = 32, GSTAGES = 4;
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* glb_void_t;
+
+template <bool SPLIT, bool ARGMAX>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
+    int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
+    float* __restrict__ logits, DrawArgs dr) {
+  constexpr int NP = SPLIT ? 2 : 1;
+  constexpr int RA = NP * GBM;                 // A rows per stage
+  constexpr int NR = RA + GBN;                 // rows per stage
+  constexpr int SB = NR * 64;                  // bytes per stage
+  constexpr int NL = NR / 16 / 4;              // load instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[GSTAGES * SB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Tile order: the dispatcher deals workgroup ids to the 8 XCDs round
+  // robin, so ids equal mod 8 share an XCD (whatever XCD the rotation starts
+  // at).  Within such a slot consecutive ids take the M tiles of one weight
+  // tile, which then streams from HBM once and from that XCD's L2 for the
+  // other M tiles.  Ids past the last weight tile (the N tiles are padded to
+  // a multiple of 8) exit at once.
+  const int mtiles = (M + GBM - 1) / GBM;
+  const int slot = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int ntile = (q / mtiles) * 8 + slot;
+  if (ntile * GBN >= N) return;
+  const int m0 = (q % mtiles) * GBM, n0 = ntile * GBN, split = blockIdx.z;
+  const int kbeg = split * kps;
+
+  // global source of each of this lane's loads (block wave + 4 j)
+  const uint16_t* gp[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int R = (wave + 4 * j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((R >> 1) & 3);
+    const uint16_t* row;
+    if (R < RA) {
+      const int pl = R / GBM;
+      const int r = min(m0 + (R % GBM), M - 1);
+      row = (pl ? Alo : A) + (size_t)r * lda;
+    } else {
+      row = seg_row_bf16(w, min(n0 + (R - RA), N - 1), K);
+    }
+    gp[j] = row + kbeg + c * 8;
+  }
+  auto issue = [&](int s) {
+    unsigned char* base = lds + (s % GSTAGES) * SB;
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t)(gp[j] + s * GBK),
+                                       (lds_void_t)(base + (wave + 4 * j) * 1024), 16, 0, 0);
+  };
+  auto frag = [&](const unsigned char* base, int R) -> u32x4 {
+    return *(const u32x4*)(base + R * 64 + ((lg ^ ((R >> 1) & 3)) << 4));
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragments of one step: B (8 x 16 weight rows) and A (4 x 16 rows per
+  // plane).  Those of step s + 1 are read while the MFMAs of step s run.
+  struct Frags {
+    u32x4 b[8], a[NP][4];
+  };
+  auto read_frags = [&](Frags& f, int s) {
+    const unsigned char* base = lds + (s % GSTAGES) * SB;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) f.b[b] = frag(base, RA + wn * 128 + b * 16 + lr);
+#pragma unroll
+    for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) f.a[pl][a] = frag(base, pl * GBM + wm * 64 + a * 16 + lr);
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_16x16x32(f.a[pl][a], f.b[b], acc[a][b]);
+  };
+  // Stage s is complete for the whole workgroup once every lane has waited
+  // for its own loads of step s (at most the later steps' loads, up to
+  // `later` steps of NL each, still outstanding) and the waves have met at a
+  // bare s_barrier (__syncthreads' fence would also wait for the later
+  // steps' loads).
+  auto stage_ready = [&](int later) {
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int steps = kps / GBK;
+  for (int s = 0; s < GSTAGES - 1 && s < steps; ++s) issue(s);
+  Frags f0, f1;
+  stage_ready(min(steps - 1, 2));
+  read_frags(f0, 0);
+  // Iteration s: stage s + 1 becomes ready, the stage that held step s - 1
+  // (whose fragments every wave has consumed) receives step s + 3, the
+  // fragments of step s + 1 are read, then step s's MFMAs run.  steps is
+  // even (launch_gemm checks), so each pass of the loop does two steps.
+  for (int s = 0; s < steps; s += 2) {
+    stage_ready(min(steps - 2 - s, 2));
+    if (s + GSTAGES - 1 < steps) issue(s + GSTAGES - 1);
+    read_frags(f1, s + 1);
+    mfmas(f0);
+    if (s + 2 < steps) {
+      stage_ready(min(steps - 3 - s, 2));
+      if (s + GSTAGES < steps) issue(s + GSTAGES);
+      read_frags(f0, s + 2);
+    }
+    mfmas(f1);
+  }
+
+  if (!ARGMAX) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * 64 + a * 16 + lg * 4 + i;
+        if (row >= M) continue;
+        float* dst = part + ((size_t)split * M + row) * N;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int col = n0 + wn * 128 + b * 16 + lr;
+          if (col < N) dst[col] = acc[a][b][i];
+        }
+      }
+    return;
+  }
+  // Row argmax over the tile's 256 columns: per wave (8 fragments, then the
+  // 16 lanes of a row), then over the two column halves in LDS.
+  __syncthreads();
+  uint64_t* hkeys = (uint64_t*)lds;   // [2][GBM], the stages are no longer read
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rloc = wm * 64 + a * 16 + lg * 4 + i;
+      const int row = m0 + rloc;
+      uint64_t key = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int col = n0 + wn * 128 + b * 16 + lr;
+        if (col < N) {
+          const float v = acc[a][b][i];
+          const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
+                                                               (uint32_t)(row % dr.gamma), (uint32_t)col)
+                                            : v;
+          const uint64_t k2 = argmax_key(kv, (uint32_t)col);
+          key = k2 > key ? k2 : key;
+          if (logits != nullptr && row < M) logits[(size_t)row * N + col] = v;
+        }
+      }
+      key = max16(key);
+      if (lr == 0) hkeys[wn * GBM + rloc] = key;
+    }
+  __syncthreads();
+  if (tid < GBM && m0 + tid < M) {
+    const uint64_t k0 = hkeys[tid], k1 = hkeys[GBM + tid];
+    best[(size_t)ntile * M + m0 + tid] = k0 > k1 ? k0 : k1;
+  }
+}
+
+// ----------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ A, int lda, int M,
                                                  WSeg w, int N, int K, float* __restrict__ part,
                                                  uint64_t* __restrict__ best,
@@ -422,6 +610,26 @@ hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda
   return hipGetLastError();
 }
 
+// K splits of the large product: one workgroup fits a CU (LDS), so the
+// grid should fill whole rounds of 256; among the divisors of the K steps
+// that keep >= 8 steps per split, the best round fill wins, the fewest
+// splits on near-ties (every split adds a partial slice to write and read).
+int big_splits(long tiles, int K) {
+  const int steps = K / GBK;
+  int best = 1;
+  double best_fill = 0.0;
+  for (int S = 1; S <= 16; ++S) {
+    if (steps % S || steps / S < 8 || (steps / S) % 2) continue;
+    const long wg = tiles * S;
+    const double fill = (double)wg / (256.0 * (double)((wg + 255) / 256));
+    if (fill > best_fill + 0.05) {
+      best_fill = fill;
+      best = S;
+    }
+  }
+  return best;
+}
+
 int largest_divisor_at_most(int n, int cap) {
   for (int d = cap < n ? cap : n; d >= 1; --d)
     if (n % d == 0) return d;
@@ -460,8 +668,17 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
     p.kpw = K / S;
     return p;
   }
-  p.kind = GEMM_TILED;
   p.waves = 4;
+  if (M >= 256 && K % (2 * GBK) == 0) {
+    // 128 x 256 tiles; below 256 rows the weight tile is reused too little
+    // for the larger tile to pay (measured), and the 128 x 128 kernel stays
+    p.kind = GEMM_BIG;
+    p.splits = 1;
+    if (!argmax) p.splits = big_splits((long)((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN), K);
+    p.kpw = K / p.splits;
+    return p;
+  }
+  p.kind = GEMM_TILED;
   const long tiles = (long)((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
   int splits = 1;
   if (!argmax && tiles < 512) {
@@ -476,6 +693,7 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
 int gemm_argmax_groups(const GemmPlan& p, int N) {
   if (p.kind == GEMM_F32) return (N + 63) / 64;
   if (p.kind == GEMM_TILED) return (N + TBN - 1) / TBN;
+  if (p.kind == GEMM_BIG) return (N + GBN - 1) / GBN;
   return (N + 64 * p.nt - 1) / (64 * p.nt);
 }
 
@@ -507,6 +725,26 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
     else
       hipLaunchKernelGGL((k_gemm_tiled<false, 64, false>), grid, dim3(256), 0, st, a, al, lda, M,
                          w, N, K, p.kpw, part, best, logits, dr);
+    return hipGetLastError();
+  }
+  if (p.kind == GEMM_BIG) {
+    if (p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K || lda % 8 != 0)
+      return hipErrorInvalidValue;
+    dim3 grid(((N + GBN - 1) / GBN + 7) / 8 * 8 * ((M + GBM - 1) / GBM), 1, p.splits);
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* al = (const uint16_t*)Alo;
+    if (al && best)
+      hipLaunchKernelGGL((k_gemm_big<true, true>), grid, dim3(256), 0, st, a, al, lda, M, w, N, K,
+                         p.kpw, part, best, logits, dr);
+    else if (al)
+      hipLaunchKernelGGL((k_gemm_big<true, false>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
+                         K, p.kpw, part, best, logits, dr);
+    else if (best)
+      hipLaunchKernelGGL((k_gemm_big<false, true>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
+                         K, p.kpw, part, best, logits, dr);
+    else
+      hipLaunchKernelGGL((k_gemm_big<false, false>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
+                         K, p.kpw, part, best, logits, dr);
     return hipGetLastError();
   }
 #define DF_SKINNY(MT, NT, U) \

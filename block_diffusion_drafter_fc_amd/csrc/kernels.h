@@ -14,7 +14,7 @@ struct WSeg {
   int32_t n;
 };
 
-enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2 };
+enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3 };
 
 // Sampled drafting: the LM head's row argmax becomes a Gumbel-max draw over
 // logit + gumbel_noise(seed, row / gamma, row % gamma, column).
