@@ -372,34 +372,43 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 }
 
 // ----------------------------------------------------------------------------
-// Large product (M > 64): 128 x 256 output tiles, 4 waves of 64 x 128 (wide
-// in N, so that the two activation planes share every weight fragment read
-// from LDS), K in steps of 32 through a ring of 4 LDS stages.
+// Large product (M >= 256): 64*WM x 256 output tiles, 2*WM waves of 64 x 128
+// (wide in N, so that the two activation planes share every weight fragment
+// read from LDS), K in steps of 32 through a ring of LDS stages.  WM = 2: 4
+// waves, one per SIMD, 4 stages, and each wave reads the next step's MFMA
+// fragments while the current step's MFMAs run.  WM = 4: 8 waves, two per
+// SIMD (each hides the other's LDS latency), 3 stages, and the weight tile is
+// shared by 256 rows instead of 128.
 //
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4: lane
 // l of a wave writes its 16 bytes at the instruction's LDS base + 16 l), so
-// no registers stage the tiles and three steps of loads stay in flight.  A
-// stage holds the tile rows back to back, 64 bytes each: the A planes' 128
-// rows each, then the 256 weight rows.  The four 16-byte chunks of row R sit
-// XOR-swizzled (chunk c at slot c ^ ((R >> 1) & 3)), so the 16 rows a
-// fragment read touches land in distinct banks; a load block of 16 rows
-// (1 KB, one wave instruction) fetches the chunks in swizzled order.
-constexpr int GBM = 128, GBN = 256, GBK = 32, GSTAGES = 4;
+// no registers stage the tiles and GSTAGES - 1 steps of loads stay in
+// flight.  A stage holds the tile rows back to back, 64 bytes each: the A
+// planes' 64*WM rows each, then the 256 weight rows.  The four 16-byte
+// chunks of row R sit XOR-swizzled (chunk c at slot c ^ ((R >> 1) & 3)), so
+// the 16 rows a fragment read touches land in distinct banks; a load block
+// of 16 rows (1 KB, one wave instruction) fetches the chunks in swizzled
+// order.
+constexpr int GBN = 256, GBK = 32;
+constexpr int big_stages(int wm) { return wm == 4 ? 3 : 4; }
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* glb_void_t;
 
-template <bool SPLIT, bool ARGMAX>
-__global__ __launch_bounds__(256, 1) void k_gemm_big(
+template <bool SPLIT, bool ARGMAX, int WM>
+__global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
     float* __restrict__ logits, DrawArgs dr) {
+  constexpr int BM = 64 * WM, NWAVE = 2 * WM, G = big_stages(WM);
+  constexpr bool DBUF = WM == 2;
   constexpr int NP = SPLIT ? 2 : 1;
-  constexpr int RA = NP * GBM;                 // A rows per stage
+  constexpr int RA = NP * BM;                  // A rows per stage
   constexpr int NR = RA + GBN;                 // rows per stage
   constexpr int SB = NR * 64;                  // bytes per stage
-  constexpr int NL = NR / 16 / 4;              // load instructions per wave per stage
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[GSTAGES * SB];
+  constexpr int NL = NR / 16 / NWAVE;          // load instructions per wave per stage
+  static_assert(NR % (16 * NWAVE) == 0, "stage rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[G * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
@@ -409,23 +418,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
   // tile, which then streams from HBM once and from that XCD's L2 for the
   // other M tiles.  Ids past the last weight tile (the N tiles are padded to
   // a multiple of 8) exit at once.
-  const int mtiles = (M + GBM - 1) / GBM;
+  const int mtiles = (M + BM - 1) / BM;
   const int slot = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int ntile = (q / mtiles) * 8 + slot;
   if (ntile * GBN >= N) return;
-  const int m0 = (q % mtiles) * GBM, n0 = ntile * GBN, split = blockIdx.z;
+  const int m0 = (q % mtiles) * BM, n0 = ntile * GBN, split = blockIdx.z;
   const int kbeg = split * kps;
 
-  // global source of each of this lane's loads (block wave + 4 j)
+  // global source of each of this lane's loads (block wave + NWAVE j)
   const uint16_t* gp[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    const int R = (wave + 4 * j) * 16 + (lane >> 2);
+    const int R = (wave + NWAVE * j) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((R >> 1) & 3);
     const uint16_t* row;
     if (R < RA) {
-      const int pl = R / GBM;
-      const int r = min(m0 + (R % GBM), M - 1);
+      const int pl = R / BM;
+      const int r = min(m0 + (R % BM), M - 1);
       row = (pl ? Alo : A) + (size_t)r * lda;
     } else {
       row = seg_row_bf16(w, min(n0 + (R - RA), N - 1), K);
@@ -433,11 +442,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
     gp[j] = row + kbeg + c * 8;
   }
   auto issue = [&](int s) {
-    unsigned char* base = lds + (s % GSTAGES) * SB;
+    unsigned char* base = lds + (s % G) * SB;
 #pragma unroll
     for (int j = 0; j < NL; ++j)
       __builtin_amdgcn_global_load_lds((glb_void_t)(gp[j] + s * GBK),
-                                       (lds_void_t)(base + (wave + 4 * j) * 1024), 16, 0, 0);
+                                       (lds_void_t)(base + (wave + NWAVE * j) * 1024), 16, 0, 0);
   };
   auto frag = [&](const unsigned char* base, int R) -> u32x4 {
     return *(const u32x4*)(base + R * 64 + ((lg ^ ((R >> 1) & 3)) << 4));
@@ -450,18 +459,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
     for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Fragments of one step: B (8 x 16 weight rows) and A (4 x 16 rows per
-  // plane).  Those of step s + 1 are read while the MFMAs of step s run.
+  // plane).
   struct Frags {
     u32x4 b[8], a[NP][4];
   };
   auto read_frags = [&](Frags& f, int s) {
-    const unsigned char* base = lds + (s % GSTAGES) * SB;
+    const unsigned char* base = lds + (s % G) * SB;
 #pragma unroll
     for (int b = 0; b < 8; ++b) f.b[b] = frag(base, RA + wn * 128 + b * 16 + lr);
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) f.a[pl][a] = frag(base, pl * GBM + wm * 64 + a * 16 + lr);
+      for (int a = 0; a < 4; ++a) f.a[pl][a] = frag(base, pl * BM + wm * 64 + a * 16 + lr);
   };
   auto mfmas = [&](const Frags& f) {
 #pragma unroll
@@ -471,11 +480,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = mfma_16x16x32(f.a[pl][a], f.b[b], acc[a][b]);
   };
-  // Stage s is complete for the whole workgroup once every lane has waited
-  // for its own loads of step s (at most the later steps' loads, up to
-  // `later` steps of NL each, still outstanding) and the waves have met at a
-  // bare s_barrier (__syncthreads' fence would also wait for the later
-  // steps' loads).
+  // Stage t is complete for the whole workgroup once every lane has waited
+  // for its own loads of step t (at most the later steps' loads, `later`
+  // steps of NL each, still outstanding) and the waves have met at a bare
+  // s_barrier (__syncthreads' fence would also wait for the later steps'
+  // loads).  Every wave's fragment reads of the stage that is refilled next
+  // have completed: their MFMAs consumed them.
   auto stage_ready = [&](int later) {
     if (later >= 2)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
@@ -488,25 +498,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
   };
 
   const int steps = kps / GBK;
-  for (int s = 0; s < GSTAGES - 1 && s < steps; ++s) issue(s);
-  Frags f0, f1;
-  stage_ready(min(steps - 1, 2));
-  read_frags(f0, 0);
-  // Iteration s: stage s + 1 becomes ready, the stage that held step s - 1
-  // (whose fragments every wave has consumed) receives step s + 3, the
-  // fragments of step s + 1 are read, then step s's MFMAs run.  steps is
-  // even (launch_gemm checks), so each pass of the loop does two steps.
-  for (int s = 0; s < steps; s += 2) {
-    stage_ready(min(steps - 2 - s, 2));
-    if (s + GSTAGES - 1 < steps) issue(s + GSTAGES - 1);
-    read_frags(f1, s + 1);
-    mfmas(f0);
-    if (s + 2 < steps) {
-      stage_ready(min(steps - 3 - s, 2));
-      if (s + GSTAGES < steps) issue(s + GSTAGES);
-      read_frags(f0, s + 2);
+  for (int s = 0; s < G - 1 && s < steps; ++s) issue(s);
+  if (DBUF) {
+    // Iteration s: stage s + 1 becomes ready, the stage that held step s - 1
+    // receives step s + G - 1, the fragments of step s + 1 are read, then
+    // step s's MFMAs run.  steps is even (launch_gemm checks), so each pass
+    // of the loop does two steps.
+    Frags f0, f1;
+    stage_ready(min(steps - 1, G - 2));
+    read_frags(f0, 0);
+    for (int s = 0; s < steps; s += 2) {
+      stage_ready(min(steps - 2 - s, G - 2));
+      if (s + G - 1 < steps) issue(s + G - 1);
+      read_frags(f1, s + 1);
+      mfmas(f0);
+      if (s + 2 < steps) {
+        stage_ready(min(steps - 3 - s, G - 2));
+        if (s + G < steps) issue(s + G);
+        read_frags(f0, s + 2);
+      }
+      mfmas(f1);
     }
-    mfmas(f1);
+  } else {
+    // Iteration s: stage s becomes ready, the stage that held step s - 1
+    // receives step s + G - 1, then step s's fragments and MFMAs.
+    Frags f;
+    for (int s = 0; s < steps; ++s) {
+      stage_ready(min(steps - 1 - s, G - 2));
+      if (s + G - 1 < steps) issue(s + G - 1);
+      read_frags(f, s);
+      mfmas(f);
+    }
   }
 
   if (!ARGMAX) {
@@ -528,7 +550,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
   // Row argmax over the tile's 256 columns: per wave (8 fragments, then the
   // 16 lanes of a row), then over the two column halves in LDS.
   __syncthreads();
-  uint64_t* hkeys = (uint64_t*)lds;   // [2][GBM], the stages are no longer read
+  uint64_t* hkeys = (uint64_t*)lds;   // [2][BM], the stages are no longer read
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -550,11 +572,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(
         }
       }
       key = max16(key);
-      if (lr == 0) hkeys[wn * GBM + rloc] = key;
+      if (lr == 0) hkeys[wn * BM + rloc] = key;
     }
   __syncthreads();
-  if (tid < GBM && m0 + tid < M) {
-    const uint64_t k0 = hkeys[tid], k1 = hkeys[GBM + tid];
+  if (tid < BM && m0 + tid < M) {
+    const uint64_t k0 = hkeys[tid], k1 = hkeys[BM + tid];
     best[(size_t)ntile * M + m0 + tid] = k0 > k1 ? k0 : k1;
   }
 }
@@ -610,21 +632,34 @@ hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda
   return hipGetLastError();
 }
 
-// K splits of the large product: one workgroup fits a CU (LDS), so the
-// grid should fill whole rounds of 256; among the divisors of the K steps
-// that keep >= 8 steps per split, the best round fill wins, the fewest
-// splits on near-ties (every split adds a partial slice to write and read).
-int big_splits(long tiles, int K) {
+// Tile height and K splits of the large product, from a cost model fitted
+// to measurements on the Qwen3-8B shapes: a round of up to 256 workgroups
+// (one per CU) costs steps/S * t_step plus ~11 us of fixed cost (filling the
+// stage ring, writing the tile, dispatch), with t_step ~1.1 us for the 4-wave
+// 128-row tile and ~1.8 us for the 8-wave 256-row tile (split activations);
+// each extra partial slice costs its write-back and the reducer's read
+// (2 * M * N * 4 bytes at ~5 TB/s).  Splits keep an even number of >= 4 steps.
+struct BigChoice {
+  int wm, splits;
+};
+
+BigChoice big_plan(int M, int N, int K, bool argmax) {
+  BigChoice best{2, 1};
+  double best_cost = 1e300;
   const int steps = K / GBK;
-  int best = 1;
-  double best_fill = 0.0;
-  for (int S = 1; S <= 16; ++S) {
-    if (steps % S || steps / S < 8 || (steps / S) % 2) continue;
-    const long wg = tiles * S;
-    const double fill = (double)wg / (256.0 * (double)((wg + 255) / 256));
-    if (fill > best_fill + 0.05) {
-      best_fill = fill;
-      best = S;
+  const long ntiles = (N + GBN - 1) / GBN;
+  for (int wm = 2; wm <= 4; wm += 2) {
+    const long tiles = (long)((M + 64 * wm - 1) / (64 * wm)) * ntiles;
+    const double t_step = wm == 4 ? 1.8 : 1.1;
+    for (int S = 1; S <= (argmax ? 1 : 16); ++S) {
+      if (steps % S || (steps / S) % 2 || steps / S < 4) continue;
+      const double rounds = (double)((tiles * S + 255) / 256);
+      const double cost = rounds * ((double)(steps / S) * t_step + 11.0) +
+                          (double)(S - 1) * M * (double)N * 8.0 / 5e6;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = BigChoice{wm, S};
+      }
     }
   }
   return best;
@@ -670,11 +705,13 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
   }
   p.waves = 4;
   if (M >= 256 && K % (2 * GBK) == 0) {
-    // 128 x 256 tiles; below 256 rows the weight tile is reused too little
-    // for the larger tile to pay (measured), and the 128 x 128 kernel stays
+    // 128 x 256 or 256 x 256 tiles; below 256 rows the weight tile is
+    // reused too little for these tiles to pay (measured), and the 128 x 128
+    // kernel stays
     p.kind = GEMM_BIG;
-    p.splits = 1;
-    if (!argmax) p.splits = big_splits((long)((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN), K);
+    const BigChoice c = big_plan(M, N, K, argmax);
+    p.mt = c.wm;
+    p.splits = c.splits;
     p.kpw = K / p.splits;
     return p;
   }
@@ -728,23 +765,28 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
     return hipGetLastError();
   }
   if (p.kind == GEMM_BIG) {
-    if (p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K || lda % 8 != 0)
+    if ((p.mt != 2 && p.mt != 4) || p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K ||
+        lda % 8 != 0)
       return hipErrorInvalidValue;
-    dim3 grid(((N + GBN - 1) / GBN + 7) / 8 * 8 * ((M + GBM - 1) / GBM), 1, p.splits);
+    const int bm = 64 * p.mt;
+    dim3 grid(((N + GBN - 1) / GBN + 7) / 8 * 8 * ((M + bm - 1) / bm), 1, p.splits);
     const uint16_t* a = (const uint16_t*)A;
     const uint16_t* al = (const uint16_t*)Alo;
-    if (al && best)
-      hipLaunchKernelGGL((k_gemm_big<true, true>), grid, dim3(256), 0, st, a, al, lda, M, w, N, K,
-                         p.kpw, part, best, logits, dr);
-    else if (al)
-      hipLaunchKernelGGL((k_gemm_big<true, false>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
-                         K, p.kpw, part, best, logits, dr);
-    else if (best)
-      hipLaunchKernelGGL((k_gemm_big<false, true>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
-                         K, p.kpw, part, best, logits, dr);
-    else
-      hipLaunchKernelGGL((k_gemm_big<false, false>), grid, dim3(256), 0, st, a, al, lda, M, w, N,
-                         K, p.kpw, part, best, logits, dr);
+#define DF_BIG(SPL, AM, WM)                                                                     \
+  hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM>), grid, dim3(128 * WM), 0, st, a, al, lda, M, w, N, \
+                     K, p.kpw, part, best, logits, dr)
+#define DF_BIG2(WM)                       \
+  if (al && best) DF_BIG(true, true, WM);  \
+  else if (al) DF_BIG(true, false, WM);    \
+  else if (best) DF_BIG(false, true, WM);  \
+  else DF_BIG(false, false, WM)
+    if (p.mt == 4) {
+      DF_BIG2(4);
+    } else {
+      DF_BIG2(2);
+    }
+#undef DF_BIG2
+#undef DF_BIG
     return hipGetLastError();
   }
 #define DF_SKINNY(MT, NT, U) \
