@@ -465,6 +465,81 @@ def sampled_bench(s, steps, warmup):
           flush=True)
 
 
+def packed_bench(s, n_blocks, steps, warmup):
+    """Packed multi-block forward with the weighted loss: n_blocks blocks of
+    one sequence (anchor positions spread over its context, seeded targets)
+    in one pass per step, after the context is injected (one JSON line)."""
+    import torch
+    from block_diffusion_drafter_fc_amd import Drafter, DrafterConfig, KVCache
+    from synth import Gen
+    from synth.configs import context_lengths, hidden_states, make_weights, page_pool
+    t0 = time.time()
+    w_host = make_weights(s)
+    wdev = {k: to_dev(v, s.bf16) for k, v in w_host.items()}
+    cfg = DrafterConfig(hidden=s.hidden, n_layers=s.n_layers, n_q_heads=s.n_q_heads,
+                        n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, intermediate=s.inter,
+                        vocab=s.vocab, n_target_feats=s.n_feats, max_block=16,
+                        mask_token_id=s.mask_id, dtype=s.dtype, rope_theta=s.rope_theta,
+                        rms_eps=s.eps)
+    drafter = Drafter(cfg, wdev)
+    L = int(context_lengths(s)[0])
+    gamma = s.block
+    pps = (L + 15) // 16 + 1
+    s1 = s.replace(batch=1)
+    n_pages, table = page_pool(s1, pps, extra=4, tag="bench.packed.pages")
+    dt = torch.bfloat16 if s.bf16 else torch.float32
+    pages = torch.zeros((s.n_layers, n_pages, 2, s.n_kv_heads, 16, s.head_dim), dtype=dt,
+                        device="cuda")
+    ctx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kv = KVCache(pages, torch.from_numpy(table[:1]).cuda(), ctx)
+    ws = torch.empty(max(drafter.workspace_bytes(1, gamma, 4096, pps),
+                         drafter.packed_workspace_bytes(n_blocks, gamma, pps)),
+                     dtype=torch.uint8, device="cuda")
+    for c0 in range(0, L, 4096):
+        n = min(4096, L - c0)
+        drafter.inject(kv, to_dev(hidden_states(s, 0, c0, n), s.bf16),
+                       torch.tensor([0, n], dtype=torch.int32, device="cuda"), ws)
+    torch.cuda.synchronize()
+    g = Gen(s.seed + 5)
+    S = warmup + steps
+    anc, pos, tgt = [], [], []
+    for k in range(S):
+        anc.append(torch.from_numpy(g.uniform_int(f"bench.pk.anchor.{k}", n_blocks, 0,
+                                                  s.vocab - 2).astype(np.int32)).cuda())
+        pos.append(torch.from_numpy(g.uniform_int(f"bench.pk.pos.{k}", n_blocks, 0,
+                                                  L).astype(np.int32)).cuda())
+        tgt.append(torch.from_numpy(g.uniform_int(f"bench.pk.tgt.{k}", n_blocks * gamma, 0,
+                                                  s.vocab - 1).astype(np.int32)
+                                    .reshape(n_blocks, gamma)).cuda())
+    logits = torch.empty((n_blocks, gamma, s.vocab), dtype=torch.float32, device="cuda")
+    bl = torch.empty(n_blocks, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    log(f"packed set-up ({time.time() - t0:.1f}s): {n_blocks} blocks of {gamma}, context {L}")
+
+    def step(k):
+        drafter.packed_forward(kv, anc[k], pos[k], gamma, logits, ws, targets=tgt[k], decay=7.0,
+                               block_loss=bl, loss=loss)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for k in range(warmup, S):
+        step(k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t
+    assert drafter.device_error() == 0
+    ms = el * 1e3 / steps
+    flops = draft_flops(s, np.asarray([p for p in pos[-1].cpu().numpy()]), n_blocks, gamma)
+    print(json.dumps({"packed_forward": {
+        "blocks": n_blocks, "block": gamma, "context": L, "ms_per_pass": round(ms, 4),
+        "blocks_per_s": round(n_blocks * 1e3 / ms, 2),
+        "tokens_per_s": round(n_blocks * (gamma - 1) * 1e3 / ms, 1),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "loss": float(loss.cpu().numpy()[0])},
+        "workload": s.name, "steps": steps, "warmup": warmup, "dtype": s.dtype}), flush=True)
+    drafter.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -479,6 +554,8 @@ def main():
                     help="summarise rocprofv3 --pmc output directories into profiles/")
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled-draft + lossless-verify step next to the greedy one")
+    ap.add_argument("--packed", type=int, default=0, metavar="N",
+                    help="time the packed forward + loss of N blocks of one sequence instead")
     ap.add_argument("--block-sweep", default=None, metavar="G1,G2,...",
                     help="time the step at each block size instead (one JSON line)")
     args = ap.parse_args()
@@ -498,6 +575,9 @@ def main():
     if args.workload not in by_name:
         sys.exit(f"unknown workload {args.workload}; one of {sorted(by_name)}")
     s = by_name[args.workload]
+    if args.packed:
+        packed_bench(s, args.packed, args.steps, args.warmup)
+        return
     if args.sampled:
         sampled_bench(s, args.steps, args.warmup)
         return

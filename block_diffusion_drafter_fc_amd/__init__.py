@@ -198,6 +198,29 @@ class Drafter:
             _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)))
 
+    def packed_workspace_bytes(self, max_blocks, max_block, max_pages_per_seq) -> int:
+        n = self.lib.dflash_packed_workspace_bytes(self.handle, max_blocks, max_block,
+                                                   max_pages_per_seq)
+        if n == 0:
+            raise DFlashError(-1, "packed_workspace_bytes: invalid arguments")
+        return int(n)
+
+    def packed_forward(self, ctx: KVCache, anchors, anchor_pos, block_size, logits, workspace,
+                       targets=None, decay=7.0, block_tokens=None, block_loss=None, loss=None,
+                       stream=None):
+        """dflash_packed_forward: the blocks of one sequence (ctx has batch 1)
+        in one pass, with the weighted cross-entropy when targets is given."""
+        import torch
+        _check(self.lib.dflash_packed_forward(
+            self.handle, ctypes.byref(ctx.c), _dev_ptr(anchors, "anchors", torch.int32),
+            _dev_ptr(anchor_pos, "anchor_pos", torch.int32), int(anchors.numel()),
+            int(block_size), _dev_ptr(targets, "targets", torch.int32), float(decay),
+            _dev_ptr(logits, "logits", torch.float32),
+            _dev_ptr(block_tokens, "block_tokens", torch.int32),
+            _dev_ptr(block_loss, "block_loss", torch.float32),
+            _dev_ptr(loss, "loss", torch.float32), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32(0)
         rc = self.lib.dflash_device_error(self.handle, _stream(stream), ctypes.byref(code))

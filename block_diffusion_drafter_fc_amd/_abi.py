@@ -20,7 +20,7 @@ EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_byt
             "dflash_packed_weight_bytes", "dflash_pack_weights",
             "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",
             "dflash_draft_block_sampled", "dflash_verify_stochastic_workspace_bytes",
-            "dflash_verify_stochastic",
+            "dflash_verify_stochastic", "dflash_packed_workspace_bytes", "dflash_packed_forward",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
             "dflash_profile_read"]
 
@@ -90,6 +90,11 @@ def load(path: str = LIB_PATH):
     lib.dflash_verify_stochastic.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp, sz,
                                              vp]
     lib.dflash_verify_stochastic.restype = ctypes.c_int
+    lib.dflash_packed_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    lib.dflash_packed_workspace_bytes.restype = sz
+    lib.dflash_packed_forward.argtypes = [vp, P(KV), vp, vp, i32, i32, vp, ctypes.c_float, vp, vp,
+                                          vp, vp, vp, sz, vp]
+    lib.dflash_packed_forward.restype = ctypes.c_int
     lib.dflash_last_error.argtypes = []
     lib.dflash_last_error.restype = ctypes.c_char_p
     lib.dflash_device_error.argtypes = [vp, vp, P(i32)]

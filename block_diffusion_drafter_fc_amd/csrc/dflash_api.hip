@@ -72,11 +72,18 @@ Dims dims_of(const dflash_config& c) {
 // Partial-slice floats of a plain product with at most M rows: the split
 // count depends on M (whole rounds of workgroups), so S * M * N is not
 // monotone in M; the workspace covers every row count up to M.
+// The split counts depend on M only through the 128-row tile counts, so
+// the maximum is reached at M itself, at 255 or at a multiple of 128.
 size_t part_floats(bool bf16, int M, int N, int K) {
   size_t best = 0;
-  for (int m = M > 64 ? 65 : 1; m <= M; ++m) {
+  auto at = [&](int m) {
     const GemmPlan p = plan_gemm(bf16, m, N, K, false);
     best = std::max(best, (size_t)p.splits * m * N);
+  };
+  at(M);
+  if (M > 64) {
+    if (M >= 255) at(255);
+    for (int m = 128; m < M; m += 128) at(m);
   }
   return best;
 }
@@ -807,6 +814,87 @@ int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
   HIPCHK(launch_verify(logits_dtype == DFLASH_BF16, block_tokens, target_logits, batch, gamma,
                        vocab, (uint64_t*)workspace, accept_len, out_tokens, target_argmax,
                        (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+// Packed forward workspace: the draft's own layout for n_blocks sequences,
+// then the broadcast page table, the per-block context lengths, the block
+// tokens and the cross-entropy scratch.
+struct PackedLayout {
+  size_t draft, table, lens, tokens, ce, total;
+};
+
+static PackedLayout packed_layout(const dflash_model* m, int n, int gamma, int max_pages) {
+  PackedLayout L{};
+  size_t off = align256(draft_layout(m, n, gamma, max_pages).total);
+  L.draft = off;
+  L.table = off;
+  off = align256(off + (size_t)n * max_pages * 4);
+  L.lens = off;
+  off = align256(off + (size_t)n * 4);
+  L.tokens = off;
+  off = align256(off + (size_t)n * gamma * 4);
+  L.ce = off;
+  off = align256(off + (size_t)n * (gamma > 1 ? gamma - 1 : 1) * 8);
+  L.total = off;
+  return L;
+}
+
+size_t dflash_packed_workspace_bytes(const dflash_model* m, int32_t max_blocks, int32_t max_block,
+                                     int32_t max_pages_per_seq) {
+  if (!m || max_blocks < 1 || max_block < 1 || max_block > m->cfg.max_block ||
+      max_pages_per_seq < 1)
+    return 0;
+  size_t need = 0;
+  for (int n = 1; n <= max_blocks; ++n)
+    for (int g = 1; g <= max_block; ++g)
+      need = std::max(need, packed_layout(m, n, g, max_pages_per_seq).total);
+  return need;
+}
+
+int dflash_packed_forward(const dflash_model* mc, const dflash_kv* ctx, const int32_t* anchors,
+                          const int32_t* anchor_pos, int32_t n_blocks, int32_t gamma,
+                          const int32_t* targets, float decay, float* logits,
+                          int32_t* block_tokens, float* block_loss, float* loss, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  dflash_model* m = const_cast<dflash_model*>(mc);
+  if (!m || !ctx || !anchors || !anchor_pos || !logits || !workspace)
+    return fail(DFLASH_E_INVAL, "packed_forward: null argument");
+  if (!ctx->pages || !ctx->page_table || !ctx->ctx_lens)
+    return fail(DFLASH_E_INVAL, "packed_forward: null pointer in the context description");
+  if (n_blocks < 1) return fail(DFLASH_E_INVAL, "packed_forward: n_blocks must be >= 1");
+  if (gamma < 1 || gamma > m->cfg.max_block)
+    return fail(DFLASH_E_CAPACITY, "packed_forward: block_size %d outside [1, %d]", gamma,
+                m->cfg.max_block);
+  if (targets && (gamma < 2 || !(decay > 0.f)))
+    return fail(DFLASH_E_INVAL, "packed_forward: the loss needs block_size >= 2 and decay > 0");
+  if (!targets && (block_loss || loss))
+    return fail(DFLASH_E_INVAL, "packed_forward: loss outputs without targets");
+  if (ctx->n_pages < 1 || ctx->max_pages_per_seq < 1)
+    return fail(DFLASH_E_INVAL, "packed_forward: empty page pool or page table");
+  const PackedLayout L = packed_layout(m, n_blocks, gamma, ctx->max_pages_per_seq);
+  if (L.total > ws_bytes)
+    return fail(DFLASH_E_CAPACITY, "packed_forward: workspace %zu bytes < %zu needed", ws_bytes,
+                L.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* table = (int32_t*)(ws + L.table);
+  int32_t* lens = (int32_t*)(ws + L.lens);
+  int32_t* toks = block_tokens ? block_tokens : (int32_t*)(ws + L.tokens);
+  HIPCHK(launch_packed_setup(ctx->page_table, ctx->max_pages_per_seq, ctx->ctx_lens, anchor_pos,
+                             n_blocks, table, lens, m->err, st));
+  dflash_kv kv{};
+  kv.pages = ctx->pages;
+  kv.n_pages = ctx->n_pages;
+  kv.max_pages_per_seq = ctx->max_pages_per_seq;
+  kv.page_table = table;
+  kv.ctx_lens = lens;
+  int rc = draft_impl(m, &kv, anchors, n_blocks, gamma, toks, logits, workspace, L.draft, stream,
+                      DrawArgs{});
+  if (rc != DFLASH_OK) return rc;
+  if (targets)
+    HIPCHK(launch_block_loss(logits, targets, n_blocks, gamma, m->cfg.vocab, (double)decay,
+                             (double*)(ws + L.ce), block_loss, loss, m->err, st));
   return DFLASH_OK;
 }
 

@@ -219,3 +219,16 @@ hipError_t launch_verify_sampled(bool bf16, const int32_t* block_tokens, const v
                                  const float* draft, const float* uniforms, int batch, int gamma,
                                  int vocab, void* workspace, int32_t* accept_len,
                                  int32_t* out_tokens, hipStream_t stream);
+
+// ---- packed multi-block forward -------------------------------------------
+// table[b][p] = page_row[p] for b < n_blocks; lens[b] = anchor_pos[b]
+// (DFLASH_DEVERR_POS and clamped to [0, ctx_len[0]] when outside).
+hipError_t launch_packed_setup(const int32_t* page_row, int max_pages, const int32_t* ctx_len,
+                               const int32_t* anchor_pos, int n_blocks, int32_t* table,
+                               int32_t* lens, uint32_t* err, hipStream_t stream);
+// Weighted cross-entropy of packed blocks: ce [n_blocks][gamma-1] fp64
+// scratch; block_loss [n_blocks] and loss [1] fp32 outputs (either may be
+// null).
+hipError_t launch_block_loss(const float* logits, const int32_t* targets, int n_blocks, int gamma,
+                             int vocab, double decay, double* ce, float* block_loss, float* loss,
+                             uint32_t* err, hipStream_t stream);

@@ -280,6 +280,39 @@ int dflash_verify_stochastic(const int32_t* block_tokens, const float* draft_log
                              int32_t vocab, int32_t* accept_len, int32_t* out_tokens,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* Packed multi-block forward (summary page: "Training Rehearses the Same
+ * Masked Blocks Used at Runtime", Figure 4; paper §4.2 "Random sampling of
+ * masked blocks") with the position-decayed loss (summary page: "Early
+ * Positions Receive More Learning Budget"; paper §4.2 eq. 1).  Forward
+ * only.  n_blocks blocks of one sequence run in one pass: block b holds
+ * [anchors[b], mask, ..., mask] at positions anchor_pos[b] + j, and its rows
+ * see the context keys [0, anchor_pos[b]) and the keys of their own block,
+ * nothing of the other blocks.
+ *   ctx         the sequence's context: page_table [1][max_pages_per_seq],
+ *               ctx_lens [1] = tokens in the cache (read only)
+ *   anchors     [n_blocks] clean anchor tokens
+ *   anchor_pos  [n_blocks] anchor positions, each in [0, ctx_lens[0]]
+ *               (else DFLASH_DEVERR_POS and the nearest bound is used)
+ *   targets     [n_blocks][block_size] true tokens (column 0 unused), or
+ *               NULL for no loss
+ *   decay       the loss weights' constant: w_k = exp(-(k-1)/decay) for the
+ *               predicted positions k = 1 .. block_size-1
+ *   logits      [n_blocks][block_size][V] fp32 out (required)
+ *   block_tokens [n_blocks][block_size] out (anchor, then argmax), or NULL
+ *   block_loss  [n_blocks] fp32 out: sum_k w_k CE_k / sum_k w_k, CE_k =
+ *               logsumexp(logits_k) - logits_k[target_k]; or NULL
+ *   loss        [1] fp32 out: mean of the block losses; or NULL
+ * A target outside [0, V) gives NaN for its block and sets
+ * DFLASH_DEVERR_TOKEN.  workspace: at least dflash_packed_workspace_bytes
+ * for this many blocks, block size and page-table width. */
+size_t dflash_packed_workspace_bytes(const dflash_model* model, int32_t max_blocks,
+                                     int32_t max_block, int32_t max_pages_per_seq);
+int dflash_packed_forward(const dflash_model* model, const dflash_kv* ctx, const int32_t* anchors,
+                          const int32_t* anchor_pos, int32_t n_blocks, int32_t block_size,
+                          const int32_t* targets, float decay, float* logits,
+                          int32_t* block_tokens, float* block_loss, float* loss,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* dflash_last_error(void);
 

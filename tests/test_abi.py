@@ -128,3 +128,14 @@ def test_stochastic_verify_rejects_bad_arguments(lib):
     assert b"aligned" in lib.dflash_last_error()
     assert call(args(wsb=need - 1)) == -4
     assert b"workspace" in lib.dflash_last_error()
+
+
+def test_packed_forward_rejects_bad_arguments(lib):
+    kv = _abi.KV(FAKE.value, 1, 1, FAKE.value, FAKE.value)
+    call = lambda **kw: lib.dflash_packed_forward(
+        kw.get("m", FAKE), ctypes.byref(kv), kw.get("anc", FAKE), kw.get("pos", FAKE),
+        kw.get("n", 4), kw.get("g", 16), kw.get("tgt", None), kw.get("decay", 7.0),
+        kw.get("lg", FAKE), None, kw.get("bl", None), kw.get("loss", None), FAKE, 1 << 30, None)
+    assert call(m=None) == -1
+    assert call(anc=None) == -1 and call(pos=None) == -1 and call(lg=None) == -1
+    assert lib.dflash_packed_workspace_bytes(None, 4, 16, 8) == 0
