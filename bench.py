@@ -540,6 +540,67 @@ def packed_bench(s, n_blocks, steps, warmup):
     drafter.close()
 
 
+def ar_bench(s, gammas, steps, warmup):
+    """Autoregressive drafting (block_size - 1 causal passes) next to the
+    one-pass block draft on the same model, context and anchors, per block
+    size (one JSON line): the pages' draft-cost argument measured here."""
+    import torch
+    from block_diffusion_drafter_fc_amd import Drafter, DrafterConfig, KVCache
+    from synth.configs import anchors, context_lengths, hidden_states, make_weights, page_pool
+    w_host = make_weights(s)
+    wdev = {k: to_dev(v, s.bf16) for k, v in w_host.items()}
+    cfg = DrafterConfig(hidden=s.hidden, n_layers=s.n_layers, n_q_heads=s.n_q_heads,
+                        n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, intermediate=s.inter,
+                        vocab=s.vocab, n_target_feats=s.n_feats, max_block=16,
+                        mask_token_id=s.mask_id, dtype=s.dtype, rope_theta=s.rope_theta,
+                        rms_eps=s.eps)
+    drafter = Drafter(cfg, wdev)
+    B = s.batch
+    L0 = context_lengths(s).astype(np.int64)
+    pps = int(L0.max() + 15) // 16 + 1
+    n_pages, table = page_pool(s, pps, extra=4, tag="bench.ar.pages")
+    dt = torch.bfloat16 if s.bf16 else torch.float32
+    pages = torch.zeros((s.n_layers, n_pages, 2, s.n_kv_heads, 16, s.head_dim), dtype=dt,
+                        device="cuda")
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kv = KVCache(pages, torch.from_numpy(table).cuda(), ctx)
+    ws = torch.empty(max(drafter.workspace_bytes(B, 16, 4096, pps),
+                         drafter.ar_workspace_bytes(B, 16, pps)), dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        for c0 in range(0, int(L0[b]), 4096):
+            n = min(4096, int(L0[b]) - c0)
+            cu = np.zeros(B + 1, np.int32)
+            cu[b + 1:] = n
+            drafter.inject(kv, to_dev(hidden_states(s, b, c0, n), s.bf16),
+                           torch.from_numpy(cu).cuda(), ws)
+    a = torch.from_numpy(anchors(s, B, tag="bench.ar.anchor")).cuda()
+    rows = []
+    for gamma in gammas:
+        res = {}
+        blk = torch.empty((B, gamma), dtype=torch.int32, device="cuda")
+        for mode in ("block", "ar"):
+            call = ((lambda: drafter.draft(kv, a, gamma, blk, ws)) if mode == "block" else
+                    (lambda: drafter.draft_ar(kv, a, gamma, blk, ws)))
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            res[mode] = (time.perf_counter() - t) * 1e3 / steps
+        rows.append({"block": gamma, "block_draft_ms": round(res["block"], 4),
+                     "ar_draft_ms": round(res["ar"], 4),
+                     "ar_over_block": round(res["ar"] / res["block"], 2),
+                     "block_tokens_per_s": round(B * (gamma - 1) * 1e3 / res["block"], 1),
+                     "ar_tokens_per_s": round(B * (gamma - 1) * 1e3 / res["ar"], 1)})
+        log(f"block {gamma}: {rows[-1]}")
+    assert drafter.device_error() == 0
+    print(json.dumps({"ar_vs_block": rows, "workload": s.name, "batch": B, "steps": steps,
+                      "warmup": warmup, "dtype": s.dtype}), flush=True)
+    drafter.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -554,6 +615,8 @@ def main():
                     help="summarise rocprofv3 --pmc output directories into profiles/")
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled-draft + lossless-verify step next to the greedy one")
+    ap.add_argument("--ar", default=None, metavar="G1,G2,...",
+                    help="time autoregressive drafting next to the block draft at these block sizes")
     ap.add_argument("--packed", type=int, default=0, metavar="N",
                     help="time the packed forward + loss of N blocks of one sequence instead")
     ap.add_argument("--block-sweep", default=None, metavar="G1,G2,...",
@@ -575,6 +638,9 @@ def main():
     if args.workload not in by_name:
         sys.exit(f"unknown workload {args.workload}; one of {sorted(by_name)}")
     s = by_name[args.workload]
+    if args.ar:
+        ar_bench(s, [int(g) for g in args.ar.split(",")], args.steps, args.warmup)
+        return
     if args.packed:
         packed_bench(s, args.packed, args.steps, args.warmup)
         return

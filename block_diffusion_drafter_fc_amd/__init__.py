@@ -221,6 +221,22 @@ class Drafter:
             _dev_ptr(loss, "loss", torch.float32), _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)))
 
+    def ar_workspace_bytes(self, max_batch, max_block, max_pages_per_seq) -> int:
+        n = self.lib.dflash_ar_workspace_bytes(self.handle, max_batch, max_block, max_pages_per_seq)
+        if n == 0:
+            raise DFlashError(-1, "ar_workspace_bytes: invalid arguments")
+        return int(n)
+
+    def draft_ar(self, kv: KVCache, anchor, block_size, block_tokens, workspace, logits=None,
+                 stream=None):
+        """dflash_draft_block_ar: block_size - 1 causal passes, one token each."""
+        import torch
+        _check(self.lib.dflash_draft_block_ar(
+            self.handle, ctypes.byref(kv.c), _dev_ptr(anchor, "anchor", torch.int32),
+            int(anchor.numel()), int(block_size), _dev_ptr(block_tokens, "block_tokens", torch.int32),
+            _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32(0)
         rc = self.lib.dflash_device_error(self.handle, _stream(stream), ctypes.byref(code))

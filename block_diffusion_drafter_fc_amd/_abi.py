@@ -21,6 +21,7 @@ EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_byt
             "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",
             "dflash_draft_block_sampled", "dflash_verify_stochastic_workspace_bytes",
             "dflash_verify_stochastic", "dflash_packed_workspace_bytes", "dflash_packed_forward",
+            "dflash_ar_workspace_bytes", "dflash_draft_block_ar",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
             "dflash_profile_read"]
 
@@ -95,6 +96,10 @@ def load(path: str = LIB_PATH):
     lib.dflash_packed_forward.argtypes = [vp, P(KV), vp, vp, i32, i32, vp, ctypes.c_float, vp, vp,
                                           vp, vp, vp, sz, vp]
     lib.dflash_packed_forward.restype = ctypes.c_int
+    lib.dflash_ar_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    lib.dflash_ar_workspace_bytes.restype = sz
+    lib.dflash_draft_block_ar.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.dflash_draft_block_ar.restype = ctypes.c_int
     lib.dflash_last_error.argtypes = []
     lib.dflash_last_error.restype = ctypes.c_char_p
     lib.dflash_device_error.argtypes = [vp, vp, P(i32)]

@@ -43,7 +43,7 @@ __device__ __forceinline__ void attn_block_keys(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
     const float* __restrict__ vb, int gamma, int Hq, int Hkv, int kvh, int b, int B, int split,
     float* __restrict__ part_o, float* __restrict__ part_ml, float (*ks)[DH + 4],
-    float (*vs)[DH + 4]) {
+    float (*vs)[DH + 4], int causal) {
   constexpr int QW = DH / 4;   // head dimensions per lane
   const int G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -81,7 +81,7 @@ __device__ __forceinline__ void attn_block_keys(
     }
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
-    sc[key] = key < gamma ? acc * sl2 : -INFINITY;
+    sc[key] = key < gamma && (!causal || key <= j) ? acc * sl2 : -INFINITY;
   }
   float mx = sc[0];
 #pragma unroll
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
     int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err, int causal) {
   constexpr int P = 32 * DH / 8;
   constexpr size_t KS_B = (size_t)32 * (DH + 8) * 2, VT_B = (size_t)DH * (32 + 8) * 2;
   constexpr size_t CTX_LDS = 2 * (KS_B + VT_B);
@@ -132,7 +132,8 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
   if (s == n_ctx_splits) {
     attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
-                        (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4));
+                        (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4),
+                        causal);
     return;
   }
   const int G = Hq / Hkv, T = 64 * G, tid = threadIdx.x;
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(
     const float* __restrict__ pages, int n_pages, const int32_t* __restrict__ page_table,
     int max_pages, int page_size, const int32_t* __restrict__ ctx_lens, int gamma, int Hq,
     int Hkv, int dh, int layer, float* __restrict__ part_o, float* __restrict__ part_ml,
-    uint32_t* err) {
+    uint32_t* err, int causal) {
   __shared__ float qs[256];
   __shared__ float ps[256];
   __shared__ const float* vrow[256];
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(
         } else {
           set_dev_error(err, pi < max_pages ? 1u : 2u);
         }
-      } else {
+      } else if (!causal || key - L <= j) {
         kp = kb + ((size_t)(b * gamma + key - L) * Hkv + kvh) * dh;
         vp = vb + ((size_t)(b * gamma + key - L) * Hkv + kvh) * dh;
       }
@@ -453,7 +454,7 @@ hipError_t run_ctx1(const AttnArgs& a, const AttnPlan& p, dim3 grid, dim3 block,
   hipLaunchKernelGGL((k_attn_bf16<DH, NPT, PF>), grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
                      (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
                      a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk,
-                     p.n_ctx_splits, a.part_o, a.part_ml, a.err);
+                     p.n_ctx_splits, a.part_o, a.part_ml, a.err, a.causal);
   return hipGetLastError();
 }
 
@@ -493,7 +494,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
     hipLaunchKernelGGL(k_attn_f32, grid, dim3(256), 0, st, (const float*)a.q, (const float*)a.k,
                        (const float*)a.v, (const float*)a.pages, a.n_pages, a.page_table,
                        a.max_pages, a.page_size, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.dh, a.layer,
-                       a.part_o, a.part_ml, a.err);
+                       a.part_o, a.part_ml, a.err, a.causal);
     return hipGetLastError();
   }
   // splits 0 .. n_ctx_splits-1: cached context; split n_ctx_splits: block keys

@@ -523,10 +523,19 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   return DFLASH_OK;
 }
 
+// A pass of the autoregressive variant: the rows' tokens come from
+// tokens[b*stride + j], the block keys are causal, and row 0's output is an
+// argmax like the others (no anchor substitution).
+struct ArPass {
+  const int32_t* tokens;
+  int stride;
+};
+
 // One draft pass; dr.on turns the LM head's argmax into a Gumbel-max draw.
 static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t* anchor,
                       int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
-                      void* workspace, size_t ws_bytes, void* stream, const DrawArgs& dr) {
+                      void* workspace, size_t ws_bytes, void* stream, const DrawArgs& dr,
+                      const ArPass* ar = nullptr) {
   dflash_model* m = const_cast<dflash_model*>(mc);
   if (!m || !kv || !anchor || !block_tokens || !workspace)
     return fail(DFLASH_E_INVAL, "draft_block: null argument");
@@ -604,6 +613,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
   at.part_o = att_o;
   at.part_ml = att_ml;
   at.err = m->err;
+  at.causal = ar ? 1 : 0;
 
   const int Nqkv = d.QD + 2 * d.KVD;
   const WSeg lm = seg1(m->w.lm_head, d.V);
@@ -616,7 +626,8 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     float* rope = (float*)(ws + L.rope);
     HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
                         nullptr, eps, nullptr, 0, ss, rope, kv->ctx_lens, d.dh,
-                        m->cfg.rope_theta, m->err, st));
+                        m->cfg.rope_theta, m->err, st, ar ? ar->tokens : nullptr,
+                        ar ? ar->stride : 0));
     int ss_tiles = 1;
     SkinnyArgs base{};
     base.M = M;
@@ -708,7 +719,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     a.K = d.D;
     a.amax = m->amax;
     a.actr = m->actr;
-    a.anchor = anchor;
+    a.anchor = ar ? nullptr : anchor;
     a.block_tokens = block_tokens;
     a.logits = logits;
     a.draw = dr;
@@ -720,7 +731,8 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
 
   HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
                       m->w.layer[0].attn_norm, eps, y, y_pl, nullptr, nullptr, nullptr, d.dh,
-                      m->cfg.rope_theta, m->err, st));
+                      m->cfg.rope_theta, m->err, st, ar ? ar->tokens : nullptr,
+                        ar ? ar->stride : 0));
   for (int l = 0; l < d.NL; ++l) {
     const dflash_layer_weights& W = m->w.layer[l];
     WSeg qkv{};
@@ -772,7 +784,8 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
   HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st,
                      dr));
   if ((rc = prof_end()) != DFLASH_OK) return rc;
-  HIPCHK(launch_argmax_finalize(best, L.groups, anchor, batch, gamma, block_tokens, st));
+  HIPCHK(launch_argmax_finalize(best, L.groups, ar ? nullptr : anchor, batch, gamma, block_tokens,
+                                st));
   return DFLASH_OK;
 }
 
@@ -781,6 +794,59 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
                        void* workspace, size_t ws_bytes, void* stream) {
   return draft_impl(m, kv, anchor, batch, gamma, block_tokens, logits, workspace, ws_bytes,
                     stream, DrawArgs{});
+}
+
+// Autoregressive drafting workspace: a draft pass of up to block_size - 1
+// rows per sequence, then the pass's row tokens [batch][block_size].
+static size_t ar_layout_total(const dflash_model* m, int batch, int gamma, int max_pages,
+                              size_t* tok_off) {
+  size_t need = 0;
+  for (int g = 1; g < gamma; ++g) need = std::max(need, draft_layout(m, batch, g, max_pages).total);
+  need = align256(need);
+  if (tok_off) *tok_off = need;
+  return align256(need + (size_t)batch * gamma * 4);
+}
+
+size_t dflash_ar_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_block,
+                                 int32_t max_pages_per_seq) {
+  if (!m || max_batch < 1 || max_block < 1 || max_block > m->cfg.max_block ||
+      max_pages_per_seq < 1)
+    return 0;
+  size_t need = 0;
+  for (int b = 1; b <= max_batch; ++b)
+    for (int g = 1; g <= max_block; ++g)
+      need = std::max(need, ar_layout_total(m, b, g, max_pages_per_seq, nullptr));
+  return need;
+}
+
+int dflash_draft_block_ar(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                          int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  if (!m || !kv || !anchor || !block_tokens || !workspace)
+    return fail(DFLASH_E_INVAL, "draft_block_ar: null argument");
+  if (batch < 1) return fail(DFLASH_E_INVAL, "draft_block_ar: batch must be >= 1");
+  if (gamma < 1 || gamma > m->cfg.max_block)
+    return fail(DFLASH_E_CAPACITY, "draft_block_ar: block_size %d outside [1, %d]", gamma,
+                m->cfg.max_block);
+  if (kv->max_pages_per_seq < 1)
+    return fail(DFLASH_E_INVAL, "draft_block_ar: empty page table");
+  size_t tok_off = 0;
+  const size_t need = ar_layout_total(m, batch, gamma, kv->max_pages_per_seq, &tok_off);
+  if (need > ws_bytes)
+    return fail(DFLASH_E_CAPACITY, "draft_block_ar: workspace %zu bytes < %zu needed", ws_bytes,
+                need);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* pass_tokens = (int32_t*)((char*)workspace + tok_off);
+  HIPCHK(launch_ar_seed(anchor, batch, gamma, block_tokens, st));
+  const ArPass ar{block_tokens, gamma};
+  for (int i = 1; i < gamma; ++i) {
+    const int rc = draft_impl(m, kv, anchor, batch, i, pass_tokens,
+                              i == gamma - 1 ? logits : nullptr, workspace, tok_off, stream,
+                              DrawArgs{}, &ar);
+    if (rc != DFLASH_OK) return rc;
+    HIPCHK(launch_ar_pick(pass_tokens, batch, i, gamma, block_tokens, st));
+  }
+  return DFLASH_OK;
 }
 
 int dflash_draft_block_sampled(const dflash_model* m, const dflash_kv* kv,

@@ -27,7 +27,9 @@ __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anch
                                                 size_t y_plane, float* __restrict__ ss_out,
                                                 float* __restrict__ rope,
                                                 const int32_t* __restrict__ ctx_lens, int dh,
-                                                float theta, uint32_t* err) {
+                                                float theta, uint32_t* err,
+                                                const int32_t* __restrict__ tokens,
+                                                int tok_stride) {
   __shared__ float red[16];
   const int r = blockIdx.x, b = r / gamma, j = r % gamma;
   if (rope != nullptr && (int)threadIdx.x < dh / 2) {
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anch
     rope[((size_t)r * (dh / 2) + threadIdx.x) * 2] = cs;
     rope[((size_t)r * (dh / 2) + threadIdx.x) * 2 + 1] = sn;
   }
-  int tok = j == 0 ? anchor[b] : mask_id;
+  int tok = tokens != nullptr ? tokens[(size_t)b * tok_stride + j] : (j == 0 ? anchor[b] : mask_id);
   if (tok < 0 || tok >= vocab) {
     if (threadIdx.x == 0) set_dev_error(err, 4u);
     tok = 0;
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const uint64_t* __restr
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) key = redk[w] > key ? redk[w] : key;
     const int j = r % gamma;
-    block_tokens[r] = j == 0 ? anchor[r / gamma] : (int32_t)argmax_key_index(key);
+    block_tokens[r] = j == 0 && anchor ? anchor[r / gamma] : (int32_t)argmax_key_index(key);
   }
 }
 
@@ -391,18 +393,19 @@ __global__ void k_verify_finalize(const uint64_t* __restrict__ best,
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
                         int vocab, const void* embed, int D, float* x, const void* g, float eps,
                         void* y, size_t y_plane, float* ss, float* rope, const int32_t* ctx_lens,
-                        int dh, float theta, uint32_t* err, hipStream_t st) {
+                        int dh, float theta, uint32_t* err, hipStream_t st,
+                        const int32_t* tokens, int tok_stride) {
   dim3 grid(batch * gamma);
   if (D % 4 != 0 || D > 8192 || dh > 2048) return hipErrorInvalidValue;
   if (rope != nullptr && ctx_lens == nullptr) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(k_embed<true>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
                        vocab, (const uint16_t*)embed, D, x, (const uint16_t*)g, eps, y, y_plane,
-                       ss, rope, ctx_lens, dh, theta, err);
+                       ss, rope, ctx_lens, dh, theta, err, tokens, tok_stride);
   else
     hipLaunchKernelGGL(k_embed<false>, grid, dim3(1024), 0, st, anchor, gamma, mask_id,
                        vocab, (const float*)embed, D, x, (const float*)g, eps, y, y_plane, ss,
-                       rope, ctx_lens, dh, theta, err);
+                       rope, ctx_lens, dh, theta, err, tokens, tok_stride);
   return hipGetLastError();
 }
 

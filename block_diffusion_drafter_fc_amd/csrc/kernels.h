@@ -95,7 +95,7 @@ struct SkinnyArgs {
   // anchor[b] for j == 0, else the argmax column) and re-zeroes amax and actr
   unsigned long long* amax;
   unsigned long long* actr;
-  const int32_t* anchor;
+  const int32_t* anchor;   // null: row 0 also gets its argmax
   int32_t* block_tokens;
   float* logits;           // [M][N] or null
   DrawArgs draw;           // SO_ARGMAX: draw instead of argmax (draw.gamma = gamma)
@@ -162,6 +162,7 @@ struct AttnArgs {
   float* part_o;        // [n_ctx_splits+1][B][Hq][gamma][dh]
   float* part_ml;       // [n_ctx_splits+1][B][Hq][gamma][2]  (max in log2 units, sum)
   uint32_t* err;
+  int causal;           // 1: block query j sees block keys 0..j only
 };
 hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
@@ -172,10 +173,13 @@ hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part
 // ss non-null: write the row sums of squares ss[M] instead of y.
 // rope non-null: also write rope[M][dh/2][2] = (cos, sin) of the rotary
 // angles at the position ctx_lens[b] + j of row r = b*gamma + j.
+// tokens non-null: row r = b*gamma + j takes tokens[b*tok_stride + j]
+// instead of (j == 0 ? anchor[b] : mask_id).
 hipError_t launch_embed(bool bf16, const int32_t* anchor, int batch, int gamma, int mask_id,
                         int vocab, const void* embed, int D, float* x, const void* g, float eps,
                         void* y, size_t y_plane, float* ss, float* rope, const int32_t* ctx_lens,
-                        int dh, float theta, uint32_t* err, hipStream_t stream);
+                        int dh, float theta, uint32_t* err, hipStream_t stream,
+                        const int32_t* tokens = nullptr, int tok_stride = 0);
 // Outputs named y, q, h, c are transient activations: fp32 for fp32 models,
 // split hi/lo bf16 planes for bf16 models (the lo plane starts *_plane
 // elements after the hi plane).
@@ -189,8 +193,8 @@ hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, 
                                size_t q_plane, float* k, float* v, hipStream_t stream);
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
                          size_t h_plane, hipStream_t stream);
-// block_tokens[r] = r % gamma == 0 ? anchor[r / gamma] : column of the
-// largest key of row r over best[0..groups)[r].
+// block_tokens[r] = r % gamma == 0 && anchor ? anchor[r / gamma] : column of
+// the largest key of row r over best[0..groups)[r].
 hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_t* anchor,
                                   int batch, int gamma, int32_t* block_tokens, hipStream_t stream);
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
@@ -232,3 +236,10 @@ hipError_t launch_packed_setup(const int32_t* page_row, int max_pages, const int
 hipError_t launch_block_loss(const float* logits, const int32_t* targets, int n_blocks, int gamma,
                              int vocab, double decay, double* ce, float* block_loss, float* loss,
                              uint32_t* err, hipStream_t stream);
+
+// ---- autoregressive drafting (DFlash-AR) ----------------------------------
+// block[b][0] = anchor[b]; after pass i, block[b][i] = pass_tokens[b*i + i-1].
+hipError_t launch_ar_seed(const int32_t* anchor, int batch, int gamma, int32_t* block,
+                          hipStream_t stream);
+hipError_t launch_ar_pick(const int32_t* pass_tokens, int batch, int i, int gamma, int32_t* block,
+                          hipStream_t stream);

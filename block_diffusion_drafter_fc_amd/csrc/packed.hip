@@ -109,7 +109,36 @@ __global__ void k_block_loss(const double* __restrict__ ce, int n_blocks, int ga
   }
 }
 
+// Autoregressive drafting: block[b][0] = anchor[b].
+__global__ void k_ar_seed(const int32_t* __restrict__ anchor, int batch, int gamma,
+                          int32_t* __restrict__ block) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) block[(size_t)b * gamma] = anchor[b];
+}
+
+// After pass i (rows 0..i-1 of each sequence): block[b][i] = the argmax of
+// the pass's last row, pass_tokens[b*i + i-1].
+__global__ void k_ar_pick(const int32_t* __restrict__ pass_tokens, int batch, int i, int gamma,
+                          int32_t* __restrict__ block) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) block[(size_t)b * gamma + i] = pass_tokens[(size_t)b * i + i - 1];
+}
+
 }  // namespace
+
+hipError_t launch_ar_seed(const int32_t* anchor, int batch, int gamma, int32_t* block,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_ar_seed, dim3((batch + 255) / 256), dim3(256), 0, st, anchor, batch, gamma,
+                     block);
+  return hipGetLastError();
+}
+
+hipError_t launch_ar_pick(const int32_t* pass_tokens, int batch, int i, int gamma, int32_t* block,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_ar_pick, dim3((batch + 255) / 256), dim3(256), 0, st, pass_tokens, batch, i,
+                     gamma, block);
+  return hipGetLastError();
+}
 
 hipError_t launch_packed_setup(const int32_t* page_row, int max_pages, const int32_t* ctx_len,
                                const int32_t* anchor_pos, int n_blocks, int32_t* table,

@@ -490,7 +490,8 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
         key = k2 > key ? k2 : key;
       }
       const int j = tid % a.gamma;
-      a.block_tokens[tid] = j == 0 ? a.anchor[tid / a.gamma] : (int32_t)argmax_key_index(key);
+      a.block_tokens[tid] = j == 0 && a.anchor ? a.anchor[tid / a.gamma]
+                                               : (int32_t)argmax_key_index(key);
     }
     __syncthreads();
     for (int i = tid; i < kXcds * 64; i += 256) atomicExch(&a.amax[i], 0ull);
@@ -672,7 +673,7 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
   const int n_tiles = skinny_tiles(out, a.N, a.dh, a.I);
   if (n_tiles < 0) return hipErrorInvalidValue;
   if (out == SO_ARGMAX && (p.splits != 1 || a.amax == nullptr || a.actr == nullptr ||
-                           a.anchor == nullptr || a.block_tokens == nullptr || a.gamma < 1))
+                           a.block_tokens == nullptr || a.gamma < 1))
     return hipErrorInvalidValue;
   if (tile_groups(out, a.dh) * p.splits > kMaxPer) return hipErrorInvalidValue;
   if (asrc == SA_NORM && (a.ss_in == nullptr || a.ss_tiles < 1 || a.ss_tiles > kMaxSsTiles ||

@@ -313,6 +313,28 @@ int dflash_packed_forward(const dflash_model* model, const dflash_kv* ctx, const
                           int32_t* block_tokens, float* block_loss, float* loss,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* Autoregressive drafting with the same drafter (paper §5.5.5, DFlash-AR:
+ * K/V injection, autoregressive drafting; summary page "Block Diffusion
+ * Makes Draft Cost Nearly Independent of Block Length": one forward pass per
+ * proposed token).  For i = 1 .. block_size-1, pass i runs the drafter over
+ * the tokens [anchor, d_1, ..., d_{i-1}] at positions ctx_lens[b] + j with a
+ * causal mask inside them (row j sees the cached context and rows 0..j),
+ * and d_i is the lowest-index argmax of the pass's last row.  Each pass
+ * recomputes all its rows.
+ *   block_tokens [batch][block_size] out: [anchor, d_1, ..., d_{block_size-1}]
+ *                (also the passes' input, so it must not alias anchor)
+ *   logits       [batch][block_size-1][V] fp32 out, or NULL: the last
+ *                pass's rows; row j gives the scores that chose d_{j+1}
+ *                (equal to pass j+1's last row, the mask being causal)
+ *   workspace    at least dflash_ar_workspace_bytes(model, batch, block_size,
+ *                max_pages_per_seq)
+ * The cache and ctx_lens are read only. */
+size_t dflash_ar_workspace_bytes(const dflash_model* model, int32_t max_batch, int32_t max_block,
+                                 int32_t max_pages_per_seq);
+int dflash_draft_block_ar(const dflash_model* model, const dflash_kv* kv, const int32_t* anchor,
+                          int32_t batch, int32_t block_size, int32_t* block_tokens, float* logits,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread. */
 const char* dflash_last_error(void);
 

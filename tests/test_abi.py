@@ -139,3 +139,12 @@ def test_packed_forward_rejects_bad_arguments(lib):
     assert call(m=None) == -1
     assert call(anc=None) == -1 and call(pos=None) == -1 and call(lg=None) == -1
     assert lib.dflash_packed_workspace_bytes(None, 4, 16, 8) == 0
+
+
+def test_ar_draft_rejects_bad_arguments(lib):
+    kv = _abi.KV(FAKE.value, 1, 1, FAKE.value, FAKE.value)
+    assert lib.dflash_draft_block_ar(None, ctypes.byref(kv), FAKE, 1, 16, FAKE, None, FAKE,
+                                     1 << 30, None) == -1
+    assert lib.dflash_draft_block_ar(FAKE, ctypes.byref(kv), None, 1, 16, FAKE, None, FAKE,
+                                     1 << 30, None) == -1
+    assert lib.dflash_ar_workspace_bytes(None, 1, 16, 8) == 0
