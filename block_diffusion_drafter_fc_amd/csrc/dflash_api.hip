@@ -780,9 +780,15 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
   }
 
   const GemmPlan p = plan_gemm(bf, M, d.V, d.D, true);
+  // On the large-product kernel (>= 256 rows, MFMA-bound) the LM head takes
+  // its input in bf16, the workload's activation precision, which halves its
+  // matrix-core work: the hi plane alone is the bf16 rounding of the fp32
+  // row.  The lo plane carries the layers' fp32 activations; the LM head is
+  // the last product, so its rounding only adds a bounded logit error
+  // (sum over D of |h| * |W| * 2^-9) and is not amplified by later layers.
+  const void* lm_lo = p.kind == GEMM_BIG ? nullptr : lo(y, y_pl);
   if ((rc = prof_begin()) != DFLASH_OK) return rc;
-  HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, lm, d.V, d.D, nullptr, best, logits, st,
-                     dr));
+  HIPCHK(launch_gemm(p, bf, y, lm_lo, d.D, M, lm, d.V, d.D, nullptr, best, logits, st, dr));
   if ((rc = prof_end()) != DFLASH_OK) return rc;
   HIPCHK(launch_argmax_finalize(best, L.groups, ar ? nullptr : anchor, batch, gamma, block_tokens,
                                 st));
