@@ -30,7 +30,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxCtxSplits = 256;            // bounded by plan_attention
 constexpr int kMaxChunk = 1024;               // context keys per workgroup (64 pages)
-constexpr int kMaxParts = kMaxCtxSplits + 1;  // + the block's own keys
 
 // The block's own gamma keys (workgroup s == n_ctx_splits of the same grid):
 // fp32 on the vector ALUs, since the block keys and values are transient fp32
@@ -403,50 +402,68 @@ __global__ __launch_bounds__(256) void k_attn_f32(
   }
 }
 
+// Workgroup (h, b, z) merges rows z*R .. z*R+R-1 of query head h of
+// sequence b; thread t takes row z*R + t / (dh/4) and columns 4 (t % (dh/4))
+// .. +3.  Each thread forms its row's weights 2^(m_s - max) in registers (the
+// threads of a row read the same (max, sum) pairs, which the caches serve)
+// and sums its columns over the parts in part order.  Loads are issued in
+// groups of kCombineGroup parts ahead of the arithmetic, so a thread waits
+// once per group rather than once per part.
+constexpr int kCombineGroup = 8;
+
 template <bool BF16>
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_parts, int gamma, int Hq, int dh,
-                                                      void* __restrict__ o, size_t o_plane) {
-  // Phase 1: thread s < n_parts fetches split s's (max, sum) -- all at once --
-  // and the group forms the common maximum and the weights 2^(m_s - max).
-  // Phase 2: thread d sums the weighted partial outputs over the splits.
-  __shared__ float wgt[kMaxParts];
-  __shared__ float red[4];
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z, d = threadIdx.x;
-  const size_t stride = (size_t)B * Hq * gamma;            // partial rows per split
+                                                      int rows, void* __restrict__ o,
+                                                      size_t o_plane) {
+  const int h = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const int per = dh / 4;
+  const int j = blockIdx.z * rows + threadIdx.x / per, d0 = (threadIdx.x % per) * 4;
+  if (j >= gamma) return;
+  const size_t stride = (size_t)B * Hq * gamma;            // partial rows per part
   const size_t pr0 = ((size_t)b * Hq + h) * gamma + j;
+  const float2* ml_row = (const float2*)part_ml + pr0;
   float mx = -INFINITY;
-  for (int s = d; s < n_parts; s += blockDim.x) {
-    if (part_ml[(pr0 + s * stride) * 2 + 1] > 0.f) mx = fmaxf(mx, part_ml[(pr0 + s * stride) * 2]);
+  for (int s0 = 0; s0 < n_parts; s0 += kCombineGroup) {
+    float2 ml[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u)
+      ml[u] = s0 + u < n_parts ? ml_row[(s0 + u) * stride] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u)
+      if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
   }
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-  if ((d & 63) == 0) red[d >> 6] = mx;
-  __syncthreads();
-  mx = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();
-  for (int s = d; s < n_parts; s += blockDim.x) {
-    const float l = part_ml[(pr0 + s * stride) * 2 + 1];
-    wgt[s] = l > 0.f ? exp2f(part_ml[(pr0 + s * stride) * 2] - mx) : 0.f;
-  }
-  __syncthreads();
-  float num = 0.f, den = 0.f;
-  if (d < dh) {
-    // loads are unconditional (every slot is written: empty splits carry
-    // weight 0 and a stale value that the select drops) so they can be
-    // issued together
-#pragma unroll 16
-    for (int s = 0; s < n_parts; ++s) {
-      const float ww = wgt[s];
-      const float ov = part_o[(pr0 + s * stride) * dh + d];
-      const float lv = part_ml[(pr0 + s * stride) * 2 + 1];
-      num += ww != 0.f ? ww * ov : 0.f;
-      den += ww != 0.f ? ww * lv : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s0 = 0; s0 < n_parts; s0 += kCombineGroup) {
+    float2 ml[kCombineGroup];
+    f32x4 v[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      if (s0 + u < n_parts) {
+        ml[u] = ml_row[(s0 + u) * stride];
+        v[u] = *(const f32x4*)(part_o + (pr0 + (s0 + u) * stride) * dh + d0);
+      } else {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    const float v = den > 0.f ? num / den : 0.f;
-    Split<BF16>::store(o, o_plane, ((size_t)(b * gamma + j) * Hq + h) * dh + d, v);
+    // an empty part (sum 0) may hold stale values: it is selected away, not
+    // multiplied by a zero weight
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const bool live = ml[u].y > 0.f;
+      const float w = live ? exp2f(ml[u].x - mx) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = live ? acc[e] + w * v[u][e] : acc[e];
+      den = live ? den + w * ml[u].y : den;
+    }
   }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const size_t dst = ((size_t)(b * gamma + j) * Hq + h) * dh + d0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Split<BF16>::store(o, o_plane, dst + e, acc[e] * inv);
 }
 
 template <int DH, int NPT, int PF>
@@ -514,13 +531,23 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
 hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part_ml, int n_parts,
                                int batch, int gamma, int Hq, int dh, void* o, size_t o_plane,
                                hipStream_t st) {
-  dim3 grid(gamma, Hq, batch);
-  dim3 block(dh < 64 ? 64 : dh);
+  if (dh % 4 != 0 || dh > 1024 || gamma < 1 || n_parts < 1) return hipErrorInvalidValue;
+  // rows per workgroup: at least one full wave, then more rows while the
+  // grid keeps >= 1024 workgroups, at most 256 threads
+  const int per = dh / 4;
+  int rows = 1;
+  while (rows < gamma && rows * per < 64) rows *= 2;
+  while (rows < gamma && 2 * rows * per <= 256 &&
+         (long long)Hq * batch * ((gamma + 2 * rows - 1) / (2 * rows)) >= 1024)
+    rows *= 2;
+  if (rows > gamma) rows = gamma;
+  dim3 grid(Hq, batch, (gamma + rows - 1) / rows);
+  dim3 block(rows * per);
   if (bf16)
     hipLaunchKernelGGL(k_attn_combine<true>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, o, o_plane);
+                       Hq, dh, rows, o, o_plane);
   else
     hipLaunchKernelGGL(k_attn_combine<false>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, o, o_plane);
+                       Hq, dh, rows, o, o_plane);
   return hipGetLastError();
 }
