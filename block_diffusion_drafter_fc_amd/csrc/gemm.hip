@@ -377,8 +377,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 // read from LDS), K in steps of 32 through a ring of LDS stages.  WM = 2: 4
 // waves, one per SIMD, 4 stages, and each wave reads the next step's MFMA
 // fragments while the current step's MFMAs run.  WM = 4: 8 waves, two per
-// SIMD (each hides the other's LDS latency), 3 stages, and the weight tile is
-// shared by 256 rows instead of 128.
+// SIMD in two groups half a step apart (one group reads fragments while the
+// other runs MFMAs), 3 stages, and the weight tile is shared by 256 rows
+// instead of 128.
 //
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4: lane
 // l of a wave writes its 16 bytes at the instruction's LDS base + 16 l), so
@@ -520,15 +521,29 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
       mfmas(f1);
     }
   } else {
-    // Iteration s: stage s becomes ready, the stage that held step s - 1
-    // receives step s + G - 1, then step s's fragments and MFMAs.
+    // Two wave groups (waves 0-3 and 4-7, one of each per SIMD) run half a
+    // step apart: every wave runs read(s) | barrier | MFMAs(s) | barrier,
+    // and group 1 starts one barrier late, so one group's fragment reads
+    // overlap the other group's MFMAs on every SIMD (in lockstep, both
+    // waves of a SIMD would wait for their reads together).  A wave issues
+    // step s + G - 1 at the start of its read phase of step s; that stage
+    // last held step s - 1, which both groups read before the previous
+    // barrier.  Stage s + 1 must be complete at the barrier that ends group
+    // 0's MFMA phase of step s: group 0 waits for it there, group 1 at the
+    // end of its read phase of step s, which is the same barrier.
     Frags f;
+    const int grp = wave >> 2;
+    stage_ready(min(steps - 1, G - 2));
+    if (grp == 1) __builtin_amdgcn_s_barrier();
     for (int s = 0; s < steps; ++s) {
-      stage_ready(min(steps - 1 - s, G - 2));
       if (s + G - 1 < steps) issue(s + G - 1);
       read_frags(f, s);
+      const int later = max(min(steps - 2 - s, G - 2), 0);   // steps' loads left in flight
+      stage_ready(grp == 1 ? later : min(later + 1, steps - 1 - s));
       mfmas(f);
+      stage_ready(later);
     }
+    if (grp == 0) __builtin_amdgcn_s_barrier();
   }
 
   if (!ARGMAX) {
