@@ -372,9 +372,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 }
 
 // ----------------------------------------------------------------------------
-// Large product (M >= 256): 64*WM x 256 output tiles, 2*WM waves of 64 x 128
-// (wide in N, so that the two activation planes share every weight fragment
-// read from LDS), K in steps of 32 through a ring of LDS stages.  WM = 2: 4
+// Large product (M >= 256): 64*WM x BN output tiles (BN = 256, or 192 where
+// 256-column tiles leave CUs idle), 2*WM waves of 64 x BN/2 (wide in N, so
+// that the two activation planes share every weight fragment read from
+// LDS), K in steps of 32 through a ring of LDS stages.  WM = 2: 4
 // waves, one per SIMD, 4 stages, and each wave reads the next step's MFMA
 // fragments while the current step's MFMAs run.  WM = 4: 8 waves, two per
 // SIMD in two groups half a step apart (one group reads fragments while the
@@ -383,20 +384,21 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 //
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4: lane
 // l of a wave writes its 16 bytes at the instruction's LDS base + 16 l), so
-// no registers stage the tiles and GSTAGES - 1 steps of loads stay in
-// flight.  A stage holds the tile rows back to back, 64 bytes each: the A
-// planes' 64*WM rows each, then the 256 weight rows.  The four 16-byte
+// no registers stage the tiles and G - 1 steps of loads stay in flight.  A
+// stage holds the tile rows back to back, 64 bytes each: the A planes'
+// 64*WM rows each, then the BN weight rows; every wave issues the same number
+// of 16-row load blocks, and blocks past the tile land in a spare area.  The four 16-byte
 // chunks of row R sit XOR-swizzled (chunk c at slot c ^ ((R >> 1) & 3)), so
 // the 16 rows a fragment read touches land in distinct banks; a load block
 // of 16 rows (1 KB, one wave instruction) fetches the chunks in swizzled
 // order.
-constexpr int GBN = 256, GBK = 32;
+constexpr int GBN = 256, GBK = 32;   // widest weight tile, K step
 constexpr int big_stages(int wm) { return wm == 4 ? 3 : 4; }
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* glb_void_t;
 
-template <bool SPLIT, bool ARGMAX, int WM>
+template <bool SPLIT, bool ARGMAX, int WM, int BN>
 __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
@@ -405,10 +407,11 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
   constexpr bool DBUF = WM == 2;
   constexpr int NP = SPLIT ? 2 : 1;
   constexpr int RA = NP * BM;                  // A rows per stage
-  constexpr int NR = RA + GBN;                 // rows per stage
-  constexpr int SB = NR * 64;                  // bytes per stage
-  constexpr int NL = NR / 16 / NWAVE;          // load instructions per wave per stage
-  static_assert(NR % (16 * NWAVE) == 0, "stage rows must split evenly over the waves");
+  constexpr int NR = RA + BN;                  // rows per stage
+  constexpr int NL = (NR / 16 + NWAVE - 1) / NWAVE;   // load instructions per wave per stage
+  constexpr int SB = NL * NWAVE * 1024;        // bytes per stage (blocks past NR: spare)
+  constexpr int NBF = BN / 32;                 // 16-column weight fragments per wave
+  static_assert(NR % 16 == 0 && BN % 64 == 0, "tile rows come in blocks of 16");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[G * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -422,8 +425,8 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
   const int mtiles = (M + BM - 1) / BM;
   const int slot = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int ntile = (q / mtiles) * 8 + slot;
-  if (ntile * GBN >= N) return;
-  const int m0 = (q % mtiles) * BM, n0 = ntile * GBN, split = blockIdx.z;
+  if (ntile * BN >= N) return;
+  const int m0 = (q % mtiles) * BM, n0 = ntile * BN, split = blockIdx.z;
   const int kbeg = split * kps;
 
   // global source of each of this lane's loads (block wave + NWAVE j)
@@ -438,7 +441,8 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
       const int r = min(m0 + (R % BM), M - 1);
       row = (pl ? Alo : A) + (size_t)r * lda;
     } else {
-      row = seg_row_bf16(w, min(n0 + (R - RA), N - 1), K);
+      // (spare blocks past the tile re-read its first weight row)
+      row = seg_row_bf16(w, min(R < NR ? n0 + (R - RA) : n0, N - 1), K);
     }
     gp[j] = row + kbeg + c * 8;
   }
@@ -453,21 +457,21 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
     return *(const u32x4*)(base + R * 64 + ((lg ^ ((R >> 1) & 3)) << 4));
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][NBF];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NBF; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Fragments of one step: B (8 x 16 weight rows) and A (4 x 16 rows per
+  // Fragments of one step: B (NBF x 16 weight rows) and A (4 x 16 rows per
   // plane).
   struct Frags {
-    u32x4 b[8], a[NP][4];
+    u32x4 b[NBF], a[NP][4];
   };
   auto read_frags = [&](Frags& f, int s) {
     const unsigned char* base = lds + (s % G) * SB;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) f.b[b] = frag(base, RA + wn * 128 + b * 16 + lr);
+    for (int b = 0; b < NBF; ++b) f.b[b] = frag(base, RA + wn * (BN / 2) + b * 16 + lr);
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_16x16x32(f.a[pl][a], f.b[b], acc[a][b]);
+        for (int b = 0; b < NBF; ++b) acc[a][b] = mfma_16x16x32(f.a[pl][a], f.b[b], acc[a][b]);
   };
   // Stage t is complete for the whole workgroup once every lane has waited
   // for its own loads of step t (at most the later steps' loads, `later`
@@ -555,14 +559,14 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
         if (row >= M) continue;
         float* dst = part + ((size_t)split * M + row) * N;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const int col = n0 + wn * 128 + b * 16 + lr;
+        for (int b = 0; b < NBF; ++b) {
+          const int col = n0 + wn * (BN / 2) + b * 16 + lr;
           if (col < N) dst[col] = acc[a][b][i];
         }
       }
     return;
   }
-  // Row argmax over the tile's 256 columns: per wave (8 fragments, then the
+  // Row argmax over the tile's BN columns: per wave (NBF fragments, then the
   // 16 lanes of a row), then over the two column halves in LDS.
   __syncthreads();
   uint64_t* hkeys = (uint64_t*)lds;   // [2][BM], the stages are no longer read
@@ -574,8 +578,8 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
       const int row = m0 + rloc;
       uint64_t key = 0;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int col = n0 + wn * 128 + b * 16 + lr;
+      for (int b = 0; b < NBF; ++b) {
+        const int col = n0 + wn * (BN / 2) + b * 16 + lr;
         if (col < N) {
           const float v = acc[a][b][i];
           const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
@@ -651,29 +655,33 @@ hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda
 // to measurements on the Qwen3-8B shapes: a round of up to 256 workgroups
 // (one per CU) costs steps/S * t_step plus ~11 us of fixed cost (filling the
 // stage ring, writing the tile, dispatch), with t_step ~1.1 us for the 4-wave
-// 128-row tile and ~1.8 us for the 8-wave 256-row tile (split activations);
+// 128-row tile and ~1.45 us for the 8-wave 256-row tile (split activations,
+// 256 weight columns; proportionally less for 192);
 // each extra partial slice costs its write-back and the reducer's read
 // (2 * M * N * 4 bytes at ~5 TB/s).  Splits keep an even number of >= 4 steps.
 struct BigChoice {
-  int wm, splits;
+  int wm, splits, bn;
 };
 
 BigChoice big_plan(int M, int N, int K, bool argmax) {
-  BigChoice best{2, 1};
+  BigChoice best{2, 1, GBN};
   double best_cost = 1e300;
   const int steps = K / GBK;
-  const long ntiles = (N + GBN - 1) / GBN;
-  for (int wm = 2; wm <= 4; wm += 2) {
-    const long tiles = (long)((M + 64 * wm - 1) / (64 * wm)) * ntiles;
-    const double t_step = wm == 4 ? 1.8 : 1.1;
-    for (int S = 1; S <= (argmax ? 1 : 16); ++S) {
-      if (steps % S || (steps / S) % 2 || steps / S < 4) continue;
-      const double rounds = (double)((tiles * S + 255) / 256);
-      const double cost = rounds * ((double)(steps / S) * t_step + 11.0) +
-                          (double)(S - 1) * M * (double)N * 8.0 / 5e6;
-      if (cost < best_cost) {
-        best_cost = cost;
-        best = BigChoice{wm, S};
+  for (int bn = GBN; bn >= 192; bn -= 64) {
+    if (argmax && bn != GBN) continue;
+    const long ntiles = (N + bn - 1) / bn;
+    for (int wm = 2; wm <= 4; wm += 2) {
+      const long tiles = (long)((M + 64 * wm - 1) / (64 * wm)) * ntiles;
+      const double t_step = (wm == 4 ? 1.45 : 1.1) * bn / GBN;
+      for (int S = 1; S <= (argmax ? 1 : 16); ++S) {
+        if (steps % S || (steps / S) % 2 || steps / S < 4) continue;
+        const double rounds = (double)((tiles * S + 255) / 256);
+        const double cost = rounds * ((double)(steps / S) * t_step + 11.0) +
+                            (double)(S - 1) * M * (double)N * 8.0 / 5e6;
+        if (cost < best_cost) {
+          best_cost = cost;
+          best = BigChoice{wm, S, bn};
+        }
       }
     }
   }
@@ -726,6 +734,7 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
     p.kind = GEMM_BIG;
     const BigChoice c = big_plan(M, N, K, argmax);
     p.mt = c.wm;
+    p.nt = c.bn;
     p.splits = c.splits;
     p.kpw = K / p.splits;
     return p;
@@ -745,7 +754,7 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
 int gemm_argmax_groups(const GemmPlan& p, int N) {
   if (p.kind == GEMM_F32) return (N + 63) / 64;
   if (p.kind == GEMM_TILED) return (N + TBN - 1) / TBN;
-  if (p.kind == GEMM_BIG) return (N + GBN - 1) / GBN;
+  if (p.kind == GEMM_BIG) return (N + p.nt - 1) / p.nt;
   return (N + 64 * p.nt - 1) / (64 * p.nt);
 }
 
@@ -780,21 +789,23 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
     return hipGetLastError();
   }
   if (p.kind == GEMM_BIG) {
-    if ((p.mt != 2 && p.mt != 4) || p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K ||
-        lda % 8 != 0)
+    if ((p.mt != 2 && p.mt != 4) || (p.nt != GBN && (p.nt != 192 || best)) ||
+        p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K || lda % 8 != 0)
       return hipErrorInvalidValue;
     const int bm = 64 * p.mt;
-    dim3 grid(((N + GBN - 1) / GBN + 7) / 8 * 8 * ((M + bm - 1) / bm), 1, p.splits);
+    dim3 grid(((N + p.nt - 1) / p.nt + 7) / 8 * 8 * ((M + bm - 1) / bm), 1, p.splits);
     const uint16_t* a = (const uint16_t*)A;
     const uint16_t* al = (const uint16_t*)Alo;
-#define DF_BIG(SPL, AM, WM)                                                                     \
-  hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM>), grid, dim3(128 * WM), 0, st, a, al, lda, M, w, N, \
-                     K, p.kpw, part, best, logits, dr)
-#define DF_BIG2(WM)                       \
-  if (al && best) DF_BIG(true, true, WM);  \
-  else if (al) DF_BIG(true, false, WM);    \
-  else if (best) DF_BIG(false, true, WM);  \
-  else DF_BIG(false, false, WM)
+#define DF_BIG(SPL, AM, WM, BN)                                                              \
+  hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM, BN>), grid, dim3(128 * WM), 0, st, a, al, lda, M, \
+                     w, N, K, p.kpw, part, best, logits, dr)
+#define DF_BIG2(WM)                                       \
+  if (al && best) DF_BIG(true, true, WM, GBN);             \
+  else if (best) DF_BIG(false, true, WM, GBN);             \
+  else if (al && p.nt == GBN) DF_BIG(true, false, WM, GBN); \
+  else if (al) DF_BIG(true, false, WM, 192);               \
+  else if (p.nt == GBN) DF_BIG(false, false, WM, GBN);     \
+  else DF_BIG(false, false, WM, 192)
     if (p.mt == 4) {
       DF_BIG2(4);
     } else {
