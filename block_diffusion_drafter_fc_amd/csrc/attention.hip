@@ -54,6 +54,7 @@ __device__ __forceinline__ void attn_block_keys(
     *(f32x4*)&vs[key][d] = *(const f32x4*)&vb[off];
   }
   __syncthreads();
+  if (wave >= G) return;   // loader-only waves of a small KV group
   const int j = lane >> 2, qd = lane & 3;
   const int jj = j < gamma ? j : 0;
   float qv[QW];
@@ -107,43 +108,63 @@ __device__ __forceinline__ void attn_block_keys(
   }
 }
 
-// Context path.  A tile is 32 keys: P = 32*DH/8 sixteen-byte pieces of K
-// and as many of V.  Each thread moves NPT pieces of each per tile (piece
-// c = tid + i*T, T = 64*G threads; pieces past P re-read the last one and are
-// not stored).  The split's page-table slice is read once into LDS; up to PF
-// tiles of K/V loads are in flight in a register ring while earlier tiles
-// are scored, and the LDS tiles are double-buffered, so a tile costs one
-// barrier.  Loads are never predicated (keys past the end are clamped and
-// masked at the store), which keeps the compiler's wait counts exact.
-template <int DH, int NPT, int PF>
-__global__ __launch_bounds__(512) void k_attn_bf16(
+// Context path.  A tile is 32 keys; a stage of the LDS ring holds its K rows
+// (32 x DH bf16, row-major) and its values transposed (DH x 32), so both MFMA
+// operands read 16 contiguous bytes per lane.  The cache stores each page's
+// values already transposed ([head_dim][16]), so both halves of a stage are
+// 1 KB blocks of contiguous memory that global_load_lds_dwordx4 moves straight
+// into LDS (lane l's 16 bytes land at the block base + 16 l): no registers
+// stage the tiles, the loads are fully coalesced, and NST - 1 tiles stay in
+// flight.  The W waves of a workgroup issue the stage's blocks evenly; waves
+// past the G query heads of the KV group only load.  Chunks sit
+// XOR-swizzled within their rows (K: by kswz, V: by (row >> 1) & 3) so that
+// the 16 rows a fragment read touches land in distinct banks; the swizzle is
+// applied to the global source of each lane, the LDS placement being fixed.
+template <int DH>
+DF_DEV int kswz(int R) {
+  return DH == 128 ? ((((R >> 3) << 2) | (R & 3)) & 15) : ((((R >> 3) << 1) | ((R >> 1) & 1)) & 7);
+}
+DF_DEV int vswz(int R) { return (R >> 1) & 3; }
+
+typedef __attribute__((address_space(3))) void* attn_lds_t;
+typedef __attribute__((address_space(1))) void* attn_glb_t;
+
+template <int DH, int W, int NST>
+__global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void k_attn_ctx(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
     const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
     int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err, int causal) {
-  constexpr int P = 32 * DH / 8;
-  constexpr size_t KS_B = (size_t)32 * (DH + 8) * 2, VT_B = (size_t)DH * (32 + 8) * 2;
-  constexpr size_t CTX_LDS = 2 * (KS_B + VT_B);
-  constexpr size_t BLK_LDS = (size_t)2 * 16 * (DH + 4) * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
+  constexpr int KT = 32 * DH * 2;              // bytes of the K tile (= the V tile)
+  constexpr int SB = 2 * KT;                   // bytes per stage
+  constexpr int NB = SB / 1024;                // 1 KB load blocks per stage
+  constexpr int NLW = NB / W;                  // blocks per wave
+  static_assert(NB % W == 0, "stage blocks must split evenly over the waves");
+  constexpr int CPR = DH / 8;                  // 16-byte chunks per K row
+  constexpr int KPB = 1024 / (DH * 2);         // K rows per block
+  constexpr int CTX_LDS = NST * SB;
+  constexpr int BLK_LDS = 2 * 16 * (DH + 4) * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
   __shared__ int pg_s[64];
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  const int G = Hq / Hkv;
   if (s == n_ctx_splits) {
     attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
                         (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4),
                         causal);
     return;
   }
-  const int G = Hq / Hkv, T = 64 * G, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int h = kvh * G + wave;
+  const bool comp = wave < G;
+  const int h = kvh * G + (comp ? wave : 0);
   const int L = ctx_lens[b];
   const int kbeg = s * chunk;
   const int kend = min(kbeg + chunk, L);
   const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0
   if (kend <= kbeg) {
-    if (lg == 0 && lr < gamma) {
+    if (comp && lg == 0 && lr < gamma) {
       part_ml[(prow + lr) * 2 + 0] = -INFINITY;
       part_ml[(prow + lr) * 2 + 1] = 0.f;
     }
@@ -172,53 +193,59 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     if (bad && lane < npg) set_dev_error(err, pi < max_pages ? 1u : 2u);
     pg_s[lane] = bad ? -1 : pg;
   }
-  __syncthreads();   // pg_s
+  __syncthreads();   // pg_s; the Q loads are complete too
 
-  const size_t head_stride = (size_t)16 * DH;            // one page of one head
-  const size_t kv_stride = (size_t)Hkv * head_stride;     // K part -> V part
-  const uint16_t* lpages = pages + ((size_t)layer * n_pages * 2 * Hkv + kvh) * head_stride;
+  const size_t kv_stride = (size_t)Hkv * 16 * DH;   // K part of a page -> its V part
+  const uint16_t* lpages = pages + ((size_t)layer * n_pages * 2 * Hkv + kvh) * 16 * DH;
   const int ntile = (kend - kbeg + 31) >> 5;
-  // piece i of this thread: key row kr[i] of the tile, dimension offset
-  // d8[i].  Consecutive lanes take consecutive keys, so each transposed V
-  // store (one dimension, 32 keys) fills 64 contiguous bytes of a Vt row and
-  // the two half-waves land 32 banks apart: no LDS bank conflicts.
-  int kr[NPT], d8[NPT];
+  // Sources of this lane's blocks, relative to the page: K blocks hold KPB
+  // key rows, V blocks 16 dimension rows of 4 chunks (8 keys each; chunks
+  // 0-1 from the tile's first page, 2-3 from its second).
+  int src_off[NLW];
+  bool src_second[NLW];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    int c = tid + i * T;
-    c = c < P ? c : P - 1;
-    kr[i] = c % 32;
-    d8[i] = (c / 32) * 8;
+  for (int jj = 0; jj < NLW; ++jj) {
+    const int blk = wave + W * jj;
+    if (blk < NB / 2) {
+      const int R = blk * KPB + lane / CPR;
+      const int c = (lane % CPR) ^ kswz<DH>(R);
+      src_off[jj] = (R & 15) * DH + c * 8;
+      src_second[jj] = R >= 16;
+    } else {
+      const int d = (blk - NB / 2) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ vswz(d);
+      src_off[jj] = (int)kv_stride + d * 16 + (c & 1) * 8;
+      src_second[jj] = c >= 2;
+    }
   }
-  u32x4 rk[PF][NPT], rv[PF][NPT];
-  auto issue = [&](int t, u32x4* k, u32x4* v) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      int key = kbeg + t * 32 + kr[i];
-      key = key < kend ? key : kend - 1;
-      const int pg = pg_s[(key >> 4) - pg0];
-      const uint16_t* base = lpages + (size_t)(pg < 0 ? 0 : pg) * 2 * kv_stride +
-                             (size_t)(key & 15) * DH + d8[i];
-      k[i] = ld16(base);
-      v[i] = ld16(base + kv_stride);
-    }
+  auto page_of = [&](int slot) {   // page-table slot relative to pg0, clamped; bad -> page 0
+    const int pg = pg_s[slot < npg ? slot : npg - 1];
+    return pg < 0 ? 0 : pg;
   };
-  auto store = [&](int t, const u32x4* k, const u32x4* v) {
-    uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])(lds + (t & 1) * (KS_B + VT_B));
-    uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (t & 1) * (KS_B + VT_B) + KS_B);
+  auto issue = [&](int t) {
+    unsigned char* base = lds + (t % NST) * SB;
+    const int slot = 2 * t;   // kbeg is a multiple of 32 keys
+    const size_t p0 = (size_t)page_of(slot) * 2 * kv_stride;
+    const size_t p1 = (size_t)page_of(slot + 1) * 2 * kv_stride;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      // (a piece past P was clamped to piece P-1: it stores the same bytes)
-      const int key = kbeg + t * 32 + kr[i];
-      const int kc = key < kend ? key : kend - 1;
-      const bool ok = (key < kend) & (pg_s[(kc >> 4) - pg0] >= 0);   // no short circuit: no branch
-      const u32x4 vk = ok ? k[i] : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 vv = ok ? v[i] : u32x4{0u, 0u, 0u, 0u};
-      st16(&Ks[kr[i]][d8[i]], vk);
-      const uint16_t* ve = (const uint16_t*)&vv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[d8[i] + e][kr[i]] = ve[e];
-    }
+    for (int jj = 0; jj < NLW; ++jj)
+      __builtin_amdgcn_global_load_lds(
+          (attn_glb_t)(lpages + (src_second[jj] ? p1 : p0) + src_off[jj]),
+          (attn_lds_t)(base + (wave + W * jj) * 1024), 16, 0, 0);
+  };
+  // Stage t is complete for the workgroup once every lane has waited for
+  // its own loads of tile t (at most `later` younger tiles' loads still
+  // outstanding) and the waves have met at a bare s_barrier (the fence of
+  // __syncthreads would also wait for the younger tiles' loads).
+  auto stage_ready = [&](int later) {
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLW) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   f32x4 o[ND];
@@ -228,82 +255,89 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
   const float sl2 = kLog2e / sqrtf((float)DH);
   const int ra = 8 * (lr >> 2) + (lr & 3), rb = ra + 4;
 
-  auto score = [&](int t) {
-    const int t0 = kbeg + t * 32;
-    uint16_t (*Ks)[DH + 8] = (uint16_t (*)[DH + 8])(lds + (t & 1) * (KS_B + VT_B));
-    uint16_t (*Vt)[32 + 8] = (uint16_t (*)[32 + 8])(lds + (t & 1) * (KS_B + VT_B) + KS_B);
+  // The running maximum m_run is kept in raw score units (the scale sl2 > 0
+  // keeps the order) and folded into each exponent with one FMA.
+  auto score = [&](int t, int valid, bool bad0, bool bad1) {
+    const unsigned char* st = lds + (t % NST) * SB;
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const u32x4 ka = ld16(&Ks[ra][i * 32 + lg * 8]), kb2 = ld16(&Ks[rb][i * 32 + lg * 8]);
+      const int c = 4 * i + lg;   // dimensions i*32 + lg*8 .. +7
+      const u32x4 ka = *(const u32x4*)(st + ra * (DH * 2) + ((c ^ kswz<DH>(ra)) << 4));
+      const u32x4 kb2 = *(const u32x4*)(st + rb * (DH * 2) + ((c ^ kswz<DH>(rb)) << 4));
       sa = mfma_16x16x32(ka, qop[i], sa);
       sa = mfma_16x16x32(ka, qlo[i], sa);
       sb = mfma_16x16x32(kb2, qop[i], sb);
       sb = mfma_16x16x32(kb2, qlo[i], sb);
     }
-    // lane (query lr, group lg) now holds keys t0 + 8*lg + 0..7
+    // lane (query lr, group lg) now holds keys 8*lg + 0..7 of the tile
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = sa[r] * sl2;
-      sv[4 + r] = sb[r] * sl2;
+      sv[r] = sa[r];
+      sv[4 + r] = sb[r];
     }
+    if (valid < 32 || bad0 || bad1) {   // uniform: only a split's last tile or a bad page
+      const bool bad = lg < 2 ? bad0 : bad1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (t0 + 8 * lg + e >= kend) sv[e] = -INFINITY;
-    float mt = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+      for (int e = 0; e < 8; ++e)
+        if (bad || 8 * lg + e >= valid) sv[e] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    // while every key so far is masked the maximum stays -inf: using 0 in
+    // the exponents then gives weights exp2(-inf) = 0
+    const float mu = m_new == -INFINITY ? 0.f : m_new * sl2;
+    const float alpha = __builtin_amdgcn_exp2f(m_run * sl2 - mu);   // 1 unless the max grew
     uint32_t pw[4], lw[4];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pa = exp2f(sv[2 * e] - m_new), pb = exp2f(sv[2 * e + 1] - m_new);
+      const float pa = __builtin_amdgcn_exp2f(fmaf(sv[2 * e], sl2, -mu));
+      const float pb = __builtin_amdgcn_exp2f(fmaf(sv[2 * e + 1], sl2, -mu));
       pw[e] = pack_bf2(pa, pb);
       lw[e] = pack_bf2(pa - __uint_as_float(pw[e] << 16), pb - __uint_as_float(pw[e] & 0xFFFF0000u));
       psum += pa + pb;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] *= alpha;
+    }
     const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]}, plo = {lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      o[d] *= alpha;
-      const u32x4 vt = ld16(&Vt[d * 16 + lr][lg * 8]);
+      const int R = d * 16 + lr;
+      const u32x4 vt = *(const u32x4*)(st + KT + R * 64 + ((lg ^ vswz(R)) << 4));
       o[d] = mfma_16x16x32(vt, pop, o[d]);
       o[d] = mfma_16x16x32(vt, plo, o[d]);
     }
   };
 
-  // prologue: tiles 0 .. PF-1 in flight (tiles past the end re-read the
-  // split's last key and are never stored)
-  // (scheduling barriers keep the tiles' loads in issue order, so waiting for
-  // the oldest tile never waits for the younger ones)
-#pragma unroll
-  for (int j = 0; j < PF; ++j) {
-    issue(j, rk[j], rv[j]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Whole groups of PF steps, none of them conditional (a skipped step would
-  // make the compiler assume its loads might be missing and wait longer).
-  // Steps past the last tile see only masked keys and add exactly nothing:
-  // tile 0 always holds a key, so the running maximum is finite by then.
-  for (int t0 = 0; t0 < ntile; t0 += PF) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int t = t0 + j;
-      store(t, rk[j], rv[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(t + PF, rk[j], rv[j]);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int t = 0; t < NST - 1 && t < ntile; ++t) issue(t);
+  for (int t = 0; t < ntile; ++t) {
+    stage_ready(min(ntile - 1 - t, NST - 2));
+    if (t + NST - 1 < ntile) issue(t + NST - 1);
+    const int valid = min(32, kend - (kbeg + 32 * t));
+    const bool bad0 = pg_s[2 * t] < 0, bad1 = valid > 16 && pg_s[2 * t + 1] < 0;
+    if (valid < 32 || bad0 || bad1) {
+      // masked keys (past the split, or in a page outside the pool) get
+      // zero values, so their zero weights never meet stale non-finite bits
+      unsigned char* vt = lds + (t % NST) * SB + KT;
+      for (int e = tid; e < DH * 32; e += 64 * W) {
+        const int d = e >> 5, k = e & 31;
+        if (k >= valid || (k < 16 ? bad0 : bad1))
+          *(uint16_t*)(vt + d * 64 + ((((k >> 3) ^ vswz(d))) << 4) + (k & 7) * 2) = 0;
+      }
       __syncthreads();
-      score(t);
     }
+    if (comp) score(t, valid, bad0, bad1);
   }
+  if (!comp) return;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (lr < gamma) {
@@ -313,7 +347,7 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
 #pragma unroll
       for (int r = 0; r < 4; ++r) po[d * 16 + 4 * lg + r] = o[d][r];
     if (lg == 0) {
-      part_ml[(prow + lr) * 2 + 0] = m_run;
+      part_ml[(prow + lr) * 2 + 0] = m_run * sl2;   // log2 units (-inf stays -inf)
       part_ml[(prow + lr) * 2 + 1] = l_run;
     }
   }
@@ -331,6 +365,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(
   __shared__ float qs[256];
   __shared__ float ps[256];
   __shared__ const float* vrow[256];
+  __shared__ int vstep[256];   // element stride of a value row (transposed pages: page_size)
   __shared__ float red[16];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, B = gridDim.z;
   const int kvh = h / (Hq / Hkv), tid = threadIdx.x;
@@ -346,14 +381,16 @@ __global__ __launch_bounds__(256) void k_attn_f32(
     float sc = -INFINITY;
     const float* kp = nullptr;
     const float* vp = nullptr;
+    int vs = 1;
     if (key < total) {
       if (key < L) {
         const int pi = key / page_size;
         const int pg = pi < max_pages ? page_table[(size_t)b * max_pages + pi] : -1;
         if (pg >= 0 && pg < n_pages) {
-          kp = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride +
-               (size_t)(key % page_size) * dh;
-          vp = kp + kv_stride;
+          const float* page = pages + (((size_t)layer * n_pages + pg) * 2 * Hkv + kvh) * head_stride;
+          kp = page + (size_t)(key % page_size) * dh;
+          vp = page + kv_stride + key % page_size;   // values stored [dh][page_size]
+          vs = page_size;
         } else {
           set_dev_error(err, pi < max_pages ? 1u : 2u);
         }
@@ -368,6 +405,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(
       }
     }
     vrow[tid] = vp;
+    vstep[tid] = vs;
     // chunk maximum
     float mx = sc;
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
@@ -388,7 +426,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(
       float acc = o_acc * alpha;
       const int n = min(256, total - c0);
       for (int t = 0; t < n; ++t)
-        if (ps[t] != 0.f) acc = fmaf(ps[t], vrow[t][tid], acc);
+        if (ps[t] != 0.f) acc = fmaf(ps[t], vrow[t][(size_t)tid * vstep[t]], acc);
       o_acc = acc;
     }
     __syncthreads();
@@ -466,30 +504,23 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   for (int e = 0; e < 4; ++e) Split<BF16>::store(o, o_plane, dst + e, acc[e] * inv);
 }
 
-template <int DH, int NPT, int PF>
-hipError_t run_ctx1(const AttnArgs& a, const AttnPlan& p, dim3 grid, dim3 block, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_bf16<DH, NPT, PF>), grid, block, 0, st, (const uint16_t*)a.q, a.q_plane,
-                     (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages, a.n_pages,
-                     a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv, a.layer, p.chunk,
-                     p.n_ctx_splits, a.part_o, a.part_ml, a.err, a.causal);
+template <int DH, int W, int NST>
+hipError_t run_ctx1(const AttnArgs& a, const AttnPlan& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_ctx<DH, W, NST>), grid, dim3(64 * W), 0, st, (const uint16_t*)a.q,
+                     a.q_plane, (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages,
+                     a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
+                     a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err, a.causal);
   return hipGetLastError();
 }
 
-// Pieces per thread NPT = ceil(32*DH/8 / (64*G)); the prefetch depth PF
-// keeps the load ring at <= 64 VGPRs.  At NPT = 2 (head dim 128, 4 query
-// heads per KV head) a ring of 2 tiles measured faster than 4: the kernel
-// drops from 192 to 157 VGPRs, three workgroups fit a CU instead of two
-// (batch 1: 10.5 -> 9.5 us, batch 32: 119 -> 107 us, 4 x 32K: 154 -> 146 us).
+// W = 4 waves for up to 4 query heads per KV head, else 8; NST stages of
+// 2 * 32 * DH * 2 bytes (head dim 128: 3 stages, 48 KB, three workgroups per
+// CU; head dim 64: 4 stages, 32 KB).
 template <int DH>
-hipError_t run_ctx(const AttnArgs& a, const AttnPlan& p, dim3 grid, dim3 block, hipStream_t st) {
-  const int P = 32 * DH / 8, T = (int)block.x;
-  switch ((P + T - 1) / T) {
-    case 1: return run_ctx1<DH, 1, 4>(a, p, grid, block, st);
-    case 2: return run_ctx1<DH, 2, 2>(a, p, grid, block, st);
-    case 3: return run_ctx1<DH, 3, 2>(a, p, grid, block, st);
-    case 4: return run_ctx1<DH, 4, 2>(a, p, grid, block, st);
-    default: return run_ctx1<DH, 8, 1>(a, p, grid, block, st);
-  }
+hipError_t run_ctx(const AttnArgs& a, const AttnPlan& p, dim3 grid, hipStream_t st) {
+  constexpr int NST = DH == 128 ? 3 : 4;
+  if (a.Hq / a.Hkv <= 4) return run_ctx1<DH, 4, NST>(a, p, grid, st);
+  return run_ctx1<DH, 8, NST>(a, p, grid, st);
 }
 
 }  // namespace
@@ -519,12 +550,11 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
   }
   // splits 0 .. n_ctx_splits-1: cached context; split n_ctx_splits: block keys
   dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
-  dim3 block(64 * (a.Hq / a.Hkv));
   if (a.gamma > 16 || p.chunk > kMaxChunk || p.chunk % 128 || p.n_ctx_splits > kMaxCtxSplits ||
-      a.page_size != 16)
+      a.page_size != 16 || a.Hq % a.Hkv != 0 || a.Hq / a.Hkv > 8 || a.n_pages < 1)
     return hipErrorInvalidValue;
-  if (a.dh == 128) return run_ctx<128>(a, p, grid, block, st);
-  if (a.dh == 64) return run_ctx<64>(a, p, grid, block, st);
+  if (a.dh == 128) return run_ctx<128>(a, p, grid, st);
+  if (a.dh == 64) return run_ctx<64>(a, p, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -291,10 +291,16 @@ __global__ void k_inject_scatter(const float* __restrict__ part, int splits, int
     a = a2;
     c2 = b2;
   }
-  const size_t dst = ((((size_t)layer * n_pages + pg) * 2 + kv) * Hkv + kvh) * page_size * dh +
-                     (size_t)(pos % page_size) * dh;
-  Act<BF16>::store(pages, dst + i, a);
-  Act<BF16>::store(pages, dst + i + half, c2);
+  // K rows are [page_size][dh], values transposed [dh][page_size]
+  const size_t page = ((((size_t)layer * n_pages + pg) * 2 + kv) * Hkv + kvh) * page_size * dh;
+  const int slot = pos % page_size;
+  if (kv == 0) {
+    Act<BF16>::store(pages, page + (size_t)slot * dh + i, a);
+    Act<BF16>::store(pages, page + (size_t)slot * dh + i + half, c2);
+  } else {
+    Act<BF16>::store(pages, page + (size_t)i * page_size + slot, a);
+    Act<BF16>::store(pages, page + (size_t)(i + half) * page_size + slot, c2);
+  }
 }
 
 __global__ void k_advance_ctx(int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_new,

@@ -210,7 +210,7 @@ DF_DEV void epi_swiglu(const SkinnyArgs& a, int S, int tile) {
 }
 
 // Head y of [K^0 | V^0 | K^1 | V^1 | ...] for the inject tokens: RoPE on K at
-// the token's position, store bf16 into its page.
+// the token's position, store bf16 into its page (K row-major, V transposed).
 DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
   const int half = a.dh / 2, quads = half / 4;
   const int kvh = y % a.Hkv, kv = (y / a.Hkv) % 2, layer = y / (2 * a.Hkv);
@@ -233,13 +233,16 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
     const size_t o = (size_t)t * a.N + c0 + i;
     sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + half, x1, x2);
     if (kv == 0) rope4(a.rope + ((size_t)t * half + i) * 2, x1, x2);
+    // K rows are [page_size][dh], values transposed [dh][page_size]
     uint16_t* dst = (uint16_t*)a.pages +
-                    ((((size_t)layer * a.n_pages + pg) * 2 + kv) * a.Hkv + kvh) * a.page_size * a.dh +
-                    (size_t)(pos % a.page_size) * a.dh;
+                    ((((size_t)layer * a.n_pages + pg) * 2 + kv) * a.Hkv + kvh) * a.page_size * a.dh;
+    const int slot = pos % a.page_size;
+    const size_t rs = kv == 0 ? 1 : (size_t)a.page_size;              // step between dimensions
+    dst += kv == 0 ? (size_t)slot * a.dh : (size_t)slot;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dst[i + e] = f2bf(x1[e]);
-      dst[i + e + half] = f2bf(x2[e]);
+      dst[(i + e) * rs] = f2bf(x1[e]);
+      dst[(i + e + half) * rs] = f2bf(x2[e]);
     }
   }
 }

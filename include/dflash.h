@@ -120,7 +120,10 @@ typedef struct {
 /* Paged draft KV cache: the injected target context of every draft layer
  * (paper §4.1: the projected features are stored in the draft model's KV
  * cache and reused across drafting iterations).  Block K/V are never stored.
- *   pages      [n_layers][n_pages][2 (K, V)][n_kv_heads][page_size][head_dim]
+ *   pages      [n_layers][n_pages][2 (K, V)][n_kv_heads][page_size * head_dim]:
+ *              the K half of a page is [page_size][head_dim] (token-major),
+ *              the V half is [head_dim][page_size] (dimension-major), so
+ *              that attention streams both as contiguous blocks
  *   page_table [batch][max_pages_per_seq]: page of tokens
  *              [i*page_size, (i+1)*page_size) of each sequence
  *   ctx_lens   [batch]: tokens already in the cache per sequence; K is

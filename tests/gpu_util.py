@@ -28,6 +28,16 @@ def to_dev(a: np.ndarray, bf16: bool):
     return t.to("cuda")
 
 
+def values_view(pages: np.ndarray) -> np.ndarray:
+    """The value halves of a [layers][pages][2][Hkv][page_size][dh] page
+    array, seen as [layers][pages][Hkv][dh][page_size]: each page stores its
+    values transposed (dimension-major), its keys row-major."""
+    nl, n_pages, _, hkv, ps, dh = pages.shape
+    v = pages[:, :, 1].reshape(nl, n_pages, hkv, dh, ps)
+    assert np.shares_memory(v, pages)
+    return v
+
+
 def to_host(t, bf16: bool) -> np.ndarray:
     import torch
     t = t.detach().to("cpu").contiguous()
@@ -93,7 +103,7 @@ class PagedCache:
         pg = self.table[b][pos // self.s.page_size]
         slot = pos % self.s.page_size
         self.host[:, pg, 0, :, slot, :] = np.transpose(k, (1, 0, 2, 3))
-        self.host[:, pg, 1, :, slot, :] = np.transpose(v, (1, 0, 2, 3))
+        values_view(self.host)[:, pg, :, :, slot] = np.transpose(v, (1, 0, 2, 3))
 
     def upload(self, ctx_lens):
         import torch
@@ -124,7 +134,7 @@ class PagedCache:
         pg = self.table[b][pos // self.s.page_size]
         slot = pos % self.s.page_size
         k = host[:, pg, 0, :, slot, :]   # [n][layers][Hkv][dh]
-        v = host[:, pg, 1, :, slot, :]
+        v = values_view(host)[:, pg, :, :, slot]
         return (np.transpose(host_values(k, self.s.bf16), (1, 0, 2, 3)),
                 np.transpose(host_values(v, self.s.bf16), (1, 0, 2, 3)))
 
