@@ -444,12 +444,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(
 // sequence b; thread t takes row z*R + t / (dh/4) and columns 4 (t % (dh/4))
 // .. +3.  Each thread forms its row's weights 2^(m_s - max) in registers (the
 // threads of a row read the same (max, sum) pairs, which the caches serve)
-// and sums its columns over the parts in part order.  Loads are issued in
-// groups of kCombineGroup parts ahead of the arithmetic, so a thread waits
-// once per group rather than once per part.
-constexpr int kCombineGroup = 8;
-
-template <bool BF16>
+// and sums its columns over the parts in part order.  Up to PG parts
+// (SINGLE) every load is issued before any arithmetic, so a thread waits for
+// memory once; longer part lists run a max pass, then groups of PG parts.
+template <bool BF16, int PG, bool SINGLE>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_parts, int gamma, int Hq, int dh,
@@ -462,23 +460,10 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   const size_t stride = (size_t)B * Hq * gamma;            // partial rows per part
   const size_t pr0 = ((size_t)b * Hq + h) * gamma + j;
   const float2* ml_row = (const float2*)part_ml + pr0;
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < n_parts; s0 += kCombineGroup) {
-    float2 ml[kCombineGroup];
+  // parts s0 .. s0+PG-1 of this thread's row and columns (past the end: empty)
+  auto load = [&](int s0, float2* ml, f32x4* v) {
 #pragma unroll
-    for (int u = 0; u < kCombineGroup; ++u)
-      ml[u] = s0 + u < n_parts ? ml_row[(s0 + u) * stride] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < kCombineGroup; ++u)
-      if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int s0 = 0; s0 < n_parts; s0 += kCombineGroup) {
-    float2 ml[kCombineGroup];
-    f32x4 v[kCombineGroup];
-#pragma unroll
-    for (int u = 0; u < kCombineGroup; ++u) {
+    for (int u = 0; u < PG; ++u) {
       if (s0 + u < n_parts) {
         ml[u] = ml_row[(s0 + u) * stride];
         v[u] = *(const f32x4*)(part_o + (pr0 + (s0 + u) * stride) * dh + d0);
@@ -487,15 +472,45 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
         v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    // an empty part (sum 0) may hold stale values: it is selected away, not
-    // multiplied by a zero weight
+  };
+  float mx = -INFINITY;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  // an empty part (sum 0) may hold stale values: it is selected away, not
+  // multiplied by a zero weight
+  auto accumulate = [&](const float2* ml, const f32x4* v) {
 #pragma unroll
-    for (int u = 0; u < kCombineGroup; ++u) {
+    for (int u = 0; u < PG; ++u) {
       const bool live = ml[u].y > 0.f;
       const float w = live ? exp2f(ml[u].x - mx) : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = live ? acc[e] + w * v[u][e] : acc[e];
       den = live ? den + w * ml[u].y : den;
+    }
+  };
+  if (SINGLE) {
+    float2 ml[PG];
+    f32x4 v[PG];
+    load(0, ml, v);
+#pragma unroll
+    for (int u = 0; u < PG; ++u)
+      if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
+    accumulate(ml, v);
+  } else {
+    for (int s0 = 0; s0 < n_parts; s0 += PG) {
+      float2 ml[PG];
+#pragma unroll
+      for (int u = 0; u < PG; ++u)
+        ml[u] = s0 + u < n_parts ? ml_row[(s0 + u) * stride] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int u = 0; u < PG; ++u)
+        if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
+    }
+    for (int s0 = 0; s0 < n_parts; s0 += PG) {
+      float2 ml[PG];
+      f32x4 v[PG];
+      load(s0, ml, v);
+      accumulate(ml, v);
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -573,11 +588,18 @@ hipError_t launch_attn_combine(bool bf16, const float* part_o, const float* part
   if (rows > gamma) rows = gamma;
   dim3 grid(Hq, batch, (gamma + rows - 1) / rows);
   dim3 block(rows * per);
-  if (bf16)
-    hipLaunchKernelGGL(k_attn_combine<true>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, rows, o, o_plane);
-  else
-    hipLaunchKernelGGL(k_attn_combine<false>, grid, block, 0, st, part_o, part_ml, n_parts, gamma,
-                       Hq, dh, rows, o, o_plane);
+#define DF_COMB(BF, PG, SINGLE)                                                               \
+  hipLaunchKernelGGL((k_attn_combine<BF, PG, SINGLE>), grid, block, 0, st, part_o, part_ml, n_parts, \
+                     gamma, Hq, dh, rows, o, o_plane)
+  if (bf16) {
+    if (n_parts <= 8) DF_COMB(true, 8, true);
+    else if (n_parts <= 24) DF_COMB(true, 24, true);
+    else DF_COMB(true, 8, false);
+  } else {
+    if (n_parts <= 8) DF_COMB(false, 8, true);
+    else if (n_parts <= 24) DF_COMB(false, 24, true);
+    else DF_COMB(false, 8, false);
+  }
+#undef DF_COMB
   return hipGetLastError();
 }
