@@ -249,9 +249,16 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 
 // --------------------------------------------------------------- the kernel
 // grid: (n_tiles rounded up to a multiple of 8) * per workgroups of 256
-// threads, per = tile_groups * S.
+// threads, per = tile_groups * S.  The LM head (SO_ARGMAX) over packed
+// weights: workgroup t takes the gpw consecutive 64-column groups
+// [t * gpw, t * gpw + gpw) as one run of sub-chunks -- their packed tiles are
+// adjacent, so the weight stream continues from group to group as one
+// contiguous chunk and the activations are re-staged from column 0 -- and
+// folds each group's argmax keys into running per-row maxima; n_tiles is then
+// the number of workgroups.  Otherwise gpw = 1.
 template <int MT, int ASRC, int OUT, bool PACKED>
-__global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles) {
+__global__ __launch_bounds__(256, OUT == SO_ARGMAX ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
+                                                   int gpw) {
   constexpr int U = 8 / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
   constexpr bool TWO = ASRC != SA_BF16;   // two planes in LDS
@@ -272,10 +279,10 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   if (tile >= n_tiles) return;
   // queue rotation of the workgroup -> XCD placement (see the publish step)
   const unsigned rot = (OUT != SO_ARGMAX && a.qhint != nullptr) ? (*a.qhint & 7u) : 0u;
-  const int grp = tile * tg + member / S, split = member % S;
+  const int grp = OUT == SO_ARGMAX ? tile * gpw : tile * tg + member / S, split = member % S;
   const int kbeg = split * kps;
   const int M = a.M, N = a.N, K = a.K;
-  const int vcol0 = grp * 64 + wave * 16;                  // virtual column of the wave
+  int vcol0 = grp * 64 + wave * 16;                        // virtual column of the wave
   const bool active = vcol0 < N;
   // Weight rows of this wave: virtual rows vcol0 .. vcol0 + 15.
   //  Plain layout: rows of the segments, 16 contiguous bytes per lane at
@@ -406,12 +413,15 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   // across the barrier, and the MFMAs wait only for their own batch (loads
   // retire in order).  The loads are not predicated (waves past N read a
   // clamped row), so the wait counts stay exact.
-  auto step = [&](auto load_tag, int k, int buf, const u32x4* bw, u32x4* bnext) {
+  const int nsub = kps / KC;   // >= 1 sub-chunks per group
+  auto step = [&](auto load_tag, int J, int buf, const u32x4* bw, u32x4* bnext) {
     constexpr bool LOAD = decltype(load_tag)::value;
     if (LOAD) {
-      fetch(k + KC);
+      // sub-chunk J + 1: its activations at column ((J + 1) mod nsub) * KC,
+      // its weights J + 1 sub-chunks into this workgroup's stream
+      fetch(((J + 1) % nsub) * KC);
 #pragma unroll
-      for (int u = 0; u < U; ++u) bnext[u] = wload(k + KC, u);
+      for (int u = 0; u < U; ++u) bnext[u] = wload((J + 1) * KC, u);
       __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
     }
 #pragma unroll
@@ -433,17 +443,52 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   };
   using Load = std::integral_constant<bool, true>;
   using Last = std::integral_constant<bool, false>;
-  const int nsub = kps / KC;   // >= 1
+  // LM head: argmax keys of the groups done so far, per (row tile, row)
+  uint64_t best[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) best[m][i] = 0;
+  // fold the finished group's columns into best (and store its logits), then
+  // start the next group
+  auto group_end = [&](int J) {
+    if (OUT != SO_ARGMAX || (J + 1) % nsub != 0) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + lg * 4 + i;
+        const int col = vcol0 + lr;
+        if (col < N) {
+          const float v = acc[m][i];
+          const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
+                                                        (uint32_t)(row % a.gamma), (uint32_t)col)
+                                     : v;
+          const uint64_t key = argmax_key(kv, (uint32_t)col);
+          best[m][i] = key > best[m][i] ? key : best[m][i];
+          if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
+        }
+        acc[m][i] = 0.f;
+      }
+    vcol0 += 64;
+  };
+  const int ngrp = OUT == SO_ARGMAX ? min(gpw, (N + 63) / 64 - grp) : 1;
+  const int nj = ngrp * nsub;   // sub-chunks of this workgroup
   int j = 0;
-  for (; j + 2 < nsub; j += 2) {
-    step(Load{}, j * KC, 0, bc, bn);
-    step(Load{}, (j + 1) * KC, 1, bn, bc);
+  for (; j + 2 < nj; j += 2) {
+    step(Load{}, j, 0, bc, bn);
+    group_end(j);
+    step(Load{}, j + 1, 1, bn, bc);
+    group_end(j + 1);
   }
-  if (nsub - j == 2) {
-    step(Load{}, j * KC, 0, bc, bn);
-    step(Last{}, (j + 1) * KC, 1, bn, bc);
+  if (nj - j == 2) {
+    step(Load{}, j, 0, bc, bn);
+    group_end(j);
+    step(Last{}, j + 1, 1, bn, bc);
+    group_end(j + 1);
   } else {
-    step(Last{}, j * KC, 0, bc, bn);
+    step(Last{}, j, 0, bc, bn);
+    group_end(j);
   }
 
   if (OUT == SO_ARGMAX) {
@@ -458,17 +503,7 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + lg * 4 + i;
-        const int col = vcol0 + lr;
-        uint64_t key = 0;
-        if (active && col < N) {
-          const float v = acc[m][i];
-          const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
-                                                        (uint32_t)(row % a.gamma), (uint32_t)col)
-                                     : v;
-          key = argmax_key(kv, (uint32_t)col);
-          if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
-        }
-        key = max16(key);
+        const uint64_t key = max16(best[m][i]);
         if (lr == 0) wkeys[wave][row] = key;
       }
     __syncthreads();
@@ -566,16 +601,26 @@ __global__ __launch_bounds__(256, 4) void k_skinny(SkinnyArgs a, int S, int kps,
   if (OUT == SO_KV) epi_kv(a, S, tile);
 }
 
+// LM head over packed weights: about this many workgroups, each streaming a
+// contiguous run of groups (one long chunk per workgroup keeps HBM pages open
+// and pays the start and publish latency once).
+constexpr int kArgmaxWgTarget = 512;
+
 template <int MT, int ASRC, int OUT>
 hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
   const int per = tile_groups(OUT, a.dh) * p.splits;
+  int gpw = 1;
+  if (OUT == SO_ARGMAX && a.packed != nullptr) {
+    gpw = (n_tiles + kArgmaxWgTarget - 1) / kArgmaxWgTarget;
+    n_tiles = (n_tiles + gpw - 1) / gpw;   // workgroups
+  }
   const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
   if (a.packed != nullptr)
     hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true>), dim3(padded * per), dim3(256), 0, st, a,
-                       p.splits, p.kpw, n_tiles);
+                       p.splits, p.kpw, n_tiles, gpw);
   else
     hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, false>), dim3(padded * per), dim3(256), 0, st, a,
-                       p.splits, p.kpw, n_tiles);
+                       p.splits, p.kpw, n_tiles, gpw);
   return hipGetLastError();
 }
 
