@@ -256,10 +256,10 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 // contiguous chunk and the activations are re-staged from column 0 -- and
 // folds each group's argmax keys into running per-row maxima; n_tiles is then
 // the number of workgroups.  Otherwise gpw = 1.
-template <int MT, int ASRC, int OUT, bool PACKED>
+template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8>
 __global__ __launch_bounds__(256, OUT == SO_ARGMAX ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
                                                    int gpw) {
-  constexpr int U = 8 / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
+  constexpr int U = UW / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
   constexpr bool TWO = ASRC != SA_BF16;   // two planes in LDS
   constexpr int NP = TWO ? 2 : 1;
@@ -615,7 +615,12 @@ hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t 
     n_tiles = (n_tiles + gpw - 1) / gpw;   // workgroups
   }
   const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
-  if (a.packed != nullptr)
+  if (OUT == SO_ARGMAX && MT == 1 && a.packed != nullptr && p.kpw % 512 == 0)
+    // one row tile: 16 blocks (512 columns) of weights per batch, half the
+    // staging rounds and barriers per byte
+    hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16>), dim3(padded * per), dim3(256), 0, st,
+                       a, p.splits, p.kpw, n_tiles, gpw);
+  else if (a.packed != nullptr)
     hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true>), dim3(padded * per), dim3(256), 0, st, a,
                        p.splits, p.kpw, n_tiles, gpw);
   else
