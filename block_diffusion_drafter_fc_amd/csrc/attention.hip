@@ -130,7 +130,8 @@ typedef __attribute__((address_space(3))) void* attn_lds_t;
 typedef __attribute__((address_space(1))) void* attn_glb_t;
 
 template <int DH, int W, int NST>
-__global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void k_attn_ctx(
+// (4 waves: three workgroups per CU by registers; 8 waves: two)
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? 3 : 4))) void k_attn_ctx(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
     const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,

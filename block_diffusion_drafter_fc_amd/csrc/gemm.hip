@@ -373,14 +373,14 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
 
 // ----------------------------------------------------------------------------
 // Large product (M >= 128): 64*WM x BN output tiles (BN = 256, or 192 where
-// 256-column tiles leave CUs idle), 2*WM waves of 64 x BN/2 (wide in N, so
-// that the two activation planes share every weight fragment read from
-// LDS), K in steps of 32 through a ring of LDS stages.  WM = 2: 4
-// waves, one per SIMD, 4 stages, and each wave reads the next step's MFMA
-// fragments while the current step's MFMAs run.  WM = 4: 8 waves, two per
-// SIMD in two groups half a step apart (one group reads fragments while the
-// other runs MFMAs), 3 stages, and the weight tile is shared by 256 rows
-// instead of 128.
+// 256-column tiles leave CUs idle), WM*NWN waves of 64 x BN/NWN (wide in N,
+// so that the two activation planes share every weight fragment read from
+// LDS), K in steps of 32 through a ring of LDS stages.  WM = 2 on 4 waves
+// (one per SIMD, 4 stages): each wave reads the next step's MFMA fragments
+// while the current step's MFMAs run.  8 waves (WM = 4, 3 stages; or WM = 2
+// with NWN = 4 waves of 64 x BN/4 along N, 4 stages): two per SIMD in two
+// groups half a step apart, one group reading fragments while the other runs
+// MFMAs.
 //
 // Loads go straight from global memory to LDS (global_load_lds_dwordx4: lane
 // l of a wave writes its 16 bytes at the instruction's LDS base + 16 l), so
@@ -398,24 +398,25 @@ constexpr int big_stages(int wm) { return wm == 4 ? 3 : 4; }
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* glb_void_t;
 
-template <bool SPLIT, bool ARGMAX, int WM, int BN>
-__global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
+template <bool SPLIT, bool ARGMAX, int WM, int BN, int NWN = 2>
+__global__ __launch_bounds__(64 * WM * NWN, 1) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
     float* __restrict__ logits, DrawArgs dr) {
-  constexpr int BM = 64 * WM, NWAVE = 2 * WM, G = big_stages(WM);
-  constexpr bool DBUF = WM == 2;
+  constexpr int BM = 64 * WM, NWAVE = WM * NWN, G = big_stages(WM);
+  constexpr bool DBUF = NWAVE == 4;            // one wave per SIMD; else two groups
+  constexpr int WCOL = BN / NWN;               // weight columns per wave
   constexpr int NP = SPLIT ? 2 : 1;
   constexpr int RA = NP * BM;                  // A rows per stage
   constexpr int NR = RA + BN;                  // rows per stage
   constexpr int NL = (NR / 16 + NWAVE - 1) / NWAVE;   // load instructions per wave per stage
   constexpr int SB = NL * NWAVE * 1024;        // bytes per stage (blocks past NR: spare)
-  constexpr int NBF = BN / 32;                 // 16-column weight fragments per wave
+  constexpr int NBF = WCOL / 16;               // 16-column weight fragments per wave
   static_assert(NR % 16 == 0 && BN % 64 == 0, "tile rows come in blocks of 16");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[G * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   // Tile order: the dispatcher deals workgroup ids to the 8 XCDs round
   // robin, so ids equal mod 8 share an XCD (whatever XCD the rotation starts
   // at).  Within such a slot consecutive ids take the M tiles of one weight
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
   auto read_frags = [&](Frags& f, int s) {
     const unsigned char* base = lds + (s % G) * SB;
 #pragma unroll
-    for (int b = 0; b < NBF; ++b) f.b[b] = frag(base, RA + wn * (BN / 2) + b * 16 + lr);
+    for (int b = 0; b < NBF; ++b) f.b[b] = frag(base, RA + wn * WCOL + b * 16 + lr);
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
@@ -492,7 +493,9 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
   // loads).  Every wave's fragment reads of the stage that is refilled next
   // have completed: their MFMAs consumed them.
   auto stage_ready = [&](int later) {
-    if (later >= 2)
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NL) : "memory");
+    else if (later == 2)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
     else if (later == 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
@@ -560,16 +563,16 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
         float* dst = part + ((size_t)split * M + row) * N;
 #pragma unroll
         for (int b = 0; b < NBF; ++b) {
-          const int col = n0 + wn * (BN / 2) + b * 16 + lr;
+          const int col = n0 + wn * WCOL + b * 16 + lr;
           if (col < N) dst[col] = acc[a][b][i];
         }
       }
     return;
   }
   // Row argmax over the tile's BN columns: per wave (NBF fragments, then the
-  // 16 lanes of a row), then over the two column halves in LDS.
+  // 16 lanes of a row), then over the NWN column slices in LDS.
   __syncthreads();
-  uint64_t* hkeys = (uint64_t*)lds;   // [2][BM], the stages are no longer read
+  uint64_t* hkeys = (uint64_t*)lds;   // [NWN][BM], the stages are no longer read
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
       uint64_t key = 0;
 #pragma unroll
       for (int b = 0; b < NBF; ++b) {
-        const int col = n0 + wn * (BN / 2) + b * 16 + lr;
+        const int col = n0 + wn * WCOL + b * 16 + lr;
         if (col < N) {
           const float v = acc[a][b][i];
           const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
@@ -595,8 +598,10 @@ __global__ __launch_bounds__(128 * WM, 1) void k_gemm_big(
     }
   __syncthreads();
   if (tid < BM && m0 + tid < M) {
-    const uint64_t k0 = hkeys[tid], k1 = hkeys[BM + tid];
-    best[(size_t)ntile * M + m0 + tid] = k0 > k1 ? k0 : k1;
+    uint64_t k0 = hkeys[tid];
+#pragma unroll
+    for (int x = 1; x < NWN; ++x) k0 = hkeys[x * BM + tid] > k0 ? hkeys[x * BM + tid] : k0;
+    best[(size_t)ntile * M + m0 + tid] = k0;
   }
 }
 
@@ -651,36 +656,42 @@ hipError_t run_skinny(const GemmPlan& p, const void* A, const void* Alo, int lda
   return hipGetLastError();
 }
 
-// Tile height and K splits of the large product, from a cost model fitted
-// to measurements on the Qwen3-8B shapes: a round of up to 256 workgroups
-// (one per CU) costs steps/S * t_step plus ~11 us of fixed cost (filling the
-// stage ring, writing the tile, dispatch), with t_step ~1.1 us for the 4-wave
-// 128-row tile and ~1.45 us for the 8-wave 256-row tile (split activations,
-// 256 weight columns; proportionally less for 192);
-// each extra partial slice costs its write-back and the reducer's read
-// (2 * M * N * 4 bytes at ~5 TB/s).  Splits keep an even number of >= 4 steps.
+// Tile height, waves, width and K splits of the large product, from a cost
+// model fitted to measurements: a round of up to 256 workgroups (one per CU)
+// costs steps/S K steps plus a fixed cost (filling the stage ring, writing the
+// tile, dispatch); each extra partial slice costs its write-back and the
+// reducer's read (2 * M * N * 4 bytes at ~5 TB/s).  Splits keep an even
+// number of >= 4 steps.
+// Per round: steps/S * t_step * BN/256 + fixed (us), least-squares fits to a
+// sweep of every configuration on the Qwen3-8B and wide-drafter product shapes
+// at 128, 256 and 512 rows (random bf16 data): 128-row tile on 4 waves, on 8
+// waves, 256-row tile on 8 waves.
+constexpr double kBigStep[3] = {0.885, 0.719, 1.021};
+constexpr double kBigFixed[3] = {10.8, 11.6, 16.8};
+
 struct BigChoice {
-  int wm, splits, bn;
+  int wm, splits, bn, waves;
 };
 
 BigChoice big_plan(int M, int N, int K, bool argmax) {
-  BigChoice best{2, 1, GBN};
+  BigChoice best{2, 1, GBN, 4};
   double best_cost = 1e300;
   const int steps = K / GBK;
   for (int bn = GBN; bn >= 192; bn -= 64) {
     if (argmax && bn != GBN) continue;
     const long ntiles = (N + bn - 1) / bn;
-    for (int wm = 2; wm <= 4; wm += 2) {
+    for (int v = 0; v < 3; ++v) {   // (tile height, waves): (128, 4), (128, 8), (256, 8)
+      const int wm = v == 2 ? 4 : 2, waves = v == 0 ? 4 : 8;
       const long tiles = (long)((M + 64 * wm - 1) / (64 * wm)) * ntiles;
-      const double t_step = (wm == 4 ? 1.45 : 1.1) * bn / GBN;
+      const double t_step = kBigStep[v] * bn / GBN, fixed = kBigFixed[v];
       for (int S = 1; S <= (argmax ? 1 : 16); ++S) {
         if (steps % S || (steps / S) % 2 || steps / S < 4) continue;
         const double rounds = (double)((tiles * S + 255) / 256);
-        const double cost = rounds * ((double)(steps / S) * t_step + 11.0) +
+        const double cost = rounds * ((double)(steps / S) * t_step + fixed) +
                             (double)(S - 1) * M * (double)N * 8.0 / 5e6;
         if (cost < best_cost) {
           best_cost = cost;
-          best = BigChoice{wm, S, bn};
+          best = BigChoice{wm, S, bn, waves};
         }
       }
     }
@@ -736,6 +747,7 @@ GemmPlan plan_gemm(bool bf16, int M, int N, int K, bool argmax) {
     const BigChoice c = big_plan(M, N, K, argmax);
     p.mt = c.wm;
     p.nt = c.bn;
+    p.waves = c.waves;
     p.splits = c.splits;
     p.kpw = K / p.splits;
     return p;
@@ -791,26 +803,29 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
   }
   if (p.kind == GEMM_BIG) {
     if ((p.mt != 2 && p.mt != 4) || (p.nt != GBN && (p.nt != 192 || best)) ||
-        p.kpw % (2 * GBK) != 0 || (long)p.kpw * p.splits != K || lda % 8 != 0)
+        (p.waves != 2 * p.mt && !(p.mt == 2 && p.waves == 8)) || p.kpw % (2 * GBK) != 0 ||
+        (long)p.kpw * p.splits != K || lda % 8 != 0)
       return hipErrorInvalidValue;
     const int bm = 64 * p.mt;
     dim3 grid(((N + p.nt - 1) / p.nt + 7) / 8 * 8 * ((M + bm - 1) / bm), 1, p.splits);
     const uint16_t* a = (const uint16_t*)A;
     const uint16_t* al = (const uint16_t*)Alo;
-#define DF_BIG(SPL, AM, WM, BN)                                                              \
-  hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM, BN>), grid, dim3(128 * WM), 0, st, a, al, lda, M, \
-                     w, N, K, p.kpw, part, best, logits, dr)
-#define DF_BIG2(WM)                                       \
-  if (al && best) DF_BIG(true, true, WM, GBN);             \
-  else if (best) DF_BIG(false, true, WM, GBN);             \
-  else if (al && p.nt == GBN) DF_BIG(true, false, WM, GBN); \
-  else if (al) DF_BIG(true, false, WM, 192);               \
-  else if (p.nt == GBN) DF_BIG(false, false, WM, GBN);     \
-  else DF_BIG(false, false, WM, 192)
+#define DF_BIG(SPL, AM, WM, BN, NWN)                                                          \
+  hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM, BN, NWN>), grid, dim3(64 * WM * NWN), 0, st, a, al, \
+                     lda, M, w, N, K, p.kpw, part, best, logits, dr)
+#define DF_BIG2(WM, NWN)                                       \
+  if (al && best) DF_BIG(true, true, WM, GBN, NWN);             \
+  else if (best) DF_BIG(false, true, WM, GBN, NWN);             \
+  else if (al && p.nt == GBN) DF_BIG(true, false, WM, GBN, NWN); \
+  else if (al) DF_BIG(true, false, WM, 192, NWN);               \
+  else if (p.nt == GBN) DF_BIG(false, false, WM, GBN, NWN);     \
+  else DF_BIG(false, false, WM, 192, NWN)
     if (p.mt == 4) {
-      DF_BIG2(4);
+      DF_BIG2(4, 2);
+    } else if (p.waves == 8) {
+      DF_BIG2(2, 4);
     } else {
-      DF_BIG2(2);
+      DF_BIG2(2, 2);
     }
 #undef DF_BIG2
 #undef DF_BIG
