@@ -9,8 +9,8 @@ tests; a block's loss within twice the logits tolerance plus 1e-5 relative
 
 Covers: blocks at anchor position 0 (no context) and at the full context,
 unsorted anchor positions, both the fused (<= 64 rows) and the plain
-(> 64 rows) draft paths, the 256-row product kernel (24 blocks of 16 on the
-Qwen3-8B shape), fp32 and bf16 models, and the device error for an anchor
+(> 64 rows) draft paths, the large-product kernel (8 and 24 blocks of 16 on
+the Qwen3-8B shape), fp32 and bf16 models, and the device error for an anchor
 past the context."""
 import numpy as np
 import pytest
@@ -98,7 +98,9 @@ def test_packed_mini_bf16(n_blocks):
     check_against_oracle(s, L, ap, 16, 7.0, res)
 
 
-@pytest.mark.parametrize("n_blocks", [4, 24])    # 64 rows fused; 384 rows on the large-product kernel
+# 64 rows fused; 128 rows on the large-product kernel's 8-wave 128-row tile;
+# 384 rows on its other tiles
+@pytest.mark.parametrize("n_blocks", [4, 8, 24])
 def test_packed_qwen3_8b(n_blocks):
     s = CONFIGS[2]
     L = 2048
