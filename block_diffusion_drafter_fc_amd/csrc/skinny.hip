@@ -257,7 +257,7 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 // folds each group's argmax keys into running per-row maxima; n_tiles is then
 // the number of workgroups.  Otherwise gpw = 1.
 template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8>
-__global__ __launch_bounds__(256, OUT == SO_ARGMAX ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
+__global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
                                                    int gpw) {
   constexpr int U = UW / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
@@ -615,9 +615,13 @@ hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t 
     n_tiles = (n_tiles + gpw - 1) / gpw;   // workgroups
   }
   const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
-  if (OUT == SO_ARGMAX && MT == 1 && a.packed != nullptr && p.kpw % 512 == 0)
-    // one row tile: 16 blocks (512 columns) of weights per batch, half the
-    // staging rounds and barriers per byte
+  // 16 weight blocks per batch (512 columns at one row tile): half the
+  // staging rounds and barriers per byte, at two workgroups per CU.  The LM
+  // head always; with 2 or 4 row tiles also the unpaired products (at one row
+  // tile they measured slower, and the paired ones at 640+ workgroups would
+  // no longer fit one round).
+  if ((OUT == SO_ARGMAX || (MT > 1 && OUT != SO_SWIGLU && OUT != SO_KV)) && a.packed != nullptr &&
+      p.kpw % (32 * 16 / MT) == 0)
     hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16>), dim3(padded * per), dim3(256), 0, st,
                        a, p.splits, p.kpw, n_tiles, gpw);
   else if (a.packed != nullptr)
