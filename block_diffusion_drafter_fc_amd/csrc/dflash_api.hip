@@ -780,7 +780,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
   }
 
   const GemmPlan p = plan_gemm(bf, M, d.V, d.D, true);
-  // On the large-product kernel (>= 256 rows, MFMA-bound) the LM head takes
+  // On the large-product kernel (>= 128 rows, MFMA-bound) the LM head takes
   // its input in bf16, the workload's activation precision, which halves its
   // matrix-core work: the hi plane alone is the bf16 rounding of the fp32
   // row.  The lo plane carries the layers' fp32 activations; the LM head is
