@@ -92,6 +92,26 @@ __global__ __launch_bounds__(kRowThreads) void k_rmsnorm(const float* __restrict
 constexpr int kResThreads = 1024;
 constexpr int kResMaxPass = 2;   // D <= 8192
 
+// Four consecutive values (element i, a multiple of 4) to split planes
+// (bf16 models: hi and lo, one 8-byte store each) or fp32 (one 16-byte store).
+template <bool BF16>
+DF_DEV void store4(void* base, size_t plane, size_t i, const f32x4& v) {
+  if (BF16) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      h[e] = pack_bf2(v[2 * e], v[2 * e + 1]);
+      l[e] = pack_bf2(v[2 * e] - __uint_as_float(h[e] << 16),
+                      v[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
+    }
+    uint16_t* hi = (uint16_t*)base;
+    *(uint2*)&hi[i] = make_uint2(h[0], h[1]);
+    *(uint2*)&hi[plane + i] = make_uint2(l[0], l[1]);
+  } else {
+    *(f32x4*)&((float*)base)[i] = v;
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict__ x,
                                                                const float* __restrict__ part,
@@ -122,11 +142,12 @@ __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict
 #pragma unroll
   for (int p = 0; p < kResMaxPass; ++p) {
     const int d = (p * kResThreads + threadIdx.x) * 4;
-    if (d < D)
+    if (d < D) {
+      f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Split<BF16>::store(y, y_plane, (size_t)r * D + d + e,
-                           v[p][e] * inv * Act<BF16>::load(g, d + e));
+      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * Act<BF16>::load(g, d + e);
+      store4<BF16>(y, y_plane, (size_t)r * D + d, o);
+    }
   }
 }
 
@@ -240,10 +261,12 @@ __global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __rest
 #pragma unroll
   for (int p = 0; p < kResMaxPass; ++p) {
     const int d = (p * kResThreads + threadIdx.x) * 4;
-    if (d < D)
+    if (d < D) {
+      f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Split<BF16>::store(c, c_plane, (size_t)t * D + d + e, v[p][e] * inv * Act<BF16>::load(g, d + e));
+      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * Act<BF16>::load(g, d + e);
+      store4<BF16>(c, c_plane, (size_t)t * D + d, o);
+    }
   }
 }
 
