@@ -189,21 +189,31 @@ __global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M
   }
 }
 
-// h = silu(gate) * up, gate = columns [0, I), up = columns [I, 2I).
-template <bool BF16>
+// h = silu(gate) * up, gate = columns [0, I), up = columns [I, 2I).  VEC
+// (I % 4 == 0): four columns per thread, 16-byte loads, one store per plane.
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, int splits, int M,
                                                 int I, void* __restrict__ h, size_t h_plane) {
-  const int r = blockIdx.y, c = blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int C = VEC ? 4 : 1;
+  const int r = blockIdx.y, c = (blockIdx.x * blockDim.x + threadIdx.x) * C;
   if (c >= I) return;
-  float gt = 0.f, up = 0.f;
+  f32x4 gt = {0.f, 0.f, 0.f, 0.f}, up = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float* p = part + ((size_t)s * M + r) * (2 * (size_t)I);
-    gt += p[c];
-    up += p[I + c];
+    if (VEC) {
+      gt += *(const f32x4*)&p[c];
+      up += *(const f32x4*)&p[I + c];
+    } else {
+      gt[0] += p[c];
+      up[0] += p[I + c];
+    }
   }
-  const float sg = gt / (1.0f + expf(-gt));
-  Split<BF16>::store(h, h_plane, (size_t)r * I + c, sg * up);
+  f32x4 o;
+#pragma unroll
+  for (int e = 0; e < C; ++e) o[e] = gt[e] / (1.0f + expf(-gt[e])) * up[e];
+  if (VEC) store4<BF16>(h, h_plane, (size_t)r * I + c, o);
+  else Split<BF16>::store(h, h_plane, (size_t)r * I + c, o[0]);
 }
 
 // Row r of the block: the anchor for j == 0, else the column of the largest
@@ -478,11 +488,16 @@ hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, 
 
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
                          size_t h_plane, hipStream_t st) {
-  dim3 grid((I + 255) / 256, M);
-  if (bf16)
-    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
+  const bool vec = I % 4 == 0 && h_plane % 4 == 0;
+  dim3 grid((I / (vec ? 4 : 1) + 255) / 256, M);
+  if (bf16 && vec)
+    hipLaunchKernelGGL((k_swiglu<true, true>), grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
+  else if (bf16)
+    hipLaunchKernelGGL((k_swiglu<true, false>), grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
+  else if (vec)
+    hipLaunchKernelGGL((k_swiglu<false, true>), grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
   else
-    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
+    hipLaunchKernelGGL((k_swiglu<false, false>), grid, dim3(256), 0, st, part, splits, M, I, h, h_plane);
   return hipGetLastError();
 }
 
