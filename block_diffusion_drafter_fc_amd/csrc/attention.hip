@@ -127,7 +127,22 @@ DF_DEV int kswz(int R) {
 DF_DEV int vswz(int R) { return (R >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void* attn_lds_t;
-typedef __attribute__((address_space(1))) void* attn_glb_t;
+
+// One direct-to-LDS load: the wave's 64 lanes each move 16 bytes from `src`
+// to LDS address lds_base + 16 lane (lds_base wave-uniform, in M0).  Issued
+// as inline assembly so that the compiler does not track the LDS write:
+// given a load it cannot tell apart from the stage being read, it would wait
+// for every load in flight before each LDS read and serialise the ring.  The
+// caller orders reads after these loads itself (vmcnt wait, then s_barrier).
+DF_DEV void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
 
 template <int DH, int W, int NST>
 // (4 waves: three workgroups per CU by registers; 8 waves: two)
@@ -230,9 +245,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
     const size_t p1 = (size_t)page_of(slot + 1) * 2 * kv_stride;
 #pragma unroll
     for (int jj = 0; jj < NLW; ++jj)
-      __builtin_amdgcn_global_load_lds(
-          (attn_glb_t)(lpages + (src_second[jj] ? p1 : p0) + src_off[jj]),
-          (attn_lds_t)(base + (wave + W * jj) * 1024), 16, 0, 0);
+      lds_dma16(lpages + (src_second[jj] ? p1 : p0) + src_off[jj],
+                (uint32_t)(size_t)(attn_lds_t)(base + (wave + W * jj) * 1024));
   };
   // Stage t is complete for the workgroup once every lane has waited for
   // its own loads of tile t (at most `later` younger tiles' loads still
@@ -319,6 +333,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
     }
   };
 
+  // The Q fragments must be in registers before the ring starts: the
+  // compiler does not count the ring's loads, and a wait of its own for Q
+  // placed inside the loop would also wait for every tile in flight.
+#pragma unroll
+  for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(qop[i]), "v"(qlo[i]));
   for (int t = 0; t < NST - 1 && t < ntile; ++t) issue(t);
   for (int t = 0; t < ntile; ++t) {
     stage_ready(min(ntile - 1 - t, NST - 2));
