@@ -128,6 +128,17 @@ DF_DEV int vswz(int R) { return (R >> 1) & 3; }
 
 typedef __attribute__((address_space(3))) void* attn_lds_t;
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 of the wave, with the
+// VALU row swaps (16-lane rows, then 32-lane halves) instead of two LDS
+// permutes: each swap hands every lane the value of its partner row, so the
+// max of the two returned halves is max(x[l], x[partner]).
+DF_DEV float wave_max_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 // One direct-to-LDS load: the wave's 64 lanes each move 16 bytes from `src`
 // to LDS address lds_base + 16 lane (lds_base wave-uniform, in M0).  Issued
 // as inline assembly so that the compiler does not track the LDS write:
@@ -300,8 +311,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
     }
     float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = wave_max_xor16_32(mt);
     const float m_new = fmaxf(m_run, mt);
     // while every key so far is masked the maximum stays -inf: using 0 in
     // the exponents then gives weights exp2(-inf) = 0
