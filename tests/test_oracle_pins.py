@@ -177,6 +177,38 @@ def test_inject_fuses_feature_blocks_in_order(which):
             assert np.array_equal(v[t, l].reshape(-1), c[(1 - l) * KV:(2 - l) * KV])
 
 
+def test_inject_rounds_the_fused_context_to_bf16_before_projecting():
+    # Paper §7.3 sizes the fc output at two bytes per value, so in bf16 mode
+    # c is rounded before W_K/W_V.  With W_c selecting the first feature and
+    # a key that adds two entries of c, k_j = bf16(bf16(c_j) + bf16(c_j+16)):
+    # rounding only the stored key would give bf16(c_j + c_j+16).
+    s = tiny(bf16=True)
+    D, KV = s.hidden, s.n_kv_heads * s.head_dim
+    one = np.uint16(0x3F80)
+    w = make_weights(s)
+    fc = np.zeros((D, 5 * D), np.uint16)
+    fc[np.arange(D), np.arange(D)] = one
+    w["fc_w"] = fc
+    for l in range(s.n_layers):
+        wk = np.zeros((KV, D), np.uint16)
+        wk[np.arange(KV), np.arange(KV)] = one
+        wk[np.arange(KV), KV + np.arange(KV)] = one
+        w[f"l{l}.wk"] = wk
+    hid = hidden_states(s, 0, 0, 4)
+    k, _ = oracle.Model(s, w).inject(hid, np.zeros(4, np.int32))   # position 0: no rotation
+    gain = (w["fc_norm"].astype(np.uint32) << 16).view(np.float32)
+    f1 = (hid[:, :D].astype(np.uint32) << 16).view(np.float32)
+    differs = 0
+    for t in range(4):
+        c = oracle.rmsnorm(f1[t], gain, s.eps)
+        cr = oracle.round_bf16(c)
+        expect = oracle.round_bf16(cr[:KV] + cr[KV:2 * KV])
+        for l in range(s.n_layers):
+            assert np.array_equal(k[t, l].reshape(-1), expect)
+        differs += int(np.sum(expect != oracle.round_bf16(c[:KV] + c[KV:2 * KV])))
+    assert differs > 0          # the construction tells the two readings apart
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_inject_is_per_token_chunk_invariant(bf16):
     s = tiny(bf16=bf16)
@@ -313,6 +345,91 @@ def test_argmax_ties_resolve_to_the_lowest_index():
     assert oracle.argmax([1.0, 3.0, 3.0, 2.0]) == 1
     assert oracle.argmax([-1.0, -1.0]) == 0
     assert oracle.argmax([0.0, 0.0, 5.0, 5.0, 5.0]) == 2
+
+
+def test_argmax_signed_zeros_tie_and_take_the_lowest_index():
+    # -0.0 == +0.0, so whichever comes first wins
+    assert oracle.argmax([-1.0, -0.0, 0.0, -2.0]) == 1
+    assert oracle.argmax([-1.0, 0.0, -0.0, -2.0]) == 1
+    tgt = np.full((2, 6), 0xBF80, np.uint16)     # bf16 -1.0
+    tgt[0, [2, 4]] = [0x8000, 0x0000]            # -0.0 before +0.0
+    tgt[1, [1, 3]] = [0x0000, 0x8000]
+    tau, out, T = oracle.verify(np.array([9, 2], np.int32), tgt, True)
+    assert list(T) == [2, 1] and tau == 2 and list(out) == [2, 1]
+
+
+# ------------------------------------------------- norm gains and their wiring
+# A zero RMSNorm gain zeroes exactly what that norm feeds, so each gain can be
+# tied to its sub-layer by an independent construction: zeroing the gain must
+# give bit for bit what zeroing that sub-layer's output projection gives.  A
+# gain wired to the wrong sub-layer (or layer) breaks the equality.
+
+def _draft_with(s, w, L, toks):
+    m = oracle.Model(s, w)
+    ck, cv = context_kv(s, 0, max(L, 1))
+    return m.draft(ck, cv, L, toks)
+
+
+def _zero(a):
+    return np.zeros_like(a)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_attention_norm_gain_feeds_only_the_attention_sublayer(bf16, layer):
+    # Empty context: with a zero input the block queries/keys/values are zero,
+    # the attention output is the mean of zero values, and the sub-layer adds
+    # nothing -- exactly as with W_O = 0.
+    s = tiny(bf16=bf16)
+    toks = np.array([11, 63, 63, 63], np.int32)
+    w = make_weights(s)
+    a = dict(w)
+    a[f"l{layer}.attn_norm"] = _zero(w[f"l{layer}.attn_norm"])
+    b = dict(w)
+    b[f"l{layer}.wo"] = _zero(w[f"l{layer}.wo"])
+    la, _ = _draft_with(s, a, 0, toks)
+    lb, _ = _draft_with(s, b, 0, toks)
+    ln, _ = _draft_with(s, w, 0, toks)
+    assert np.array_equal(la, lb)
+    assert np.max(np.abs(la - ln)) > 1e-6      # the sub-layer did contribute
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_mlp_norm_gain_feeds_only_the_mlp_sublayer(bf16, layer):
+    s = tiny(bf16=bf16)
+    toks = np.array([29, 63, 63, 63], np.int32)
+    w = make_weights(s)
+    a = dict(w)
+    a[f"l{layer}.mlp_norm"] = _zero(w[f"l{layer}.mlp_norm"])
+    b = dict(w)
+    b[f"l{layer}.w_down"] = _zero(w[f"l{layer}.w_down"])
+    la, _ = _draft_with(s, a, 7, toks)
+    lb, _ = _draft_with(s, b, 7, toks)
+    ln, _ = _draft_with(s, w, 7, toks)
+    assert np.array_equal(la, lb)
+    assert np.max(np.abs(la - ln)) > 1e-6
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_final_norm_gain_feeds_the_lm_head(bf16):
+    s = tiny(bf16=bf16)
+    toks = np.array([40, 63, 63, 63], np.int32)
+    w = make_weights(s)
+    w["final_norm"] = _zero(w["final_norm"])
+    logits, block = _draft_with(s, w, 5, toks)
+    assert np.all(logits == 0.0)
+    assert list(block) == [40, 0, 0, 0]        # all-zero rows: the lowest index
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fc_norm_gain_feeds_the_injected_keys_and_values(bf16):
+    s = tiny(bf16=bf16)
+    w = make_weights(s)
+    w["fc_norm"] = _zero(w["fc_norm"])
+    hid = hidden_states(s, 0, 0, 6)
+    k, v = oracle.Model(s, w).inject(hid, np.arange(6, dtype=np.int32))
+    assert np.all(k == 0.0) and np.all(v == 0.0)
 
 
 # ------------------------------------------------------------------- verify
