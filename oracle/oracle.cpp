@@ -12,15 +12,16 @@
 // changes the order of the additions inside one output.
 //
 // Precision.  Weights, the target's hidden states and the draft K/V cache are
-// stored in the model dtype.  In bf16 mode the only value the method itself
-// rounds is what it stores: the context keys and values written into the
-// cache by the injection (round to nearest, ties to even).  Every transient
-// value of a pass -- the fused context, norms, q/k/v of the block, attention
-// weights and outputs, the SwiGLU product, the residual stream, the logits --
-// stays in double.  (The pages fix bf16 for the weights and for the stored
-// context activations -- paper §7.3, "KV Injection Mechanism and Memory
-// Overhead" -- and say nothing of the transient activations.)  In fp32 mode
-// nothing is rounded.
+// stored in the model dtype.  In bf16 mode the method rounds (to nearest,
+// ties to even) the two context activations the paper sizes at two bytes per
+// element: the fused context c = RMSNorm(W_c f), the fc's output, and the
+// context keys and values stored in the cache (paper §7.3, "KV Injection
+// Mechanism and Memory Overhead": the projection's output at batch 1 and
+// 2048 tokens is counted at 8 MB, i.e. D = 2048 values of 2 bytes per token).
+// Every transient value of a draft pass -- norms, q/k/v of the block,
+// attention weights and outputs, the SwiGLU product, the residual stream,
+// the logits -- stays in double: the pages say nothing of their precision.
+// In fp32 mode nothing is rounded.
 //
 // Sources (titles of the pages the method is described on):
 //   [S] "DFlash: Block Diffusion for Flash Speculative Decoding", the
@@ -250,6 +251,8 @@ void oracle_inject(const oracle_dims* d, const oracle_weights* w,
   for (int t = 0; t < n_tok; ++t) {
     oracle_rmsnorm(&u[(size_t)t * D], D, w->fc_norm, d->bf16, d->eps, &c[(size_t)t * D]);
   }
+  // c is held in the model dtype (bf16: rounded), like the cache it feeds
+  for (size_t i = 0; i < (size_t)n_tok * D; ++i) c[i] = rnd(d, c[i]);
   std::vector<double> kk((size_t)n_tok * KV), vv((size_t)n_tok * KV);
   for (int l = 0; l < NL; ++l) {
     matvec_rows(w->wk[l], d->bf16, KV, D, c.data(), n_tok, kk.data());
