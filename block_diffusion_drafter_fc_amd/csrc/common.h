@@ -82,9 +82,12 @@ DF_DEV u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 DF_DEV u32x4 ld16_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 DF_DEV void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
-// Order-preserving map of an fp32 value onto uint32 (finite inputs).
+// Order-preserving map of an fp32 value onto uint32 (finite inputs).  -0.0
+// maps to the key of +0.0: the two compare equal, so a tie between them goes
+// to the lower index like any other tie.
 DF_DEV uint32_t f32_order(float f) {
   uint32_t u = __float_as_uint(f);
+  u = (u << 1) ? u : 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

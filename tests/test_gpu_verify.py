@@ -1,6 +1,7 @@
 """Greedy verification on the GPU vs the oracle: bit-exact accepted lengths,
 output tokens and target argmax tokens, on all five workloads and on edge
-cases (block of one, ties, vocab sizes off the vector width, fp32 scores)."""
+cases (block of one, ties, ties between -0.0 and +0.0, vocab sizes off the
+vector width, fp32 scores)."""
 import numpy as np
 import pytest
 
@@ -82,3 +83,26 @@ def test_verify_large_batch_bf16():
     tau = g.uniform_int("tau", B, 1, gamma)
     tgt = g.plant_target("t", blocks, tau, V, dtype="bf16")
     compare(blocks, tgt, True, tau)
+
+
+@pytest.mark.parametrize("bf16,V", [(True, 20000), (True, 20003), (False, 20004), (False, 20003)])
+def test_verify_signed_zero_ties_take_the_lower_index(bf16, V):
+    # -0.0 and +0.0 are equal scores, so the lower index wins whichever sign
+    # it carries: within one 16-byte load, within one argmax chunk (8192
+    # columns), and across chunks; on the vector and the scalar load paths.
+    # The rest of each row is -1.
+    gamma = 6
+    neg, pos, minus_one = (0x8000, 0x0000, 0xBF80) if bf16 else (-0.0, 0.0, -1.0)
+    dt = np.uint16 if bf16 else np.float32
+    pairs = [(100, 200, neg, pos), (5, 6, pos, neg), (30, 19000, pos, neg),
+             (7, 15000, neg, pos), (2, 3, neg, pos), (16390, 16391, neg, pos)]
+    tgt = np.full((2, gamma, V), minus_one, dt)
+    for j, (lo, hi, a, b) in enumerate(pairs):
+        tgt[:, j, lo], tgt[:, j, hi] = a, b
+    T = [lo for lo, _, _, _ in pairs]
+    blocks = np.array([[9] + T[:5], [9] + T[:2] + [11, 12, 13]], np.int32)
+    acc = compare(blocks, tgt, bf16)
+    assert list(acc) == [6, 3]
+    _, out, ta = run_verify(blocks, tgt, bf16)
+    assert list(ta[0]) == T and list(out[0]) == T
+    assert list(out[1]) == T[:3] + [-1, -1, -1]
