@@ -187,6 +187,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
   const bool comp = wave < G;
   const int h = kvh * G + (comp ? wave : 0);
   const int L = ctx_lens[b];
+  // The splits cover the page table's capacity; a longer context (or a
+  // negative one) cannot be read whole: report it.
+  if (s == 0 && kvh == 0 && tid == 0 && (L < 0 || L > max_pages * 16)) set_dev_error(err, 2u);
   const int kbeg = s * chunk;
   const int kend = min(kbeg + chunk, L);
   const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0

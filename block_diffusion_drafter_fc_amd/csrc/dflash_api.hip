@@ -19,7 +19,8 @@ struct dflash_model {
   unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
   unsigned long long* amax;  // LM-head argmax slots and their counter (same buffer)
   unsigned long long* actr;
-  uint32_t* qhint;           // workgroup -> XCD rotation of the last split-K launch (same buffer)
+  uint32_t* qhint;           // two words: workgroup -> XCD rotation seen by split-K launches
+  mutable uint32_t hint_seq; // split-K launches so far: selects the word a launch reads
   const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
   int device;
   bool bf16;
@@ -88,8 +89,9 @@ size_t part_floats(bool bf16, int M, int N, int K) {
   return best;
 }
 
-// State buffer: the error word; at 128 the workgroup -> XCD rotation the last
-// split-K launch observed; then the LM-head argmax slots [8 XCDs][64 rows]
+// State buffer: the error word; at 128 two words holding the workgroup ->
+// XCD rotation observed by split-K launches (each launch reads one and writes
+// the other, so all workgroups of a launch read the same value); then the LM-head argmax slots [8 XCDs][64 rows]
 // and their arrival counter, then one arrival counter per output tile of a
 // fused product.  Every call leaves the slots and counters at zero.
 constexpr size_t kQhintOffset = 128;
@@ -113,6 +115,20 @@ bool use_fused(const dflash_model* m, int M) {
   for (int t : tiles)
     if (t < 0 || t > kMaxCounters) return false;
   return true;
+}
+
+// Launch a fused product.  Split-K launches alternate between the two hint
+// words: launch n reads word n mod 2 (written by launch n - 1) and its
+// workgroup 0 writes word (n + 1) mod 2, which no workgroup of launch n reads.
+hipError_t run_skinny(const dflash_model* m, const GemmPlan& p, int asrc, int out, SkinnyArgs a,
+                      hipStream_t st) {
+  if (out != SO_ARGMAX) {
+    const uint32_t r = m->hint_seq & 1u;
+    a.qhint_rd = m->qhint + r;
+    a.qhint_wr = m->qhint + (r ^ 1u);
+    ++m->hint_seq;
+  }
+  return launch_skinny(p, asrc, out, a, st);
 }
 
 size_t skinny_part_floats(int M, int N, int K, int out, int dh) {
@@ -346,6 +362,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->amax = (unsigned long long*)((char*)state + kAmaxOffset);
   m->actr = (unsigned long long*)((char*)state + kActrOffset);
   m->qhint = (uint32_t*)((char*)state + kQhintOffset);
+  m->hint_seq = 0;
   m->packed = nullptr;
   m->device = dev;
   m->bf16 = cfg->dtype == DFLASH_BF16;
@@ -435,8 +452,6 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   char* ws = (char*)workspace;
   float* part = (float*)(ws + L.part);
   void* c = ws + L.c;
-  const size_t c_plane = (size_t)n_tok * d.D;
-  const void* c_lo = bf ? (const void*)((const uint16_t*)c + c_plane) : nullptr;
 
   const WSeg fc = seg1(m->w.fc_w, d.D);
   const WSeg kvw = wseg_kv(m);
@@ -444,8 +459,9 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   const PackLayout PL = pack_layout(m);
 
   if (L.fused) {
-    // c = W_c f (fp32, with per-tile row sums of squares), then the K/V
-    // product normalises c while staging it and writes the pages itself.
+    // u = W_c f (fp32, with per-tile row sums of squares), then the K/V
+    // product forms c = bf16(RMSNorm(u)) while staging it and writes the
+    // pages itself.
     float* cx = (float*)c;
     float* ss = (float*)(ws + L.ss);
     SkinnyArgs a{};
@@ -458,7 +474,6 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     a.K = d.F;
     a.part = part;
     a.ctr = m->ctr;
-    a.qhint = m->qhint;
     a.err = m->err;
     a.dh = d.dh;
     a.I = d.I;
@@ -472,7 +487,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     a.ctx_lens = kv->ctx_lens;
     a.theta = m->cfg.rope_theta;
     GemmPlan p = plan_skinny(n_tok, d.D, d.F, SO_STORE_SS, d.dh);
-    HIPCHK(launch_skinny(p, SA_BF16, SO_STORE_SS, a, st));
+    HIPCHK(run_skinny(m, p, SA_BF16, SO_STORE_SS, a, st));
 
     SkinnyArgs b{};
     b.A = cx;
@@ -488,7 +503,6 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     b.K = d.D;
     b.part = part;
     b.ctr = m->ctr;
-    b.qhint = m->qhint;
     b.err = m->err;
     b.Hkv = d.Hkv;
     b.dh = d.dh;
@@ -504,7 +518,7 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     b.n_pages = kv->n_pages;
     b.page_size = m->cfg.page_size;
     p = plan_skinny(n_tok, Nkv, d.D, SO_KV, d.dh);
-    HIPCHK(launch_skinny(p, SA_NORM, SO_KV, b, st));
+    HIPCHK(run_skinny(m, p, SA_NORM1, SO_KV, b, st));
     HIPCHK(launch_advance_ctx(kv->ctx_lens, cu_new, batch, st));
     return DFLASH_OK;
   }
@@ -512,9 +526,9 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
   GemmPlan p = plan_gemm(bf, n_tok, d.D, d.F, false);
   HIPCHK(launch_gemm(p, bf, hidden, nullptr, d.F, n_tok, fc, d.D, d.F, part, nullptr, nullptr, st));
   HIPCHK(launch_inject_norm(bf, part, p.splits, n_tok, d.D, m->w.fc_norm, m->cfg.rms_eps, c,
-                            c_plane, st));
+                            st));
   p = plan_gemm(bf, n_tok, Nkv, d.D, false);
-  HIPCHK(launch_gemm(p, bf, c, c_lo, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
+  HIPCHK(launch_gemm(p, bf, c, nullptr, d.D, n_tok, kvw, Nkv, d.D, part, nullptr, nullptr, st));
   HIPCHK(launch_inject_scatter(bf, part, p.splits, n_tok, cu_new, batch, kv->ctx_lens,
                                kv->page_table, kv->max_pages_per_seq, kv->n_pages,
                                m->cfg.page_size, kv->pages, d.NL, d.Hkv, d.dh,
@@ -634,7 +648,6 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     base.eps = eps;
     base.part = part;
     base.ctr = m->ctr;
-    base.qhint = m->qhint;
     base.err = m->err;
     base.gamma = gamma;
     base.Hq = d.Hq;
@@ -660,7 +673,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
       a.q_plane = q_pl;
       a.kb = k;
       a.vb = v;
-      HIPCHK(launch_skinny(plan_skinny(M, Nqkv, d.D, SO_QKV, d.dh), SA_NORM, SO_QKV, a, st));
+      HIPCHK(run_skinny(m, plan_skinny(M, Nqkv, d.D, SO_QKV, d.dh), SA_NORM, SO_QKV, a, st));
 
       at.layer = l;
       HIPCHK(launch_attention(bf, at, L.ap, st));
@@ -677,7 +690,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
       a.K = d.QD;
       a.x = x;
       a.ss_out = ss;
-      HIPCHK(launch_skinny(plan_skinny(M, d.D, d.QD, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
+      HIPCHK(run_skinny(m, plan_skinny(M, d.D, d.QD, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
       ss_tiles = d.D / 64;
 
       a = base;
@@ -692,7 +705,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
       a.K = d.D;
       a.h = h;
       a.h_plane = h_pl;
-      HIPCHK(launch_skinny(plan_skinny(M, 2 * d.I, d.D, SO_SWIGLU, d.dh), SA_NORM, SO_SWIGLU, a,
+      HIPCHK(run_skinny(m, plan_skinny(M, 2 * d.I, d.D, SO_SWIGLU, d.dh), SA_NORM, SO_SWIGLU, a,
                            st));
 
       a = base;
@@ -705,7 +718,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
       a.K = d.I;
       a.x = x;
       a.ss_out = ss;
-      HIPCHK(launch_skinny(plan_skinny(M, d.D, d.I, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
+      HIPCHK(run_skinny(m, plan_skinny(M, d.D, d.I, SO_RESID, d.dh), SA_SPLIT, SO_RESID, a, st));
     }
     SkinnyArgs a = base;
     a.A = x;
@@ -724,7 +737,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     a.logits = logits;
     a.draw = dr;
     if ((rc = prof_begin()) != DFLASH_OK) return rc;
-    HIPCHK(launch_skinny(plan_skinny(M, d.V, d.D, SO_ARGMAX, d.dh), SA_NORM, SO_ARGMAX, a, st));
+    HIPCHK(run_skinny(m, plan_skinny(M, d.V, d.D, SO_ARGMAX, d.dh), SA_NORM, SO_ARGMAX, a, st));
     if ((rc = prof_end()) != DFLASH_OK) return rc;
     return DFLASH_OK;
   }

@@ -250,8 +250,7 @@ template <bool BF16>
 __global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __restrict__ part,
                                                              int splits, int n, int D,
                                                              const typename Act<BF16>::T* __restrict__ g,
-                                                             float eps, void* __restrict__ c,
-                                                             size_t c_plane) {
+                                                             float eps, void* __restrict__ c) {
   __shared__ float red[16];
   const int t = blockIdx.x;
   f32x4 v[kResMaxPass];
@@ -275,7 +274,10 @@ __global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __rest
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * Act<BF16>::load(g, d + e);
-      store4<BF16>(c, c_plane, (size_t)t * D + d, o);
+      if (BF16)   // c is held in the model dtype: one rounded bf16 plane
+        *(uint2*)&((uint16_t*)c)[(size_t)t * D + d] = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      else
+        *(f32x4*)&((float*)c)[(size_t)t * D + d] = o;
     }
   }
 }
@@ -510,14 +512,14 @@ hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_
 }
 
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
-                              float eps, void* c, size_t c_plane, hipStream_t st) {
+                              float eps, void* c, hipStream_t st) {
   if (D % 4 != 0 || D > kResThreads * 4 * kResMaxPass) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(k_inject_norm<true>, dim3(n), dim3(kResThreads), 0, st, part, splits, n, D,
-                       (const uint16_t*)g, eps, c, c_plane);
+                       (const uint16_t*)g, eps, c);
   else
     hipLaunchKernelGGL(k_inject_norm<false>, dim3(n), dim3(kResThreads), 0, st, part, splits, n,
-                       D, (const float*)g, eps, c, c_plane);
+                       D, (const float*)g, eps, c);
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ enum SkinnyA {
   SA_BF16 = 1,   // A: exact bf16 input (target hidden states)
   SA_NORM = 2,   // A: fp32 rows x[M][lda]; the product uses RMSNorm(x) * gain,
                  // with the row sums of squares taken from ss_in[ss_tiles][M]
+  SA_NORM1 = 3,  // as SA_NORM, but the normalised rows are rounded to bf16 and
+                 // staged as one plane (the fused context of an injection)
 };
 // What happens to the product.  Except for SO_PART and SO_ARGMAX, the K
 // splits of one output tile run on one XCD and the last to finish reduces
@@ -89,7 +91,10 @@ struct SkinnyArgs {
   float* part;             // [S][M][N]
   unsigned long long* ctr; // one arrival counter per output tile, zero between launches
   uint32_t* err;
-  uint32_t* qhint;         // workgroup -> XCD rotation seen by the previous launch (or null)
+  // workgroup -> XCD rotation seen by the previous split-K launch (read), and
+  // the word this launch's workgroup 0 records what it sees in (or both null)
+  const uint32_t* qhint_rd;
+  uint32_t* qhint_wr;
   // SO_ARGMAX: row argmax keys merged into amax[8 XCDs][64] (zero between
   // launches); the last workgroup writes block_tokens[M] (row r = b*gamma + j:
   // anchor[b] for j == 0, else the argmax column) and re-zeroes amax and actr
@@ -197,8 +202,10 @@ hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I,
 // the largest key of row r over best[0..groups)[r].
 hipError_t launch_argmax_finalize(const uint64_t* best, int groups, const int32_t* anchor,
                                   int batch, int gamma, int32_t* block_tokens, hipStream_t stream);
+// c[n][D] = RMSNorm of the summed fc partials, in the model dtype (bf16
+// models: one rounded plane, the precision the context is held in).
 hipError_t launch_inject_norm(bool bf16, const float* part, int splits, int n, int D, const void* g,
-                              float eps, void* c, size_t c_plane, hipStream_t stream);
+                              float eps, void* c, hipStream_t stream);
 hipError_t launch_inject_scatter(bool bf16, const float* part, int splits, int n_tok,
                                  const int32_t* cu_new, int batch, const int32_t* ctx_lens,
                                  const int32_t* page_table, int max_pages, int n_pages,

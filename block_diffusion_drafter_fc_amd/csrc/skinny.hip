@@ -25,7 +25,9 @@
 // squares, K/V page store).  The dispatcher's round robin starts at an XCD
 // that is fixed per hardware queue (not always XCD 0 once a process has
 // several streams), so each launch takes the rotation workgroup 0 saw in the
-// previous launch (a word of the state buffer) as the expected placement.
+// previous launch as the expected placement.  It reads that from one of two
+// words of the state buffer and records its own in the other, so every
+// workgroup of one launch expects the same placement.
 // The counter also counts arrivals per XCD (read from the XCC_ID register).
 // A workgroup away from the tile's home XCD
 // writes its partials back with a device-scope fence; a reducer that saw
@@ -261,7 +263,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
                                                    int gpw) {
   constexpr int U = UW / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
-  constexpr bool TWO = ASRC != SA_BF16;   // two planes in LDS
+  constexpr bool NORM = ASRC == SA_NORM || ASRC == SA_NORM1;   // RMSNorm while staging
+  constexpr bool TWO = ASRC == SA_SPLIT || ASRC == SA_NORM;     // two planes in LDS
   constexpr int NP = TWO ? 2 : 1;
   constexpr int LPR = 256 / ROWS;         // threads per row in the norm prologue
   static_assert(ROWS * CPR % 256 == 0 && 256 % CPR == 0,
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   const int tile = (local / per) * kXcds + xcd, member = local % per;
   if (tile >= n_tiles) return;
   // queue rotation of the workgroup -> XCD placement (see the publish step)
-  const unsigned rot = (OUT != SO_ARGMAX && a.qhint != nullptr) ? (*a.qhint & 7u) : 0u;
+  const unsigned rot = (OUT != SO_ARGMAX && a.qhint_rd != nullptr) ? (*a.qhint_rd & 7u) : 0u;
   const int grp = OUT == SO_ARGMAX ? tile * gpw : tile * tg + member / S, split = member % S;
   const int kbeg = split * kps;
   const int M = a.M, N = a.N, K = a.K;
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
     for (int i = 0; i < NCH; ++i) {
       const int row = srow[i] < M ? srow[i] : M - 1;
       const int col = kbeg + k + scol[i];
-      if (ASRC == SA_NORM) {
+      if (NORM) {
         const float* xp = (const float*)a.A + (size_t)row * a.lda + col;
         r0[i] = ld16(xp);
         r1[i] = ld16(xp + 4);
@@ -351,8 +354,9 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      if (ASRC == SA_NORM) {
+      if (NORM) {
         // y = x * inv * g, split into hi = bf16(y) and lo = bf16(y - hi)
+        // (SA_NORM1: hi only)
         const float inv = inv_s[srow[i]];
         uint32_t hw[4], lw[4];
 #pragma unroll
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
           lw[e] = pack_bf2(ya - __uint_as_float(hw[e] << 16), yb - __uint_as_float(hw[e] & 0xFFFF0000u));
         }
         st16(&As[buf][0][srow[i]][scol[i]], u32x4{hw[0], hw[1], hw[2], hw[3]});
-        st16(&As[buf][1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
+        if (TWO) st16(&As[buf][NP - 1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
       } else {
         st16(&As[buf][0][srow[i]][scol[i]], r0[i]);
         if (TWO) st16(&As[buf][NP - 1][srow[i]][scol[i]], r1[i]);
@@ -379,8 +383,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   // 0, then its weights, which stay in flight while the rest is staged.
   constexpr int Q = kMaxSsTiles / LPR;
   const int nrm_row = tid / LPR, nrm_j = tid % LPR;
-  float ssv[ASRC == SA_NORM ? Q : 1];
-  if (ASRC == SA_NORM) {
+  float ssv[NORM ? Q : 1];
+  if (NORM) {
     // fully unrolled, unpredicated loads (clamped index, masked use): a loop
     // or a branch here would make the compiler drain the loads in flight
     const int rr = nrm_row < M ? nrm_row : M - 1;
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
 #pragma unroll
   for (int u = 0; u < U; ++u) bc[u] = wload(0, u);
   __builtin_amdgcn_sched_barrier(0);
-  if (ASRC == SA_NORM) {
+  if (NORM) {
     // 1 / rms of each row from the producer's per-tile sums of squares
     float s = 0.f;
 #pragma unroll
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   const unsigned xcc = xcc_id();
   const unsigned homex = (unsigned)(xcd + rot) & 7u;
   const bool home = xcc == homex;
-  if (blockIdx.x == 0 && tid == 0 && a.qhint != nullptr) *a.qhint = (xcc - (unsigned)xcd) & 7u;
+  if (blockIdx.x == 0 && tid == 0 && a.qhint_wr != nullptr) *a.qhint_wr = (xcc - (unsigned)xcd) & 7u;
   if (home) __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are in the XCD's L2
   else __threadfence();                       // write back for readers on other XCDs
   __syncthreads();
@@ -733,7 +737,7 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
                            a.block_tokens == nullptr || a.gamma < 1))
     return hipErrorInvalidValue;
   if (tile_groups(out, a.dh) * p.splits > kMaxPer) return hipErrorInvalidValue;
-  if (asrc == SA_NORM && (a.ss_in == nullptr || a.ss_tiles < 1 || a.ss_tiles > kMaxSsTiles ||
+  if ((asrc == SA_NORM || asrc == SA_NORM1) && (a.ss_in == nullptr || a.ss_tiles < 1 || a.ss_tiles > kMaxSsTiles ||
                           a.gain == nullptr))
     return hipErrorInvalidValue;
   if ((out == SO_QKV || out == SO_KV) && a.rope == nullptr) return hipErrorInvalidValue;
@@ -750,7 +754,7 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
   DF_RUN(SA_NORM, SO_SWIGLU);
   DF_RUN(SA_NORM, SO_ARGMAX);
   DF_RUN(SA_BF16, SO_STORE_SS);
-  DF_RUN(SA_NORM, SO_KV);
+  DF_RUN(SA_NORM1, SO_KV);
 #undef DF_RUN
   return hipErrorInvalidValue;
 }

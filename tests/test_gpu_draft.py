@@ -5,8 +5,9 @@ the largest reference logit; bf16 models: 2e-2 absolute) and every proposed
 token must be the oracle's argmax unless the oracle's top-2 gap there is
 below that tolerance.
 
-Covers: the five workloads (the batch-32, long-context and wide ones on
-sampled sequences), block sizes 4, 8 and 10 at the batch-1 Qwen3-8B shape, every GEMM path (1, 2, 4 row tiles and the tiled kernel,
+Covers: the five workloads (every sequence of the long-context and wide
+ones; the first, last and every fourth sequence of the batch-32 one, plus
+its longest and shortest contexts), block sizes 4, 8 and 10 at the batch-1 Qwen3-8B shape, every GEMM path (1, 2, 4 row tiles and the tiled kernel,
 packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
 one, determinism, batch invariance, other streams, and the device error
@@ -112,20 +113,22 @@ def test_draft_qwen3_8b_batch1_block_sizes(gamma):
 
 
 def test_draft_qwen3_8b_batch32_workload_sampled():
+    # every fourth sequence, the last one, and the longest and shortest
+    # contexts: a batch-offset mistake shows in any of them
     s = CONFIGS[3]
     L = context_lengths(s)
-    run_case(s, L, s.block, sample=[0, int(np.argmax(L)), int(np.argmin(L))])
+    seqs = sorted(set(range(0, s.batch, 4)) | {s.batch - 1, int(np.argmax(L)), int(np.argmin(L))})
+    run_case(s, L, s.block, sample=seqs)
 
 
-def test_draft_qwen3_8b_long_context_workload_sampled():
+def test_draft_qwen3_8b_long_context_workload():
     s = CONFIGS[4]
-    run_case(s, context_lengths(s), s.block, sample=[3])
+    run_case(s, context_lengths(s), s.block)        # all four sequences
 
 
-def test_draft_wide_workload_sampled():
+def test_draft_wide_workload():
     s = CONFIGS[5]
-    L = context_lengths(s)
-    run_case(s, L, s.block, sample=[int(np.argmax(L))])
+    run_case(s, context_lengths(s), s.block)        # all eight sequences
 
 
 # --------------------------------------------------------------- edge cases
@@ -204,3 +207,22 @@ def test_draft_device_error_word_reports_bad_page_and_anchor():
     assert drafter.device_error() == 0       # cleared by the read
     drafter.draft(kv, torch.tensor([1, s.vocab + 3], dtype=torch.int32, device="cuda"), 16, blk, ws)
     assert drafter.device_error() & 4
+
+
+def test_draft_device_error_word_reports_context_beyond_the_page_table():
+    # 8 pages of 16 keys: the attention's splits cover 128 keys, so a context
+    # of 130 cannot be read whole and must be reported (not silently cut).
+    import torch
+    s = MINI
+    drafter, _, _ = make_drafter(s)
+    cache = PagedCache(s, 2, 8)
+    kv = cache.allocate_empty()
+    ws = workspace(drafter, 2, 16, 1, 8)
+    blk = torch.zeros((2, 16), dtype=torch.int32, device="cuda")
+    anc = torch.tensor([1, 2], dtype=torch.int32, device="cuda")
+    cache.ctx_dev.copy_(torch.tensor([20, 128], dtype=torch.int32))
+    drafter.draft(kv, anc, 16, blk, ws)
+    assert drafter.device_error() == 0       # a full page table is fine
+    cache.ctx_dev.copy_(torch.tensor([20, 130], dtype=torch.int32))
+    drafter.draft(kv, anc, 16, blk, ws)
+    assert drafter.device_error() & 2
