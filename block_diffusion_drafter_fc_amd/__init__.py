@@ -184,6 +184,16 @@ class Drafter:
             _dev_ptr(logits, "logits", torch.float32), _dev_ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)))
 
+    def draft_noalloc(self, kv: KVCache, anchor, block_size, block_tokens, logits=None,
+                      stream=None):
+        """dflash_draft_block_noalloc: the draft with the library's static
+        per-GPU scratch instead of a workspace (allocates nothing)."""
+        import torch
+        _check(self.lib.dflash_draft_block_noalloc(
+            self.handle, ctypes.byref(kv.c), _dev_ptr(anchor, "anchor", torch.int32),
+            int(anchor.numel()), int(block_size), _dev_ptr(block_tokens, "block_tokens", torch.int32),
+            _dev_ptr(logits, "logits", torch.float32), _stream(stream)))
+
     def draft_sampled(self, kv: KVCache, anchor, block_size, seed, block_tokens, logits,
                       workspace, stream=None):
         """dflash_draft_block_sampled: proposals drawn by Gumbel-max from the

@@ -18,7 +18,8 @@ STATE_BYTES = 16384
 
 EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_bytes",
             "dflash_packed_weight_bytes", "dflash_pack_weights",
-            "dflash_inject_ctx", "dflash_draft_block", "dflash_verify_greedy",
+            "dflash_inject_ctx", "dflash_draft_block", "dflash_draft_block_noalloc",
+            "dflash_verify_greedy",
             "dflash_draft_block_sampled", "dflash_verify_stochastic_workspace_bytes",
             "dflash_verify_stochastic", "dflash_packed_workspace_bytes", "dflash_packed_forward",
             "dflash_ar_workspace_bytes", "dflash_draft_block_ar",
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.dflash_inject_ctx.restype = ctypes.c_int
     lib.dflash_draft_block.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp, sz, vp]
     lib.dflash_draft_block.restype = ctypes.c_int
+    lib.dflash_draft_block_noalloc.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp]
+    lib.dflash_draft_block_noalloc.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_draft_block_sampled.argtypes = [vp, P(KV), vp, i32, i32, ctypes.c_uint64, vp, vp,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -11,6 +12,13 @@
 
 #include "dflash.h"
 #include "kernels.h"
+
+// Scratch of dflash_draft_block_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes its name as an
+// address (on the host it is only a stand-in symbol): dflash_model_create
+// looks up the copy of its device with hipGetSymbolAddress and the entry
+// point uses that pointer.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
 
 struct dflash_model {
   dflash_config cfg;
@@ -33,6 +41,22 @@ struct dflash_model {
 namespace {
 
 thread_local std::string g_err;
+
+// Device address of `scratch` on each GPU (null until resolved).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Resolve the scratch array's address on device `dev`, which must be the
+// current device.  Done once per device; a failure leaves the slot null and
+// is retried by the next model creation on that device.
+void resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices || g_scratch[dev].load() != nullptr) return;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr)
+    g_scratch[dev].store(p);
+  else
+    (void)hipGetLastError();   // leave no error behind for the caller's next call
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -354,6 +378,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   int dev = 0;
   HIPCHK(hipGetDevice(&dev));
   HIPCHK(hipMemset(state, 0, DFLASH_STATE_BYTES));
+  resolve_scratch(dev);
   dflash_model* m = new dflash_model();
   m->cfg = *cfg;
   m->w = *w;
@@ -549,7 +574,7 @@ struct ArPass {
 static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t* anchor,
                       int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
                       void* workspace, size_t ws_bytes, void* stream, const DrawArgs& dr,
-                      const ArPass* ar = nullptr) {
+                      const ArPass* ar = nullptr, bool may_profile = true) {
   dflash_model* m = const_cast<dflash_model*>(mc);
   if (!m || !kv || !anchor || !block_tokens || !workspace)
     return fail(DFLASH_E_INVAL, "draft_block: null argument");
@@ -589,8 +614,9 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
 
   // LM-head timing events (dflash_profile_enable)
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  const bool prof = m->prof_on && may_profile;   // (event creation allocates)
   auto prof_begin = [&]() -> int {
-    if (!m->prof_on) return DFLASH_OK;
+    if (!prof) return DFLASH_OK;
     if (!m->pool.empty()) {
       ev = m->pool.back();
       m->pool.pop_back();
@@ -602,7 +628,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     return DFLASH_OK;
   };
   auto prof_end = [&]() -> int {
-    if (!m->prof_on) return DFLASH_OK;
+    if (!prof) return DFLASH_OK;
     HIPCHK(hipEventRecord(ev.second, st));
     m->pending.push_back(ev);
     return DFLASH_OK;
@@ -813,6 +839,32 @@ int dflash_draft_block(const dflash_model* m, const dflash_kv* kv, const int32_t
                        void* workspace, size_t ws_bytes, void* stream) {
   return draft_impl(m, kv, anchor, batch, gamma, block_tokens, logits, workspace, ws_bytes,
                     stream, DrawArgs{});
+}
+
+int dflash_draft_block_noalloc(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                               int32_t batch, int32_t gamma, int32_t* block_tokens, float* logits,
+                               void* stream) {
+  if (!m || !kv) return fail(DFLASH_E_INVAL, "draft_block_noalloc: null argument");
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev != m->device)
+    return fail(DFLASH_E_INVAL, "draft_block_noalloc: current device %d is not the model's (%d)",
+                dev, m->device);
+  void* ws = dev < kMaxDevices ? g_scratch[dev].load() : nullptr;
+  if (ws == nullptr)
+    return fail(DFLASH_E_HIP, "draft_block_noalloc: the scratch array of device %d is not "
+                              "available", dev);
+  if (batch >= 1 && gamma >= 1 && gamma <= m->cfg.max_block && kv->max_pages_per_seq >= 1) {
+    const size_t need = draft_layout(m, batch, gamma, kv->max_pages_per_seq).total;
+    if (need > DFLASH_NOALLOC_SCRATCH_BYTES)
+      return fail(DFLASH_E_CAPACITY,
+                  "draft_block_noalloc: batch %d, block %d, %d pages per sequence need %zu bytes "
+                  "of scratch; the library holds %zu per GPU",
+                  batch, gamma, kv->max_pages_per_seq, need,
+                  (size_t)DFLASH_NOALLOC_SCRATCH_BYTES);
+  }
+  return draft_impl(m, kv, anchor, batch, gamma, block_tokens, logits, ws,
+                    DFLASH_NOALLOC_SCRATCH_BYTES, stream, DrawArgs{}, nullptr, false);
 }
 
 // Autoregressive drafting workspace: a draft pass of up to block_size - 1

@@ -212,6 +212,32 @@ int dflash_draft_block(const dflash_model* model, const dflash_kv* kv, const int
                        int32_t batch, int32_t block_size, int32_t* block_tokens, float* logits,
                        void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the scratch array behind dflash_draft_block_noalloc, per GPU. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+/* dflash_draft_block for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same draft and the same results, with no workspace
+ * argument: its scratch is a static device array of
+ * DFLASH_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (dflash_model_create locates its device's copy).
+ * The call allocates nothing and never records profiling events.
+ *   - DFLASH_E_CAPACITY (before any launch) when the call needs more scratch
+ *     than that (its need is at most dflash_workspace_bytes(model, batch,
+ *     block_size, 0, kv->max_pages_per_seq) bytes).  Batch 1 at block 16 on a drafter of
+ *     hidden 4096, 32 query heads and SwiGLU width 12288 fits with a page
+ *     table of up to 8192 pages (131072 context tokens).
+ *   - DFLASH_E_INVAL when the current device is not the model's;
+ *     DFLASH_E_HIP when the array could not be located on it.
+ * All calls on one GPU share the array and it keeps the last call's
+ * contents: calls that overlap in time on one GPU race (order them on one
+ * stream).  Each call writes every scratch byte before it reads it, so
+ * nothing needs clearing between calls.  Other arguments as
+ * dflash_draft_block. */
+int dflash_draft_block_noalloc(const dflash_model* model, const dflash_kv* kv,
+                               const int32_t* anchor, int32_t batch, int32_t block_size,
+                               int32_t* block_tokens, float* logits, void* stream);
+
 /* Greedy verification (summary page: "The Target Verifier Remains the
  * Correctness Anchor" -- at temperature 0 the acceptance rule
  * min(1, p_t/p_d) accepts a proposal exactly when it is the target's argmax;
