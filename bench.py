@@ -86,6 +86,29 @@ def algorithmic_bytes(s, ctx_lens_at_draft, n_new_total: int, batch: int, gamma:
             "step": draft + inject + verify, "kv_read": kv_read}
 
 
+def draft_phase_roofline(s, ctx_lens, batch, gamma) -> float:
+    """Per-phase roofline time (s) of one draft step: the sum over its phases
+    (each layer's QKV, attention, O, gate/up and down products, then the LM
+    head) of max(bytes / HBM peak, flops / bf16 MFMA peak).  Bytes of a
+    product: its weights once, fp32 activations in and out; of attention:
+    the layer's cached K/V once."""
+    e = 2 if s.bf16 else 4
+    D, NL, V, I = s.hidden, s.n_layers, s.vocab, s.inter
+    QD, KVD = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    M = batch * gamma
+    hbm, mfma = HBM_PEAK_GBS * 1e9, BF16_MFMA_PEAK_TFLOPS * 1e12
+
+    def product(N, K):
+        return max((N * K * e + M * (N + K) * 4) / hbm, 2.0 * M * N * K / mfma)
+
+    L = np.asarray(ctx_lens, dtype=np.float64)
+    attn_bytes = float(L.sum()) * 2 * KVD * e
+    attn_flops = 4.0 * float(np.sum(L + gamma)) * gamma * s.n_q_heads * s.head_dim
+    layer = (product(QD + 2 * KVD, D) + max(attn_bytes / hbm, attn_flops / mfma) +
+             product(D, QD) + product(2 * I, D) + product(D, I))
+    return NL * layer + product(V, D)
+
+
 def draft_flops(s, ctx_lens, batch, gamma):
     D, NL, V, I = s.hidden, s.n_layers, s.vocab, s.inter
     QD, KVD = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
@@ -141,10 +164,37 @@ def to_dev(a, bf16):
     return t.to("cuda")
 
 
-def run_gpu(s, steps, warmup, sampled=False):
+def percentiles(ms) -> dict:
+    """Median and 10th/90th percentiles of per-call times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"n": int(a.size), "median_ms": round(float(np.median(a)), 4),
+            "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4)}
+
+
+def event_times(fn, n):
+    """Device time (ms) of each of n calls fn(i), from a HIP event pair
+    recorded around each call on the current stream (where the binding
+    launches)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def run_gpu(s, steps, warmup, sampled=False, replays=50):
     """Time `steps` whole steps.  sampled: the draft draws its proposals
     (fresh seed per step, logits written) and the verification is the
-    lossless stochastic one with seeded uniforms."""
+    lossless stochastic one with seeded uniforms.  Afterwards, for the
+    spread: `replays` steps timed one by one (the context rewound and
+    replayed from the first step), then `replays` draft calls and verify
+    calls timed one by one."""
     import torch
     from block_diffusion_drafter_fc_amd import (Drafter, DrafterConfig, KVCache, verify_greedy,
                                                 verify_stochastic,
@@ -153,7 +203,7 @@ def run_gpu(s, steps, warmup, sampled=False):
     from synth.configs import hidden_states, make_weights, page_pool
 
     t0 = time.time()
-    S = warmup + steps
+    S = warmup + max(steps, replays)
     wl = Workload(s, S)
     B, gamma = wl.B, wl.gamma
     w_host = make_weights(s)
@@ -243,78 +293,119 @@ def run_gpu(s, steps, warmup, sampled=False):
         draft_call(k)
         verify_call(k)
 
+    # The timed region: exactly `steps` steps after `warmup` untimed ones.
+    # The LM-head timing events are created by profile_enable, before it.
     ctx.copy_(L0_dev)
     for k in range(warmup):
         step(k)
-    torch.cuda.synchronize()
-    drafter.profile_read(reset=True)
     drafter.profile_enable(True)
+    drafter.profile_read(reset=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for k in range(warmup, S):
+    for k in range(warmup, warmup + steps):
         step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     drafter.profile_enable(False)
     lm_ms, lm_count = drafter.profile_read(reset=True)
     assert drafter.device_error() == 0
+    timed = range(warmup, warmup + steps)
+    accepted = np.stack([acc[k].cpu().numpy() for k in timed])
+    replay_ok = float(np.mean(accepted == wl.tau[warmup:warmup + steps]))
+    taus = accepted
 
-    accepted = np.stack([acc[k].cpu().numpy() for k in range(warmup, S)])
-    planted = wl.tau[warmup:S]
-    replay_ok = float(np.mean(accepted == planted))
-
-    # draft call alone, on the final context
-    n_draft = min(steps, 30)
-    torch.cuda.synchronize()
-    td = time.perf_counter()
-    for k in range(n_draft):
-        draft_call(k)
-    torch.cuda.synchronize()
-    draft_only_ms = (time.perf_counter() - td) * 1e3 / n_draft
-    # verification alone, on the last drafted block of each step
-    torch.cuda.synchronize()
-    tv = time.perf_counter()
-    for k in range(n_draft):
-        verify_call(k)
-    torch.cuda.synchronize()
-    verify_only_ms = (time.perf_counter() - tv) * 1e3 / n_draft
-    taus = np.stack([acc[k].cpu().numpy() for k in range(warmup, S)])
+    # Spread: the context rewound to the prompt, the warm-up steps replayed,
+    # then `replays` steps timed one by one (each re-injects what the first
+    # pass injected, so the cache ends as it did).
+    ctx.copy_(L0_dev)
+    for k in range(warmup):
+        step(k)
+    step_ms = event_times(lambda i: step(warmup + i), replays)
+    assert drafter.device_error() == 0
+    replay_ok = min(replay_ok, float(np.mean(
+        np.stack([acc[warmup + i].cpu().numpy() for i in range(replays)])
+        == wl.tau[warmup:warmup + replays])))
+    # the draft call alone, and verification alone, on the final context
+    draft_ms = event_times(lambda i: draft_call(i % S), replays)
+    verify_ms = event_times(lambda i: verify_call(i % S), replays)
+    assert drafter.device_error() == 0
 
     res = dict(elapsed=elapsed, steps=steps, warmup=warmup, lm_ms=lm_ms, lm_count=lm_count,
-               replay_ok=replay_ok, draft_only_ms=draft_only_ms, prefill_s=prefill_s,
-               verify_only_ms=verify_only_ms, mean_tau=float(taus.mean()),
-               prefill_tokens=prefill_tokens, wl=wl)
+               replay_ok=replay_ok, draft_only_ms=float(np.mean(draft_ms)),
+               draft_spread=percentiles(draft_ms), step_spread=percentiles(step_ms),
+               verify_spread=percentiles(verify_ms), prefill_s=prefill_s,
+               verify_only_ms=float(np.mean(verify_ms)), mean_tau=float(taus.mean()),
+               prefill_tokens=prefill_tokens, wl=wl, draft_ctx_step=warmup + replays - 1)
     drafter.close()
     return res, w_host
 
 
+def host_description() -> dict:
+    """CPU model, logical CPUs and those this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count() or 1, "usable_cpus": usable,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(s, w_host, budget_s=15.0):
-    """The oracle, as committed, on a bounded sample: whole draft blocks of one
-    sequence (its real context length, synthetic cached context) plus the
-    greedy verification of each block, until about budget_s of CPU work."""
+    """The oracle, as committed, on a bounded sample of the same step: per
+    block, inject the new context tokens of a step (their target features),
+    draft the block over the sequence's context (its real length, synthetic
+    cached context) and verify it greedily.  About budget_s of work on all
+    the oracle's threads, then one block on a single thread."""
     import oracle
     from synth import Gen
-    from synth.configs import anchors, context_kv, context_lengths
+    from synth.configs import anchors, context_kv, context_lengths, hidden_states, planted_tau
     L = int(context_lengths(s)[0])
     ck, cv = context_kv(s, 0, L)
     m = oracle.Model(s, w_host)
     toks = np.full(s.block, s.mask_id, np.int32)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one_block(n):
+        # the previous cycle's accepted tokens enter the context first
+        n_new = int(planted_tau(s, 1, f"cpu.new.{n}")[0])
+        m.inject(hidden_states(s, 0, L, n_new), np.arange(L, L + n_new, dtype=np.int32))
         toks[0] = anchors(s, 1, tag=f"cpu.anchor.{n}")[0]
         _, block = m.draft(ck, cv, L, toks)
         tgt = Gen(s.seed).plant_target(f"cpu.target.{n}", block[None], np.array([4]), s.vocab,
                                        dtype=s.dtype)
         oracle.verify(block, tgt[0], s.bf16)
+        return n_new
+
+    threads = oracle.threads()
+    n = tokens = 0
+    t0 = time.perf_counter()
+    while True:
+        tokens += one_block(n)
         n += 1
         if time.perf_counter() - t0 >= budget_s or n >= 50:
             break
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(n / dt, 4), "unit": "blocks/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} draft blocks (block {s.block}) + greedy verification of each, one "
-                      f"sequence with a {L}-token synthetic context, {dt:.1f} s"}
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    one_block(n)
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
+    out = {"value": round(n / dt, 4), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} steps of one sequence with a {L}-token synthetic context: inject "
+                     f"{tokens} new context tokens in all, draft a block of {s.block}, verify it "
+                     f"greedily; {dt:.1f} s on {threads} threads",
+           "single_thread": {"value": round(1.0 / dt1, 4), "unit": "blocks/s",
+                             "sample": f"1 step, {dt1:.1f} s"}}
+    out.update(host_description())
+    return out
 
 
 # ------------------------------------------------------------ HBM counters
@@ -601,6 +692,59 @@ def ar_bench(s, gammas, steps, warmup):
     drafter.close()
 
 
+def workload_report(s, res) -> dict:
+    """Draft-alone figures of a run: mean time over the replays, the spread,
+    blocks and tokens per second, HBM fraction, achieved TFLOP/s and the
+    per-phase roofline fraction (roofline time / measured time)."""
+    wl = res["wl"]
+    B, gamma = wl.B, wl.gamma
+    k_last = res["draft_ctx_step"]
+    timed = range(res["warmup"], res["warmup"] + res["steps"])
+    step_bytes = [algorithmic_bytes(s, wl.L_at[k], int(wl.n_new[k].sum()), B, gamma)
+                  for k in timed]
+    # the draft-alone calls run on the final context
+    d_bytes = algorithmic_bytes(s, wl.L_at[k_last], 0, B, gamma)["draft"]
+    d_ms = res["draft_only_ms"]
+    t_roof = draft_phase_roofline(s, wl.L_at[k_last], B, gamma)
+    flops = draft_flops(s, wl.L_at[k_last], B, gamma)
+    draft = {"ms": round(d_ms, 4), **res["draft_spread"],
+             "blocks_per_s": round(B * 1e3 / d_ms, 3),
+             "tokens_per_s": round(B * (gamma - 1) * 1e3 / d_ms, 1),
+             "hbm_frac": round(d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "algorithmic_GB": round(d_bytes / 1e9, 4),
+             "tflops": round(flops / (d_ms * 1e-3) / 1e12, 2),
+             "roofline_ms": round(t_roof * 1e3, 4),
+             "roofline_frac": round(t_roof * 1e3 / d_ms, 4)}
+    return {"draft_only": draft, "step_bytes": float(np.mean([b["step"] for b in step_bytes])),
+            "lm_bytes": step_bytes[0]["lm_head"]}
+
+
+def bs32_report(replays: int) -> dict:
+    """The Qwen3-8B-shaped drafter at batch 32 (concurrency-32 serving shape):
+    10 whole steps timed after 2, then the spread of `replays` steps, draft
+    calls and verify calls."""
+    from synth.configs import CONFIGS
+    s = CONFIGS[3]
+    steps, warmup = 10, 2
+    log("batch-32 workload")
+    res, _ = run_gpu(s, steps, warmup, replays=replays)
+    rep = workload_report(s, res)
+    wl = res["wl"]
+    B, gamma = wl.B, wl.gamma
+    ms_step = res["elapsed"] * 1e3 / steps
+    lm_ms = res["lm_ms"] / max(res["lm_count"], 1)
+    M = B * gamma
+    return {"workload": s.name, "batch": B, "block": gamma,
+            "contexts": f"U[1024,4096] at the start, {int(wl.L_at[-1].mean())} mean at the end",
+            "steps": steps, "warmup": warmup,
+            "step_ms": round(ms_step, 4), "step_blocks_per_s": round(B * 1e3 / ms_step, 2),
+            "step_spread": res["step_spread"],
+            "draft_only": rep["draft_only"], "verify_only": res["verify_spread"],
+            "lm_head": {"avg_launch_ms": round(lm_ms, 4),
+                        "tflops": round(2.0 * M * s.vocab * s.hidden / (lm_ms * 1e-3) / 1e12, 1)},
+            "replay_accept_match": res["replay_ok"], "mean_accept_len": round(res["mean_tau"], 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -608,6 +752,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-bs1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bs32", action="store_true",
+                    help="skip the batch-32 object of the default batch-1 run")
+    ap.add_argument("--replays", type=int, default=50,
+                    help="steps and calls timed one by one for the spread")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the counter-calibration copy")
@@ -651,23 +799,15 @@ def main():
         block_sweep(s, [int(g) for g in args.block_sweep.split(",")], args.steps, args.warmup)
         return
 
-    res, w_host = run_gpu(s, args.steps, args.warmup)
+    res, w_host = run_gpu(s, args.steps, args.warmup, replays=args.replays)
+    rep = workload_report(s, res)
     wl = res["wl"]
     B, gamma = wl.B, wl.gamma
-    timed = slice(args.warmup, args.warmup + args.steps)
     ms_step = res["elapsed"] * 1e3 / args.steps
     blocks_per_s = B * args.steps / res["elapsed"]
-    # algorithmic bytes over the timed steps
-    step_bytes = [algorithmic_bytes(s, wl.L_at[k], int(wl.n_new[k].sum()), B, gamma)
-                  for k in range(timed.start, timed.stop)]
-    mean_step_bytes = float(np.mean([b["step"] for b in step_bytes]))
-    mean_draft_bytes = float(np.mean([b["draft"] for b in step_bytes]))
-    lm_bytes = step_bytes[0]["lm_head"]
+    lm_bytes = rep["lm_bytes"]
     lm_avg_ms = res["lm_ms"] / max(res["lm_count"], 1)
     lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
-    step_gbs = mean_step_bytes / (ms_step * 1e-3) / 1e9
-    draft_gbs = mean_draft_bytes / (res["draft_only_ms"] * 1e-3) / 1e9
-    flops = draft_flops(s, wl.L_at[-1], B, gamma)
     line = {
         "metric": METRIC,
         "value": round(blocks_per_s, 3),
@@ -688,13 +828,11 @@ def main():
                    "step": "inject accepted tokens + draft block + greedy verify",
                    "parallelism": "single GPU"},
         "draft_tokens_per_s": round(blocks_per_s * (gamma - 1), 2),
-        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "step_algorithmic_GB": round(mean_step_bytes / 1e9, 4),
-        "draft_only": {"ms": round(res["draft_only_ms"], 4),
-                       "blocks_per_s": round(B * 1e3 / res["draft_only_ms"], 3),
-                       "hbm_frac": round(draft_gbs / HBM_PEAK_GBS, 4),
-                       "algorithmic_GB": round(mean_draft_bytes / 1e9, 4),
-                       "tflops": round(flops / (res["draft_only_ms"] * 1e-3) / 1e12, 2)},
+        "step_hbm_frac": round(rep["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_GB": round(rep["step_bytes"] / 1e9, 4),
+        "step_spread": res["step_spread"],
+        "draft_only": rep["draft_only"],
+        "verify_only": res["verify_spread"],
         "replay_accept_match": res["replay_ok"],
         "prefill": {"tokens": res["prefill_tokens"], "s": round(res["prefill_s"], 4)},
         "roofline": {"kernel": "LM head: final RMSNorm staged + bf16 MFMA + argmax (k_skinny)",
@@ -705,6 +843,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(s, w_host, args.cpu_budget)
+    del w_host
+    if s.name == "qwen3-8b-bs1" and not args.no_bs32:
+        line["bs32"] = bs32_report(args.replays)
     print(json.dumps(line), flush=True)
 
 

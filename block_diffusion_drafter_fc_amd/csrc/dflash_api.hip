@@ -119,6 +119,7 @@ size_t part_floats(bool bf16, int M, int N, int K) {
 // and their arrival counter, then one arrival counter per output tile of a
 // fused product.  Every call leaves the slots and counters at zero.
 constexpr size_t kQhintOffset = 128;
+constexpr size_t kProfPool = 256;   // LM-head timing event pairs created by profile_enable
 constexpr size_t kAmaxOffset = 256;
 constexpr size_t kActrOffset = kAmaxOffset + 8 * 64 * 8;
 constexpr size_t kCtrOffset = kActrOffset + 256;
@@ -1085,6 +1086,16 @@ int dflash_device_error(const dflash_model* m, void* stream, int32_t* code) {
 
 int dflash_profile_enable(dflash_model* m, int32_t on) {
   if (!m) return fail(DFLASH_E_INVAL, "profile_enable: null model");
+  // Create the event pairs up front, so timed draft calls only record them.
+  while (on && m->pool.size() + m->pending.size() < kProfPool) {
+    std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+    HIPCHK(hipEventCreate(&ev.first));
+    if (hipEventCreate(&ev.second) != hipSuccess) {
+      (void)hipEventDestroy(ev.first);
+      return fail(DFLASH_E_HIP, "profile_enable: hipEventCreate failed");
+    }
+    m->pool.push_back(ev);
+  }
   m->prof_on = on != 0;
   return DFLASH_OK;
 }

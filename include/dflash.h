@@ -374,9 +374,11 @@ int dflash_device_error(const dflash_model* model, void* stream, int32_t* code);
 
 /* Timing of the LM-head kernel of dflash_draft_block (the largest single
  * launch of the draft step).  While enabled, each draft call records a HIP
- * event pair on its stream around that launch.  dflash_profile_read waits
- * for the recorded events and returns the summed milliseconds and the
- * number of launches timed since the last reset. */
+ * event pair on its stream around that launch.  Enabling creates 256 pairs
+ * up front, so up to 256 timed calls between reads create no event (more
+ * create pairs on demand).  dflash_profile_read waits for the recorded
+ * events, returns the summed milliseconds and the number of launches timed
+ * since the last reset, and returns their pairs to the pool. */
 int dflash_profile_enable(dflash_model* model, int32_t on);
 int dflash_profile_read(dflash_model* model, double* total_ms /* [host] */,
                         int64_t* count /* [host] */, int32_t reset);

@@ -60,6 +60,8 @@ def _load():
         lib.oracle_round_bf16.restype = dbl
         lib.oracle_rmsnorm.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, dbl, vp]
         lib.oracle_rope.argtypes = [vp, ctypes.c_int, ctypes.c_int, dbl, dbl]
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_argmax.argtypes = [vp, ctypes.c_int]
         lib.oracle_argmax.restype = ctypes.c_int
         lib.oracle_attention_dense.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int,
@@ -206,6 +208,16 @@ def verify(block, target, tgt_bf16: bool):
     T = np.empty(g, dtype=np.int32)
     tau = _load().oracle_verify(_p(block), _p(target), 1 if tgt_bf16 else 0, g, V, _p(out), _p(T))
     return tau, out, T
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the oracle's OpenMP thread count (its results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def round_bf16(x):

@@ -33,6 +33,8 @@
 // Parity status of each function: pinned by tests/test_oracle_pins.py unless
 // marked otherwise.
 
+#include <omp.h>
+
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -459,5 +461,11 @@ double oracle_weighted_ce(const double* logits, const int32_t* targets,
   }
   return num / den;
 }
+
+// ---------------------------------------------------------------------------
+// Threads (timing harness only; no arithmetic): the OpenMP team size the
+// parallel loops above use.  Results do not depend on it.
+int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { if (n >= 1) omp_set_num_threads(n); }
 
 }  // extern "C"
