@@ -25,9 +25,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-file flags.  skinny.hip: keep single-lane atomics as written (no
+# wave-level aggregation), so the LM head's group claim is waited for where
+# its result is used, not right after it is issued.
+FILE_FLAGS = {"skinny.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    r = subprocess.run([HIPCC] + FLAGS + ["-c", src, "-o", obj], capture_output=True, text=True)
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    r = subprocess.run([HIPCC] + FLAGS + extra + ["-c", src, "-o", obj], capture_output=True,
+                       text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj

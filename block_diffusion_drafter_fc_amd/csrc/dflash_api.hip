@@ -27,6 +27,7 @@ struct dflash_model {
   unsigned long long* ctr;   // split-K arrival counters (same buffer, zero between calls)
   unsigned long long* amax;  // LM-head argmax slots and their counter (same buffer)
   unsigned long long* actr;
+  unsigned int* wctr;        // LM-head group counter (same buffer, zero between calls)
   uint32_t* qhint;           // two words: workgroup -> XCD rotation seen by split-K launches
   mutable uint32_t hint_seq; // split-K launches so far: selects the word a launch reads
   const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
@@ -115,9 +116,11 @@ size_t part_floats(bool bf16, int M, int N, int K) {
 
 // State buffer: the error word; at 128 two words holding the workgroup ->
 // XCD rotation observed by split-K launches (each launch reads one and writes
-// the other, so all workgroups of a launch read the same value); then the LM-head argmax slots [8 XCDs][64 rows]
-// and their arrival counter, then one arrival counter per output tile of a
-// fused product.  Every call leaves the slots and counters at zero.
+// the other, so all workgroups of a launch read the same value); then the
+// LM-head argmax slots [8 XCDs][64 rows], their arrival counter and (64 bytes
+// further) the LM head's column-group counter; then one arrival counter per
+// output tile of a fused product.  Every call leaves the slots and counters
+// at zero.
 constexpr size_t kQhintOffset = 128;
 constexpr size_t kProfPool = 256;   // LM-head timing event pairs created by profile_enable
 constexpr size_t kAmaxOffset = 256;
@@ -387,6 +390,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->ctr = (unsigned long long*)((char*)state + kCtrOffset);
   m->amax = (unsigned long long*)((char*)state + kAmaxOffset);
   m->actr = (unsigned long long*)((char*)state + kActrOffset);
+  m->wctr = (unsigned int*)((char*)state + kActrOffset + 64);
   m->qhint = (uint32_t*)((char*)state + kQhintOffset);
   m->hint_seq = 0;
   m->packed = nullptr;
@@ -759,6 +763,7 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     a.K = d.D;
     a.amax = m->amax;
     a.actr = m->actr;
+    a.wctr = m->wctr;
     a.anchor = ar ? nullptr : anchor;
     a.block_tokens = block_tokens;
     a.logits = logits;

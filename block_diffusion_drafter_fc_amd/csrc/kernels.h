@@ -100,6 +100,9 @@ struct SkinnyArgs {
   // anchor[b] for j == 0, else the argmax column) and re-zeroes amax and actr
   unsigned long long* amax;
   unsigned long long* actr;
+  // packed weights: a counter (zero between launches) from which workgroups
+  // take further column groups dynamically, or null for static runs
+  unsigned int* wctr;
   const int32_t* anchor;   // null: row 0 also gets its argmax
   int32_t* block_tokens;
   float* logits;           // [M][N] or null

@@ -258,9 +258,19 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 // contiguous chunk and the activations are re-staged from column 0 -- and
 // folds each group's argmax keys into running per-row maxima; n_tiles is then
 // the number of workgroups.  Otherwise gpw = 1.
-template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8>
+//
+// DYN (LM head over packed weights): workgroup t starts with group t and then
+// takes further groups from the counter a.wctr (zero between launches), so
+// CUs that stream faster take more groups.  Thread 0 claims the group after
+// the current one in the group's first sub-chunk, after that sub-chunk's
+// loads, and publishes it through LDS in the second, after that sub-chunk's
+// loads (so the wait for the claim only covers loads the MFMAs need anyway);
+// the group's last sub-chunk starts loading the claimed group.  Needs an even
+// number (>= 4) of sub-chunks per group.
+template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8, bool DYN = false>
 __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
                                                    int gpw) {
+  static_assert(!DYN || (OUT == SO_ARGMAX && PACKED), "dynamic groups: packed LM head only");
   constexpr int U = UW / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
   constexpr bool NORM = ASRC == SA_NORM || ASRC == SA_NORM1;   // RMSNorm while staging
@@ -272,6 +282,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][ROWS][KC + 8];
   __shared__ float inv_s[ROWS];
   __shared__ unsigned long long sh_old;
+  __shared__ int sh_grp[2];   // DYN: the group after group q, in slot (q + 1) & 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -313,7 +324,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
     bp = (const uint16_t*)a.w.ptr[sgi] + (size_t)(wrow - st) * K + kbeg + lg * 8;
     bstride = 32;
   }
-  // weights of block u of the sub-chunk at column k of the slice
+  // weights of block u of the sub-chunk at column k of the slice (DYN: of
+  // the current group, whose base bp is)
   auto wload = [&](int k, int u) { return ld16_stream(bp + (size_t)(k / 32 + u) * bstride); };
 
   // activation chunks this thread stages per sub-chunk: row srow, column scol
@@ -418,14 +430,27 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   // retire in order).  The loads are not predicated (waves past N read a
   // clamped row), so the wait counts stay exact.
   const int nsub = kps / KC;   // >= 1 sub-chunks per group
-  auto step = [&](auto load_tag, int J, int buf, const u32x4* bw, u32x4* bnext) {
+  const int ngroups = (N + 63) / 64;
+  auto step = [&](auto load_tag, int J, int buf, const u32x4* bw, u32x4* bnext,
+                  unsigned& claim) {
     constexpr bool LOAD = decltype(load_tag)::value;
+    const int jq = J % nsub, q = J / nsub;
     if (LOAD) {
       // sub-chunk J + 1: its activations at column ((J + 1) mod nsub) * KC,
-      // its weights J + 1 sub-chunks into this workgroup's stream
+      // its weights J + 1 sub-chunks into this workgroup's stream (DYN: at
+      // the start of the next group once J + 1 opens it)
       fetch(((J + 1) % nsub) * KC);
+      if (DYN && jq == nsub - 1)
+        bp = a.packed + (((size_t)sh_grp[(q + 1) & 1] * (K / 32)) * 4 + wave) * 512 + lane * 8;
 #pragma unroll
-      for (int u = 0; u < U; ++u) bnext[u] = wload((J + 1) * KC, u);
+      for (int u = 0; u < U; ++u) bnext[u] = wload((DYN ? (J + 1) % nsub : J + 1) * KC, u);
+      __builtin_amdgcn_sched_barrier(0);
+      // the claim made one sub-chunk earlier, older than this step's loads:
+      // waiting for it waits for nothing the MFMAs below do not need anyway.
+      // (Published before a claim is made in program order, so the compiler
+      // never counts a claim of this same step as pending here.)
+      if (DYN && jq == 1 && tid == 0) sh_grp[(q + 1) & 1] = n_tiles + (int)claim;
+      if (DYN && jq == 0 && tid == 0) claim = atomicAdd(a.wctr, 1u);
       __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
     }
 #pragma unroll
@@ -474,25 +499,49 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
         }
         acc[m][i] = 0.f;
       }
-    vcol0 += 64;
+    vcol0 = DYN ? sh_grp[(J / nsub + 1) & 1] * 64 + wave * 16 : vcol0 + 64;
   };
-  const int ngrp = OUT == SO_ARGMAX ? min(gpw, (N + 63) / 64 - grp) : 1;
-  const int nj = ngrp * nsub;   // sub-chunks of this workgroup
+  // DYN: sub-chunk J ends the stream when it closes a group and the group
+  // claimed after it is past the end
+  auto last_dyn = [&](int J) {
+    return (J + 1) % nsub == 0 && sh_grp[(J / nsub + 1) & 1] >= ngroups;
+  };
+  const int ngrp = OUT == SO_ARGMAX ? min(gpw, ngroups - grp) : 1;
+  const int nj = ngrp * nsub;   // sub-chunks of this workgroup (static runs)
   int j = 0;
+  if (DYN) {
+    // nsub is even (>= 4): a group starts at an even sub-chunk, so its claim
+    // (sub-chunk 0) and its publication (sub-chunk 1) share an iteration, and
+    // the stream can only end at an odd sub-chunk
+    for (;; j += 2) {
+      unsigned claim = 0;   // made and used within this iteration
+      step(Load{}, j, 0, bc, bn, claim);
+      group_end(j);
+      if (last_dyn(j + 1)) {
+        step(Last{}, j + 1, 1, bn, bc, claim);
+        group_end(j + 1);
+        break;
+      }
+      step(Load{}, j + 1, 1, bn, bc, claim);
+      group_end(j + 1);
+    }
+  } else {
+  unsigned claim = 0;   // unused by static runs
   for (; j + 2 < nj; j += 2) {
-    step(Load{}, j, 0, bc, bn);
+    step(Load{}, j, 0, bc, bn, claim);
     group_end(j);
-    step(Load{}, j + 1, 1, bn, bc);
+    step(Load{}, j + 1, 1, bn, bc, claim);
     group_end(j + 1);
   }
   if (nj - j == 2) {
-    step(Load{}, j, 0, bc, bn);
+    step(Load{}, j, 0, bc, bn, claim);
     group_end(j);
-    step(Last{}, j + 1, 1, bn, bc);
+    step(Last{}, j + 1, 1, bn, bc, claim);
     group_end(j + 1);
   } else {
-    step(Last{}, j, 0, bc, bn);
+    step(Last{}, j, 0, bc, bn, claim);
     group_end(j);
+  }
   }
 
   if (OUT == SO_ARGMAX) {
@@ -538,6 +587,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
     __syncthreads();
     for (int i = tid; i < kXcds * 64; i += 256) atomicExch(&a.amax[i], 0ull);
     if (tid == 0) atomicExch(a.actr, 0ull);
+    if (DYN && tid == 0) atomicExch(a.wctr, 0u);
     return;
   }
 
@@ -614,18 +664,33 @@ template <int MT, int ASRC, int OUT>
 hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
   const int per = tile_groups(OUT, a.dh) * p.splits;
   int gpw = 1;
+  const bool w16 = (OUT == SO_ARGMAX || (MT > 1 && OUT != SO_SWIGLU && OUT != SO_KV)) &&
+                   a.packed != nullptr && p.kpw % (32 * 16 / MT) == 0;
+  bool dyn = false;
   if (OUT == SO_ARGMAX && a.packed != nullptr) {
-    gpw = (n_tiles + kArgmaxWgTarget - 1) / kArgmaxWgTarget;
-    n_tiles = (n_tiles + gpw - 1) / gpw;   // workgroups
+    // dynamic groups need an even number (>= 4) of sub-chunks per group: the
+    // claim is made at sub-chunk 0, published at 1 and used from the last
+    const int nsub = p.kpw / (32 * 16 / MT);
+    dyn = a.wctr != nullptr && w16 && nsub >= 4 && nsub % 2 == 0;
+    if (dyn) {
+      n_tiles = n_tiles < kArgmaxWgTarget ? n_tiles : kArgmaxWgTarget;   // workgroups
+    } else {
+      gpw = (n_tiles + kArgmaxWgTarget - 1) / kArgmaxWgTarget;
+      n_tiles = (n_tiles + gpw - 1) / gpw;   // workgroups
+    }
   }
   const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
+  if (OUT == SO_ARGMAX && dyn) {
+    hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16, OUT == SO_ARGMAX>), dim3(padded * per),
+                       dim3(256), 0, st, a, p.splits, p.kpw, n_tiles, gpw);
+    return hipGetLastError();
+  }
   // 16 weight blocks per batch (512 columns at one row tile): half the
   // staging rounds and barriers per byte, at two workgroups per CU.  The LM
   // head always; with 2 or 4 row tiles also the unpaired products (at one row
   // tile they measured slower, and the paired ones at 640+ workgroups would
   // no longer fit one round).
-  if ((OUT == SO_ARGMAX || (MT > 1 && OUT != SO_SWIGLU && OUT != SO_KV)) && a.packed != nullptr &&
-      p.kpw % (32 * 16 / MT) == 0)
+  if (w16)
     hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16>), dim3(padded * per), dim3(256), 0, st,
                        a, p.splits, p.kpw, n_tiles, gpw);
   else if (a.packed != nullptr)
