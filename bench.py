@@ -20,13 +20,19 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 HBM traffic of the LM-head kernel (the "traffic" field) comes from rocprofv3
 counter runs summarised into profiles/lm_head_traffic_<workload>.json:
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D3 -o c -- python3 bench.py --copy-calibration
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-bs32 --replays 3
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o c -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-bs32 --replays 3
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D3 -o c -- python3 bench.py --read-calibration
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d D4 -o c -- python3 bench.py --copy-calibration
   python3 bench.py --counter-summary D1 D2 D3 D4
-The copy of known size calibrates each counter (bytes per counted KiB); the
-record carries a hash of the kernel sources and is ignored once they change.
+A pure read of known size with the LM head's own load pattern (16-byte
+non-temporal loads, one contiguous run per workgroup) calibrates FETCH_SIZE,
+a device copy of known size WRITE_SIZE (bytes per counted KiB); the record
+carries a hash of the kernel sources and is ignored once they change.
+
+Matrix-core use of the batch-32 draft (profiles/mfma_util_qwen3-8b-bs32.md):
+  rocprofv3 --kernel-trace --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d D5 -o c -- python3 bench.py --workload qwen3-8b-bs32 --steps 2 --warmup 1 --no-cpu-baseline --replays 2
+  python3 bench.py --mfma-summary D5
 """
 from __future__ import annotations
 
@@ -44,11 +50,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/s & draft tokens/s (block 16, Qwen3-8B-shaped, bs 1/32); %HBM peak"
-LM_KERNEL = {"bf16-skinny": "k_skinny<1, 2, 1, true, 16>"}   # LM head at M <= 16 rows: packed, norm-staged, argmax, 16-block batches
+# LM head at M <= 16 rows: packed, norm-staged, argmax, 16-block batches, column
+# groups taken dynamically
+LM_KERNEL = {"bf16-skinny": "k_skinny<1, 2, 1, true, 16, true>"}
 COPY_BYTES = 1 << 30                               # calibration copy size
 KERNEL_SOURCES = ("block_diffusion_drafter_fc_amd/csrc/skinny.hip",
                   "block_diffusion_drafter_fc_amd/csrc/common.h",
-                  "block_diffusion_drafter_fc_amd/csrc/kernels.h")
+                  "block_diffusion_drafter_fc_amd/csrc/kernels.h",
+                  "block_diffusion_drafter_fc_amd/csrc/calibrate.hip")
+READ_CAL_WORKGROUPS = 512   # the LM head's workgroup count
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, vendor peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
@@ -435,6 +445,27 @@ def copy_calibration(reps: int = 5):
     print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps}), flush=True)
 
 
+def read_calibration(reps: int = 5):
+    """A pure read of COPY_BYTES with the LM head's load pattern, reps times
+    (calibrates FETCH_SIZE: the kernel reads exactly COPY_BYTES and writes 16
+    bytes per workgroup)."""
+    import torch
+    from block_diffusion_drafter_fc_amd import read_calibration as rc
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    out = torch.empty(16 * READ_CAL_WORKGROUPS, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        rc(src, out, READ_CAL_WORKGROUPS)
+    torch.cuda.synchronize()
+    print(json.dumps({"read_bytes": COPY_BYTES, "reps": reps,
+                      "workgroups": READ_CAL_WORKGROUPS}), flush=True)
+
+
+def _csv_files(d: str, suffix: str):
+    import glob
+    return glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+
+
 def _counter_rows(d: str):
     import csv
     import glob
@@ -462,29 +493,93 @@ def counter_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload):
             sys.exit("no matching dispatches in the counter files")
         return float(np.mean(v)), len(v)
 
-    def copy_kib(d):
-        # the calibration copies: the largest dispatches of a copy kernel
-        rows = [r for r in _counter_rows(d) if "copy" in r["name"].lower()]
+    def cal_kib(d, key):
+        # the calibration dispatches: the largest ones of the calibration kernel
+        rows = [r for r in _counter_rows(d) if key in r["name"].lower()]
         if not rows:
-            sys.exit(f"no copy dispatches in {d}")
+            sys.exit(f"no '{key}' dispatches in {d}")
         top = max(r["value"] for r in rows)
         return mean_for(rows, lambda r: r["value"] >= 0.5 * top)[0]
 
     f_kib, nf = mean_for(_counter_rows(fetch_dir), lambda r: kname in r["name"])
     w_kib, nw = mean_for(_counter_rows(write_dir), lambda r: kname in r["name"])
-    cf_kib, cw_kib = copy_kib(cfetch_dir), copy_kib(cwrite_dir)
+    # FETCH_SIZE from the pure read with the LM head's pattern, WRITE_SIZE
+    # from the copy (the read's own writes are 16 bytes per workgroup)
+    cf_kib, cw_kib = cal_kib(cfetch_dir, "read_calibration"), cal_kib(cwrite_dir, "copy")
     f_scale = COPY_BYTES / (cf_kib * 1024.0)
     w_scale = COPY_BYTES / (cw_kib * 1024.0)
     rec = {"workload": workload, "kernel": kname, "source_sha256_16": kernel_source_hash(),
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
            "dispatches": [nf, nw],
-           "copy_bytes": COPY_BYTES, "copy_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
+           "calibration_bytes": COPY_BYTES,
+           "read_calibration_fetch_kib": round(cf_kib, 1), "copy_write_kib": round(cw_kib, 1),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "traffic_bytes_per_launch": int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale))}
     with open(traffic_path(workload), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec), flush=True)
+
+
+def mfma_summary(d: str, workload: str):
+    """Per kernel of a --kernel-trace --pmc MfmaUtil MfmaFlopsBF16 run:
+    dispatches, mean duration, matrix-core busy share (MfmaUtil: MFMA busy
+    cycles over active cycles x SIMDs) and counted bf16 TFLOP/s.  Printed as
+    a markdown table."""
+    import csv
+    util, flops, dur = {}, {}, {}
+    for fn in _csv_files(d, "counter_collection.csv"):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], fn, r["Dispatch_Id"])
+                if r["Counter_Name"] == "MfmaUtil":
+                    util[key] = float(r["Counter_Value"])
+                elif r["Counter_Name"] == "MfmaFlopsBF16":
+                    flops[key] = float(r["Counter_Value"])
+    for fn in _csv_files(d, "kernel_trace.csv"):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], fn.replace("kernel_trace", "counter_collection"),
+                       r["Dispatch_Id"])
+                dur[key] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
+    per = {}
+    for key, u in util.items():
+        name = key[0]
+        e = per.setdefault(name, {"n": 0, "util": 0.0, "flops": 0.0, "us": 0.0, "nd": 0})
+        e["n"] += 1
+        e["util"] += u
+        e["flops"] += flops.get(key, 0.0)
+        if key in dur:
+            e["us"] += dur[key]
+            e["nd"] += 1
+    rows = sorted(per.items(), key=lambda kv: -kv[1]["us"])
+    print(f"| kernel | dispatches | mean us | MFMA busy % | bf16 TFLOP/s (counted) |")
+    print("|---|---:|---:|---:|---:|")
+    for name, e in rows:
+        if e["flops"] == 0 and e["util"] == 0:
+            continue
+        mean_us = e["us"] / max(e["nd"], 1)
+        tf = e["flops"] / (e["us"] * 1e-6) / 1e12 if e["us"] > 0 else float("nan")
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+        print(f"| `{short[:90]}` | {e['n']} | {mean_us:.1f} | {e['util'] / e['n']:.1f} | {tf:.0f} |")
+
+
+def stats_summary(d: str):
+    """Markdown table of a rocprofv3 --stats run's kernel_stats.csv: calls,
+    average / min / max duration and share of kernel time, per kernel."""
+    import csv
+    rows = []
+    for fn in _csv_files(d, "kernel_stats.csv"):
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+        print(f"| `{name[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.1f}% |")
 
 
 def recorded_traffic(workload: str):
@@ -759,8 +854,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the counter-calibration copy")
-    ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="only run the pure-read counter calibration")
+    ap.add_argument("--counter-summary", nargs=4,
+                    metavar=("FETCH", "WRITE", "READ_CAL_FETCH", "COPY_WRITE"),
                     help="summarise rocprofv3 --pmc output directories into profiles/")
+    ap.add_argument("--stats-summary", metavar="DIR",
+                    help="markdown table of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="per-kernel matrix-core use from a rocprofv3 MfmaUtil/MfmaFlopsBF16 run")
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled-draft + lossless-verify step next to the greedy one")
     ap.add_argument("--ar", default=None, metavar="G1,G2,...",
@@ -772,6 +874,15 @@ def main():
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.read_calibration:
+        read_calibration()
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, args.workload)
         return
     if args.counter_summary:
         counter_summary(*args.counter_summary, args.workload)

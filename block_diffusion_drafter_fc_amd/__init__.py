@@ -19,6 +19,7 @@ from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_XCD, DFLASH_BF1
 
 __all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy",
            "verify_stochastic", "verify_stochastic_workspace_bytes", "load_library",
+           "read_calibration",
            "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "DEVERR_XCD", "MAX_BLOCK", "MAX_LAYERS"]
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
@@ -284,6 +285,18 @@ def verify_greedy(block_tokens, target_logits, accept_len, out_tokens, workspace
         _dev_ptr(accept_len, "accept_len", torch.int32), _dev_ptr(out_tokens, "out_tokens", torch.int32),
         _dev_ptr(target_argmax, "target_argmax", torch.int32), _dev_ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def read_calibration(src, out, workgroups=512, stream=None):
+    """dflash_read_calibration: stream all of `src` (a device tensor, size a
+    multiple of 16 bytes) with the LM head's load pattern; `out` receives
+    16 bytes per workgroup."""
+    lib = _abi.load()
+    nbytes = src.numel() * src.element_size()
+    if out.numel() * out.element_size() < 16 * workgroups:
+        raise ValueError("read_calibration: out needs 16 bytes per workgroup")
+    _check(lib.dflash_read_calibration(_dev_ptr(src, "src"), nbytes, _dev_ptr(out, "out"),
+                                       int(workgroups), _stream(stream)))
 
 
 def verify_stochastic_workspace_bytes(batch, block_size, vocab) -> int:

@@ -24,7 +24,7 @@ EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_byt
             "dflash_verify_stochastic", "dflash_packed_workspace_bytes", "dflash_packed_forward",
             "dflash_ar_workspace_bytes", "dflash_draft_block_ar",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
-            "dflash_profile_read"]
+            "dflash_profile_read", "dflash_read_calibration"]
 
 
 class Config(ctypes.Structure):
@@ -82,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.dflash_inject_ctx.restype = ctypes.c_int
     lib.dflash_draft_block.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp, sz, vp]
     lib.dflash_draft_block.restype = ctypes.c_int
+    lib.dflash_read_calibration.argtypes = [vp, sz, vp, i32, vp]
+    lib.dflash_read_calibration.restype = ctypes.c_int
     lib.dflash_draft_block_noalloc.argtypes = [vp, P(KV), vp, i32, i32, vp, vp, vp]
     lib.dflash_draft_block_noalloc.restype = ctypes.c_int
     lib.dflash_verify_greedy.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]

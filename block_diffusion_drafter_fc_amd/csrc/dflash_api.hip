@@ -1089,6 +1089,16 @@ int dflash_device_error(const dflash_model* m, void* stream, int32_t* code) {
   return DFLASH_OK;
 }
 
+int dflash_read_calibration(const void* src, size_t bytes, void* out, int32_t workgroups,
+                            void* stream) {
+  if (!src || !out) return fail(DFLASH_E_INVAL, "read_calibration: null argument");
+  if (bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65535)
+    return fail(DFLASH_E_INVAL, "read_calibration: bytes must be a positive multiple of 16 and "
+                                "workgroups in [1, 65535]");
+  HIPCHK(launch_read_calibration(src, bytes, out, workgroups, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
 int dflash_profile_enable(dflash_model* m, int32_t on) {
   if (!m) return fail(DFLASH_E_INVAL, "profile_enable: null model");
   // Create the event pairs up front, so timed draft calls only record them.

@@ -1,6 +1,14 @@
 // gemm.hip -- out = A[M][K] * W[N][K]^T for the drafter's dense products.
 //
-// Three kernels:
+// Four kernels (plan_gemm picks one; the fused products of the draft at
+// M <= 64 live in skinny.hip):
+//   k_gemm_big     bf16, M >= 128: the MFMA-bound products (batch-32 draft,
+//                  large injections, packed passes of 8+ blocks).  Output
+//                  tiles of 64*WM x BN; K moves in steps of 32 through a ring
+//                  of LDS stages filled by global_load_lds (no register
+//                  staging); waves work in two groups half a K step apart so
+//                  one group's fragment reads overlap the other's MFMAs; tile
+//                  order keeps the M tiles of a weight tile on one XCD.
 //   k_gemm_skinny  bf16, M <= 64 (the block rows of a few sequences).  The
 //                  product is a stream of the weight matrix: each lane loads
 //                  16 contiguous bytes of a weight row straight into the
@@ -9,12 +17,12 @@
 //                  shared by its 4 waves; K is split over workgroups (fp32
 //                  partial slices) so that about a thousand groups keep HBM
 //                  busy.
-//   k_gemm_tiled   bf16, larger M: 128x128 output tiles, both operands staged
-//                  through double-buffered LDS, 4 waves of 64x64.
+//   k_gemm_tiled   bf16, 64 < M < 128: 128x128 output tiles, both operands
+//                  staged through double-buffered LDS, 4 waves of 64x64.
 // With SPLIT the activations arrive as two bf16 planes (hi, lo) of an fp32
 // value and every weight fragment meets both: acc += hi*W + lo*W.
 //   k_gemm_f32     fp32 models: one thread per output, plain K loop.
-// All three can end in a fused row argmax (the LM head): the row maximum of
+// All four can end in a fused row argmax (the LM head): the row maximum of
 // a group's columns is packed with its column into a 64-bit key (value
 // order, then lowest column) and stored per (group, row); a small kernel
 // takes the maximum key of each row over the groups, which is exact and

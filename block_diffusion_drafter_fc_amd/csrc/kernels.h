@@ -253,3 +253,10 @@ hipError_t launch_ar_seed(const int32_t* anchor, int batch, int gamma, int32_t* 
                           hipStream_t stream);
 hipError_t launch_ar_pick(const int32_t* pass_tokens, int batch, int i, int gamma, int32_t* block,
                           hipStream_t stream);
+
+// ---- counter calibration ---------------------------------------------------
+// Stream `bytes` (a multiple of 16) of device memory with 16-byte
+// non-temporal loads, one contiguous run per workgroup; out[workgroups]
+// receives one 16-byte checksum per workgroup.
+hipError_t launch_read_calibration(const void* src, size_t bytes, void* out, int workgroups,
+                                   hipStream_t stream);

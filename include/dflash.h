@@ -383,6 +383,17 @@ int dflash_profile_enable(dflash_model* model, int32_t on);
 int dflash_profile_read(dflash_model* model, double* total_ms /* [host] */,
                         int64_t* count /* [host] */, int32_t reset);
 
+/* Counter calibration (a measurement aid, not part of the method): stream
+ * `bytes` of device memory at src with the LM head's load pattern (16-byte
+ * non-temporal loads, each workgroup one contiguous run, a wave 1 KB of
+ * contiguous memory per load instruction) and write one 16-byte checksum per
+ * workgroup to out [workgroups].  The bytes read are known exactly, so a
+ * hardware byte counter read over this call gives its scale for that
+ * pattern.  bytes: a positive multiple of 16; workgroups: 1..65535.
+ * DFLASH_E_INVAL otherwise or for null pointers. */
+int dflash_read_calibration(const void* src, size_t bytes, void* out, int32_t workgroups,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif
