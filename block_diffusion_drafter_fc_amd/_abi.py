@@ -5,7 +5,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash.so")
+# DFLASH_LIB points the loader at another build (the sanitizer test's)
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(HERE, "libdflash.so")
 
 DFLASH_OK = 0
 STATUS_NAMES = {0: "DFLASH_OK", -1: "DFLASH_E_INVAL", -2: "DFLASH_E_SHAPE", -3: "DFLASH_E_DTYPE",

@@ -31,9 +31,15 @@ def sources():
 FILE_FLAGS = {"skinny.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    extra = FILE_FLAGS.get(os.path.basename(src), [])
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (CPU code only:
+# the device code is built as usual).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, extra_flags=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    extra = FILE_FLAGS.get(os.path.basename(src), []) + list(extra_flags)
     r = subprocess.run([HIPCC] + FLAGS + extra + ["-c", src, "-o", obj], capture_output=True,
                        text=True)
     if r.returncode != 0:
@@ -41,20 +47,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Build libdflash.so (or, with sanitize, a host-sanitized build at `out`)."""
+    build_dir = BUILD_DIR if not sanitize else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    extra = SANITIZE_HOST if sanitize else []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] +
+                       (["-Xarch_host", "-shared-libsan"] if sanitize else []) + objs,
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -14,19 +14,24 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# DFLASH_ORACLE_LIB points the loader at another build (the sanitizer test's)
+_LIB = os.environ.get("DFLASH_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 MAX_LAYERS = 32
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so (g++ -O2, strict IEEE double, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared",
-                               "-o", tmp, _SRC])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile liboracle.so (g++ -O2, strict IEEE double, OpenMP); with
+    sanitize, an AddressSanitizer + UndefinedBehaviorSanitizer build at `out`."""
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.check_call(["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared"] +
+                              (SANITIZE if sanitize else []) + ["-o", tmp, _SRC])
+        os.replace(tmp, out)
+    return out
 
 
 class Dims(ctypes.Structure):

@@ -19,18 +19,23 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB = os.path.join(_HERE, "libsynth.so")
+# DFLASH_SYNTH_LIB points the loader at another build (the sanitizer test's)
+_LIB = os.environ.get("DFLASH_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
 _lib = None
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
-    """Compile libsynth.so next to its source (gcc, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile libsynth.so next to its source (gcc, OpenMP); with sanitize, an
+    AddressSanitizer + UndefinedBehaviorSanitizer build at `out`."""
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared"] +
+                              (SANITIZE if sanitize else []) + ["-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
