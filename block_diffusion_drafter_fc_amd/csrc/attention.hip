@@ -155,6 +155,63 @@ DF_DEV void lds_dma16(const void* src, uint32_t lds_base) {
       : "memory", "m0");
 }
 
+// Workgroup -> (split, sequence) when the grid is larger than the GPU holds
+// at once.  In launch order, Hkv consecutive workgroups (one per KV head)
+// take one (split, sequence) pair, and the pairs run longest first: every
+// sequence's full context splits, then the partly filled ones, then the
+// block keys, then the empty splits.  Dealt in grid order, the pairs of a
+// mixed batch would leave full splits waiting behind short ones for a
+// second round of workgroups.  Every wave computes the same uniform result
+// from the B <= 64 context lengths (one per lane): per sequence the counts
+// of full, partial and empty splits, their running sums over sequences, and
+// the first sequence whose running sum passes the pair's rank.
+struct AttnItem {
+  int s, b, L;
+};
+DF_DEV AttnItem attn_item_longest_first(int pair, const int32_t* __restrict__ ctx_lens, int B,
+                                        int P, int chunk, int cap, int report, uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int Lb = lane < B ? ctx_lens[lane] : 0;
+  if (report && __ballot(lane < B && (Lb < 0 || Lb > cap)) != 0 && threadIdx.x == 0)
+    set_dev_error(err, 2u);
+  const int Lc = Lb < 0 ? 0 : Lb;
+  const int fb = lane < B ? min(Lc / chunk, P) : 0;
+  const int pb = lane < B && fb < P && Lc % chunk != 0 ? 1 : 0;
+  const int eb = lane < B ? P - fb - pb : 0;
+  int incf = fb, incp = pb, ince = eb;   // inclusive running sums over sequences
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tf = __shfl_up(incf, o, 64), tp = __shfl_up(incp, o, 64),
+              te = __shfl_up(ince, o, 64);
+    if (lane >= o) {
+      incf += tf;
+      incp += tp;
+      ince += te;
+    }
+  }
+  const int F = __shfl(incf, 63, 64), Pp = __shfl(incp, 63, 64);
+  int b, s;
+  if (pair < F) {
+    b = __ffsll((long long)__ballot(incf > pair)) - 1;
+    s = pair - (__shfl(incf, b, 64) - __shfl(fb, b, 64));
+  } else if (pair < F + Pp) {
+    b = __ffsll((long long)__ballot(incp > pair - F)) - 1;
+    s = __shfl(fb, b, 64);
+  } else if (pair < F + Pp + B) {
+    b = pair - F - Pp;
+    s = P;
+  } else {
+    const int idx = pair - F - Pp - B;
+    b = __ffsll((long long)__ballot(ince > idx)) - 1;
+    s = __shfl(fb, b, 64) + __shfl(pb, b, 64) + idx - (__shfl(ince, b, 64) - __shfl(eb, b, 64));
+  }
+  AttnItem it;
+  it.b = __builtin_amdgcn_readfirstlane(b);
+  it.s = __builtin_amdgcn_readfirstlane(s);
+  it.L = __builtin_amdgcn_readfirstlane(__shfl(Lb, it.b, 64));
+  return it;
+}
+
 template <int DH, int W, int NST>
 // (4 waves: three workgroups per CU by registers; 8 waves: two)
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? 3 : 4))) void k_attn_ctx(
@@ -162,7 +219,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
     const float* __restrict__ vb, const uint16_t* __restrict__ pages, int n_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ ctx_lens,
     int gamma, int Hq, int Hkv, int layer, int chunk, int n_ctx_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err, int causal) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint32_t* err, int causal,
+    int longest_first) {
   constexpr int KT = 32 * DH * 2;              // bytes of the K tile (= the V tile)
   constexpr int SB = 2 * KT;                   // bytes per stage
   constexpr int NB = SB / 1024;                // 1 KB load blocks per stage
@@ -174,7 +232,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
   constexpr int BLK_LDS = 2 * 16 * (DH + 4) * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
   __shared__ int pg_s[64];
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  const int B = gridDim.z;
+  int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, L = 0;
+  if (longest_first) {
+    const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    kvh = lin % Hkv;
+    const AttnItem it = attn_item_longest_first(lin / Hkv, ctx_lens, B, n_ctx_splits, chunk,
+                                                max_pages * 16, lin == 0, err);
+    s = it.s;
+    b = it.b;
+    L = it.L;
+  }
   const int G = Hq / Hkv;
   if (s == n_ctx_splits) {
     attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
@@ -186,10 +254,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const bool comp = wave < G;
   const int h = kvh * G + (comp ? wave : 0);
-  const int L = ctx_lens[b];
-  // The splits cover the page table's capacity; a longer context (or a
-  // negative one) cannot be read whole: report it.
-  if (s == 0 && kvh == 0 && tid == 0 && (L < 0 || L > max_pages * 16)) set_dev_error(err, 2u);
+  if (!longest_first) {
+    L = ctx_lens[b];
+    // The splits cover the page table's capacity; a longer context (or a
+    // negative one) cannot be read whole: report it.
+    if (s == 0 && kvh == 0 && tid == 0 && (L < 0 || L > max_pages * 16)) set_dev_error(err, 2u);
+  }
   const int kbeg = s * chunk;
   const int kend = min(kbeg + chunk, L);
   const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0
@@ -552,12 +622,20 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   for (int e = 0; e < 4; ++e) Split<BF16>::store(o, o_plane, dst + e, acc[e] * inv);
 }
 
+// Longest-first order when the grid exceeds what the GPU holds at once
+// (768 workgroups: three per CU), for batches of 2..64 sequences.
+int longest_first(const AttnArgs& a, const AttnPlan& p) {
+  const long wgs = (long)(p.n_ctx_splits + 1) * a.Hkv * a.batch;
+  return a.batch > 1 && a.batch <= 64 && wgs > 768 ? 1 : 0;
+}
+
 template <int DH, int W, int NST>
 hipError_t run_ctx1(const AttnArgs& a, const AttnPlan& p, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_ctx<DH, W, NST>), grid, dim3(64 * W), 0, st, (const uint16_t*)a.q,
                      a.q_plane, (const float*)a.k, (const float*)a.v, (const uint16_t*)a.pages,
                      a.n_pages, a.page_table, a.max_pages, a.ctx_lens, a.gamma, a.Hq, a.Hkv,
-                     a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err, a.causal);
+                     a.layer, p.chunk, p.n_ctx_splits, a.part_o, a.part_ml, a.err, a.causal,
+                     longest_first(a, p));
   return hipGetLastError();
 }
 

@@ -226,3 +226,18 @@ def test_draft_device_error_word_reports_context_beyond_the_page_table():
     cache.ctx_dev.copy_(torch.tensor([20, 130], dtype=torch.int32))
     drafter.draft(kv, anc, 16, blk, ws)
     assert drafter.device_error() & 2
+
+
+@pytest.mark.parametrize("ctx", [[37], [5, 0, 129, 64, 17], [40] * 8])
+def test_draft_lm_head_ties_take_the_lowest_index(ctx):
+    # A zero final-norm gain makes every logit exactly zero, so each row is
+    # one tie across the vocabulary; the argmax must resolve it to column 0
+    # on every LM-head path (16 rows: the fused skinny head; 80 rows: the
+    # tiled product; 128 rows: the large product and its finalize kernel),
+    # as the oracle does.
+    w = make_weights(MINI)
+    w["final_norm"] = np.zeros_like(w["final_norm"])
+    _, _, _, blk, lg, _ = run_case(MINI, ctx, 16, weights=w)
+    assert np.all(lg == 0.0)
+    for b in range(len(ctx)):
+        assert list(blk[b][1:]) == [0] * 15
