@@ -10,7 +10,8 @@ checking stops at such a tie.
 
 Covers: the tiny fp32 workload, a mini bf16 model (batch 3, ragged and
 empty contexts, fused and plain paths as the pass grows), the Qwen3-8B
-shape at batch 1 and 2048 context tokens, a block of one, and agreement of
+shape at batch 1 and 2048 context tokens, attention splits run longest
+first (batch 8, a 1002-page table), a block of one, and agreement of
 the GPU's last-pass logits with its own earlier choices."""
 import numpy as np
 import pytest
@@ -84,6 +85,14 @@ def test_ar_mini_bf16_batch():
     s = MINI
     ctx = [0, 40, 133]
     check(s, ctx, 16, run_ar(s, ctx, 16))
+
+
+def test_ar_mini_bf16_longest_first_order():
+    # causal block keys when the attention runs its splits longest first
+    from test_gpu_draft import LONGEST_FIRST
+    s = MINI
+    ctx = LONGEST_FIRST[0]
+    check(s, ctx, 5, run_ar(s, ctx, 5))
 
 
 def test_ar_block_of_one():

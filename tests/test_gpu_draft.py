@@ -228,6 +228,20 @@ def test_draft_device_error_word_reports_context_beyond_the_page_table():
     assert drafter.device_error() & 2
 
 
+# Several sequences whose split grid exceeds one round of resident
+# workgroups (a 1002-page table: 64 splits x 2 KV heads x 8 sequences) run
+# their splits longest first: full splits, partly filled ones, block keys,
+# empty splits.  Empty sequences, sequences shorter than a tile and a mix of
+# full and partial splits occur.
+LONGEST_FIRST = [[0, 5, 33, 16000, 700, 0, 9999, 64], [16000, 15999] + [1] * 6]
+
+
+@pytest.mark.parametrize("ctx", LONGEST_FIRST)
+@pytest.mark.parametrize("gamma", [16, 7])
+def test_draft_mini_bf16_longest_first_order(ctx, gamma):
+    run_case(MINI, ctx, gamma)
+
+
 @pytest.mark.parametrize("ctx", [[37], [5, 0, 129, 64, 17], [40] * 8])
 def test_draft_lm_head_ties_take_the_lowest_index(ctx):
     # A zero final-norm gain makes every logit exactly zero, so each row is
