@@ -454,11 +454,13 @@ def read_calibration(reps: int = 5):
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     out = torch.empty(16 * READ_CAL_WORKGROUPS, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
-    for _ in range(reps):
-        rc(src, out, READ_CAL_WORKGROUPS)
-    torch.cuda.synchronize()
-    print(json.dumps({"read_bytes": COPY_BYTES, "reps": reps,
-                      "workgroups": READ_CAL_WORKGROUPS}), flush=True)
+    rc(src, out, READ_CAL_WORKGROUPS)   # warm-up
+    ts = event_times(lambda i: rc(src, out, READ_CAL_WORKGROUPS), reps)
+    # (this is also the read ceiling of the LM head's load pattern)
+    print(json.dumps({"read_bytes": COPY_BYTES, "reps": reps, "workgroups": READ_CAL_WORKGROUPS,
+                      "ms_median": round(float(np.median(ts)), 4),
+                      "read_GBps": round(COPY_BYTES / (float(np.median(ts)) * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def _csv_files(d: str, suffix: str):
