@@ -18,6 +18,7 @@ from ._abi import (DEVERR_PAGE, DEVERR_POS, DEVERR_TOKEN, DEVERR_XCD, DFLASH_BF1
                    MAX_BLOCK, MAX_LAYERS, STATE_BYTES)
 
 __all__ = ["DFlashError", "DrafterConfig", "Drafter", "KVCache", "verify_greedy",
+           "verify_greedy_workspace_bytes",
            "verify_stochastic", "verify_stochastic_workspace_bytes", "load_library",
            "read_calibration",
            "DEVERR_PAGE", "DEVERR_POS", "DEVERR_TOKEN", "DEVERR_XCD", "MAX_BLOCK", "MAX_LAYERS"]
@@ -297,6 +298,13 @@ def read_calibration(src, out, workgroups=512, stream=None):
         raise ValueError("read_calibration: out needs 16 bytes per workgroup")
     _check(lib.dflash_read_calibration(_dev_ptr(src, "src"), nbytes, _dev_ptr(out, "out"),
                                        int(workgroups), _stream(stream)))
+
+
+def verify_greedy_workspace_bytes(batch, block_size, vocab) -> int:
+    n = _abi.load().dflash_verify_greedy_workspace_bytes(int(batch), int(block_size), int(vocab))
+    if n == 0:
+        raise DFlashError(-1, "verify_greedy_workspace_bytes: invalid arguments")
+    return int(n)
 
 
 def verify_stochastic_workspace_bytes(batch, block_size, vocab) -> int:

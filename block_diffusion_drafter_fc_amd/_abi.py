@@ -21,7 +21,8 @@ EXPORTED = ["dflash_model_create", "dflash_model_destroy", "dflash_workspace_byt
             "dflash_packed_weight_bytes", "dflash_pack_weights",
             "dflash_inject_ctx", "dflash_draft_block", "dflash_draft_block_noalloc",
             "dflash_verify_greedy",
-            "dflash_draft_block_sampled", "dflash_verify_stochastic_workspace_bytes",
+            "dflash_draft_block_sampled", "dflash_verify_greedy_workspace_bytes",
+            "dflash_verify_stochastic_workspace_bytes",
             "dflash_verify_stochastic", "dflash_packed_workspace_bytes", "dflash_packed_forward",
             "dflash_ar_workspace_bytes", "dflash_draft_block_ar",
             "dflash_last_error", "dflash_device_error", "dflash_profile_enable",
@@ -92,6 +93,8 @@ def load(path: str = LIB_PATH):
     lib.dflash_draft_block_sampled.argtypes = [vp, P(KV), vp, i32, i32, ctypes.c_uint64, vp, vp,
                                                vp, sz, vp]
     lib.dflash_draft_block_sampled.restype = ctypes.c_int
+    lib.dflash_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.dflash_verify_greedy_workspace_bytes.restype = sz
     lib.dflash_verify_stochastic_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dflash_verify_stochastic_workspace_bytes.restype = sz
     lib.dflash_verify_stochastic.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp, sz,

@@ -28,6 +28,7 @@ struct dflash_model {
   unsigned long long* amax;  // LM-head argmax slots and their counter (same buffer)
   unsigned long long* actr;
   unsigned int* wctr;        // LM-head group counter (same buffer, zero between calls)
+  unsigned int* kvdone;      // inject K/V launch: finished tiles (same buffer, zero between calls)
   uint32_t* qhint;           // two words: workgroup -> XCD rotation seen by split-K launches
   mutable uint32_t hint_seq; // split-K launches so far: selects the word a launch reads
   const uint16_t* packed;    // weights in MFMA tile order (dflash_pack_weights), or null
@@ -117,8 +118,9 @@ size_t part_floats(bool bf16, int M, int N, int K) {
 // State buffer: the error word; at 128 two words holding the workgroup ->
 // XCD rotation observed by split-K launches (each launch reads one and writes
 // the other, so all workgroups of a launch read the same value); then the
-// LM-head argmax slots [8 XCDs][64 rows], their arrival counter and (64 bytes
-// further) the LM head's column-group counter; then one arrival counter per
+// LM-head argmax slots [8 XCDs][64 rows], their arrival counter, (64 bytes
+// further) the LM head's column-group counter and (64 more) the inject K/V
+// launch's count of finished tiles; then one arrival counter per
 // output tile of a fused product.  Every call leaves the slots and counters
 // at zero.
 constexpr size_t kQhintOffset = 128;
@@ -391,6 +393,7 @@ int dflash_model_create(const dflash_config* cfg, const dflash_weights* w, void*
   m->amax = (unsigned long long*)((char*)state + kAmaxOffset);
   m->actr = (unsigned long long*)((char*)state + kActrOffset);
   m->wctr = (unsigned int*)((char*)state + kActrOffset + 64);
+  m->kvdone = (unsigned int*)((char*)state + kActrOffset + 128);
   m->qhint = (uint32_t*)((char*)state + kQhintOffset);
   m->hint_seq = 0;
   m->packed = nullptr;
@@ -426,7 +429,8 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t 
     for (int g = 1; g <= max_block; ++g)
       need = std::max(need, draft_layout(m, b, g, max_pages_per_seq).total);
   for (int n = 1; n <= max_new_tokens; ++n) need = std::max(need, inject_layout(m, n).total);
-  need = std::max(need, align256((size_t)max_batch * max_block * 8));
+  // greedy verification of blocks over the model's vocabulary
+  need = std::max(need, align256(verify_greedy_workspace(max_batch, max_block, m->cfg.vocab)));
   return need;
 }
 
@@ -547,9 +551,11 @@ int dflash_inject_ctx(const dflash_model* m, const dflash_kv* kv, const void* hi
     b.max_pages = kv->max_pages_per_seq;
     b.n_pages = kv->n_pages;
     b.page_size = m->cfg.page_size;
+    // the launch's last tile advances ctx_lens (no separate launch)
+    b.kvdone = m->kvdone;
+    b.ctx_lens_rw = kv->ctx_lens;
     p = plan_skinny(n_tok, Nkv, d.D, SO_KV, d.dh);
     HIPCHK(run_skinny(m, p, SA_NORM1, SO_KV, b, st));
-    HIPCHK(launch_advance_ctx(kv->ctx_lens, cu_new, batch, st));
     return DFLASH_OK;
   }
 
@@ -950,7 +956,9 @@ int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
     return fail(DFLASH_E_DTYPE, "verify_greedy: unknown logits dtype %d", logits_dtype);
   if (batch < 1 || gamma < 1 || vocab < 1)
     return fail(DFLASH_E_INVAL, "verify_greedy: batch, block_size and vocab must be >= 1");
-  const size_t need = (size_t)batch * gamma * 8;
+  if (gamma > kVerifyMaxBlock)
+    return fail(DFLASH_E_CAPACITY, "verify_greedy: block_size %d > %d", gamma, kVerifyMaxBlock);
+  const size_t need = verify_greedy_workspace(batch, gamma, vocab);
   if (ws_bytes < need)
     return fail(DFLASH_E_CAPACITY, "verify_greedy: workspace %zu bytes < %zu needed", ws_bytes,
                 need);
@@ -1039,6 +1047,11 @@ int dflash_packed_forward(const dflash_model* mc, const dflash_kv* ctx, const in
     HIPCHK(launch_block_loss(logits, targets, n_blocks, gamma, m->cfg.vocab, (double)decay,
                              (double*)(ws + L.ce), block_loss, loss, m->err, st));
   return DFLASH_OK;
+}
+
+size_t dflash_verify_greedy_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab) {
+  if (batch < 1 || gamma < 1 || gamma > kVerifyMaxBlock || vocab < 1) return 0;
+  return verify_greedy_workspace(batch, gamma, vocab);
 }
 
 size_t dflash_verify_stochastic_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab) {

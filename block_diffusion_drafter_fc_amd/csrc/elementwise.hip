@@ -344,15 +344,11 @@ __global__ void k_advance_ctx(int32_t* __restrict__ ctx_lens, const int32_t* __r
   if (b < batch) ctx_lens[b] += cu_new[b + 1] - cu_new[b];
 }
 
-__global__ void k_zero_u64(uint64_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
 __global__ void k_clear_word(uint32_t* w) { *w = 0u; }
 
 // Row argmax of the target scores: workgroup (chunk, row) scans `chunk`
-// columns with 16-byte loads and merges its key into best[row].
+// columns with 16-byte loads and stores its key to best[row][chunk] (every
+// slot is written on every call, so nothing needs clearing first).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_verify_argmax(const void* __restrict__ target, int vocab,
                                                        int chunk, uint64_t* __restrict__ best) {
@@ -405,27 +401,38 @@ __global__ __launch_bounds__(256) void k_verify_argmax(const void* __restrict__ 
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) key = redk[w] > key ? redk[w] : key;
-    atomicMax((unsigned long long*)&best[row], (unsigned long long)key);
+    best[(size_t)row * gridDim.x + blockIdx.x] = key;
   }
 }
 
 // tau = n + 1 with n the longest prefix where block[j] == T_{j-1}.
-__global__ void k_verify_finalize(const uint64_t* __restrict__ best,
-                                  const int32_t* __restrict__ block_tokens, int batch, int gamma,
-                                  int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
-                                  int32_t* __restrict__ target_argmax) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
+// Workgroup b: thread j takes row j's maximum over its chunk keys, then the
+// first mismatch is the minimum over the rows that break the prefix.
+__global__ __launch_bounds__(256) void k_verify_finalize(
+    const uint64_t* __restrict__ best, int nchunk, const int32_t* __restrict__ block_tokens,
+    int gamma, int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ target_argmax) {
+  __shared__ int n_s;
+  __shared__ int32_t T_s[kVerifyMaxBlock];
+  const int b = blockIdx.x;
   const int32_t* blk = block_tokens + (size_t)b * gamma;
-  const uint64_t* bk = best + (size_t)b * gamma;
-  int n = 0;
-  while (n < gamma - 1 && blk[n + 1] == (int32_t)argmax_key_index(bk[n])) ++n;
-  accept_len[b] = n + 1;
+  if (threadIdx.x == 0) n_s = gamma - 1;
+  for (int j = threadIdx.x; j < gamma; j += blockDim.x) {
+    const uint64_t* bk = best + ((size_t)b * gamma + j) * nchunk;
+    uint64_t key = 0;
+    for (int c = 0; c < nchunk; ++c) key = bk[c] > key ? bk[c] : key;
+    T_s[j] = (int32_t)argmax_key_index(key);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < gamma - 1; j += blockDim.x)
+    if (blk[j + 1] != T_s[j]) atomicMin(&n_s, j);
+  __syncthreads();
+  const int n = n_s;
+  if (threadIdx.x == 0) accept_len[b] = n + 1;
   int32_t* out = out_tokens + (size_t)b * gamma;
-  for (int j = 0; j < gamma; ++j) {
-    const int32_t T = (int32_t)argmax_key_index(bk[j]);
-    out[j] = j < n ? blk[j + 1] : (j == n ? T : -1);
-    if (target_argmax) target_argmax[(size_t)b * gamma + j] = T;
+  for (int j = threadIdx.x; j < gamma; j += blockDim.x) {
+    out[j] = j < n ? blk[j + 1] : (j == n ? T_s[j] : -1);
+    if (target_argmax) target_argmax[(size_t)b * gamma + j] = T_s[j];
   }
 }
 
@@ -548,19 +555,24 @@ hipError_t launch_advance_ctx(int32_t* ctx_lens, const int32_t* cu_new, int batc
   return hipGetLastError();
 }
 
+size_t verify_greedy_workspace(int batch, int gamma, int vocab) {
+  return (size_t)batch * gamma * ((vocab + kVerifyChunk - 1) / kVerifyChunk) * 8;
+}
+
 hipError_t launch_verify(bool bf16, const int32_t* block_tokens, const void* target, int batch,
                          int gamma, int vocab, uint64_t* best, int32_t* accept_len,
                          int32_t* out_tokens, int32_t* target_argmax, hipStream_t st) {
+  if (gamma > kVerifyMaxBlock) return hipErrorInvalidValue;
   const int rows = batch * gamma;
-  hipLaunchKernelGGL(k_zero_u64, dim3((rows + 255) / 256), dim3(256), 0, st, best, rows);
-  const int chunk = 8192;
-  dim3 grid((vocab + chunk - 1) / chunk, rows);
+  const int chunk = kVerifyChunk;
+  const int nchunk = (vocab + chunk - 1) / chunk;
+  dim3 grid(nchunk, rows);
   if (bf16)
     hipLaunchKernelGGL(k_verify_argmax<true>, grid, dim3(256), 0, st, target, vocab, chunk, best);
   else
     hipLaunchKernelGGL(k_verify_argmax<false>, grid, dim3(256), 0, st, target, vocab, chunk, best);
-  hipLaunchKernelGGL(k_verify_finalize, dim3((batch + 63) / 64), dim3(64), 0, st, best,
-                     block_tokens, batch, gamma, accept_len, out_tokens, target_argmax);
+  hipLaunchKernelGGL(k_verify_finalize, dim3(batch), dim3(gamma < 256 ? 64 : 256), 0, st, best,
+                     nchunk, block_tokens, gamma, accept_len, out_tokens, target_argmax);
   return hipGetLastError();
 }
 

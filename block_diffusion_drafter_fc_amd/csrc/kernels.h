@@ -103,6 +103,11 @@ struct SkinnyArgs {
   // packed weights: a counter (zero between launches) from which workgroups
   // take further column groups dynamically, or null for static runs
   unsigned int* wctr;
+  // SO_KV: a launch-wide count of finished tiles (zero between launches);
+  // the workgroup that finishes the last tile advances ctx_lens by the new
+  // tokens (cu_new).  Null: the caller advances ctx_lens itself.
+  unsigned int* kvdone;
+  int32_t* ctx_lens_rw;   // the same lengths, written by that advance
   const int32_t* anchor;   // null: row 0 also gets its argmax
   int32_t* block_tokens;
   float* logits;           // [M][N] or null
@@ -216,6 +221,11 @@ hipError_t launch_inject_scatter(bool bf16, const float* part, int splits, int n
                                  float theta, uint32_t* err, hipStream_t stream);
 hipError_t launch_advance_ctx(int32_t* ctx_lens, const int32_t* cu_new, int batch,
                               hipStream_t stream);
+// Greedy verification: target columns per argmax workgroup, the largest
+// block it takes, and its workspace (one key per row and column chunk).
+constexpr int kVerifyChunk = 8192;
+constexpr int kVerifyMaxBlock = 1024;
+size_t verify_greedy_workspace(int batch, int gamma, int vocab);
 hipError_t launch_verify(bool bf16, const int32_t* block_tokens, const void* target, int batch,
                          int gamma, int vocab, uint64_t* best, int32_t* accept_len,
                          int32_t* out_tokens, int32_t* target_argmax, hipStream_t stream);

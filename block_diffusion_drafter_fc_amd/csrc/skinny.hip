@@ -652,7 +652,22 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   if (OUT == SO_STORE_SS) epi_resid<false>(a, S, tile);
   if (OUT == SO_QKV) epi_qkv(a, S, tile);
   if (OUT == SO_SWIGLU) epi_swiglu(a, S, tile);
-  if (OUT == SO_KV) epi_kv(a, S, tile);
+  if (OUT == SO_KV) {
+    epi_kv(a, S, tile);
+    if (a.kvdone != nullptr) {
+      // Every tile's epilogue has read ctx_lens before its finisher counts
+      // itself here, so the last one may advance the lengths (the next
+      // launch on the stream reads them).
+      __syncthreads();   // this workgroup's epilogue reads are done
+      __shared__ int sh_last;
+      if (tid == 0) sh_last = atomicAdd(a.kvdone, 1u) == (unsigned)n_tiles - 1u;
+      __syncthreads();
+      if (sh_last) {
+        for (int b = tid; b < a.batch; b += 256) a.ctx_lens_rw[b] += a.cu_new[b + 1] - a.cu_new[b];
+        if (tid == 0) atomicExch(a.kvdone, 0u);
+      }
+    }
+  }
 }
 
 // LM head over packed weights: about this many workgroups, each streaming a

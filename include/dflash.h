@@ -250,8 +250,13 @@ int dflash_draft_block_noalloc(const dflash_model* model, const dflash_kv* kv,
  *                 argmax of row j
  *   out_tokens    [batch][gamma] out: block[1..n], T_n, then -1
  *   target_argmax [batch][gamma] out (T_j), or NULL
- *   workspace     at least batch*gamma*8 bytes (covered by
- *                 dflash_workspace_bytes) */
+ *   workspace     at least dflash_verify_greedy_workspace_bytes(batch,
+ *                 block_size, vocab) = 8 * batch * block_size *
+ *                 ceil(vocab / 8192) bytes (one argmax key per row and
+ *                 8192-column chunk; covered by dflash_workspace_bytes for
+ *                 the model's vocabulary).  Nothing in it needs clearing.
+ * Limits: block_size <= 1024 (DFLASH_E_CAPACITY). */
+size_t dflash_verify_greedy_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab);
 int dflash_verify_greedy(const int32_t* block_tokens, const void* target_logits,
                          int32_t logits_dtype, int32_t batch, int32_t block_size, int32_t vocab,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* target_argmax,

@@ -100,6 +100,22 @@ def test_sampled_draft_requires_logits(lib):
                                           FAKE, 1 << 30, None) == -1
 
 
+def test_greedy_verify_workspace_formula(lib):
+    f = lib.dflash_verify_greedy_workspace_bytes
+    # one 8-byte key per row and 8192-column chunk
+    assert f(2, 16, 100) == 2 * 16 * 8
+    assert f(1, 16, 151936) == 16 * 19 * 8
+    assert f(3, 5, 8192) == 15 * 8 and f(3, 5, 8193) == 15 * 2 * 8
+    assert f(0, 16, 100) == 0 and f(1, 0, 100) == 0 and f(1, 16, 0) == 0 and f(1, 1025, 100) == 0
+    a = dict(block=FAKE, tgt=FAKE, dt=_abi.DFLASH_BF16, B=2, g=16, V=20000, acc=FAKE, out=FAKE,
+             ta=None, ws=FAKE)
+    ok = f(2, 16, 20000)
+    assert lib.dflash_verify_greedy(a["block"], a["tgt"], a["dt"], a["B"], a["g"], a["V"],
+                                    a["acc"], a["out"], a["ta"], a["ws"], ok - 1, None) == -4
+    assert lib.dflash_verify_greedy(a["block"], a["tgt"], a["dt"], a["B"], 1025, a["V"],
+                                    a["acc"], a["out"], a["ta"], a["ws"], 1 << 30, None) == -4
+
+
 def test_stochastic_verify_workspace_formula(lib):
     f = lib.dflash_verify_stochastic_workspace_bytes
     assert f(1, 16, 151936) == 16 * (38 * (4 * 16 + 256) + 1)

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 def run_verify(blocks, target, bf16):
     import torch
-    from block_diffusion_drafter_fc_amd import verify_greedy
+    from block_diffusion_drafter_fc_amd import verify_greedy, verify_greedy_workspace_bytes
     B, g = blocks.shape
     bt = torch.from_numpy(np.ascontiguousarray(blocks, dtype=np.int32)).cuda()
     tt = torch.from_numpy(np.ascontiguousarray(target))
@@ -23,7 +23,10 @@ def run_verify(blocks, target, bf16):
     acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     out = torch.full((B, g), -7, dtype=torch.int32, device="cuda")
     ta = torch.full((B, g), -7, dtype=torch.int32, device="cuda")
-    ws = torch.empty(B * g * 8, dtype=torch.uint8, device="cuda")
+    # the exact size the call asks for, filled with junk: nothing in it may
+    # need clearing
+    ws = torch.full((verify_greedy_workspace_bytes(B, g, target.shape[-1]),), 0xA5,
+                    dtype=torch.uint8, device="cuda")
     verify_greedy(bt, tt, acc, out, ws, target_argmax=ta)
     torch.cuda.synchronize()
     return acc.cpu().numpy(), out.cpu().numpy(), ta.cpu().numpy()
