@@ -816,14 +816,13 @@ def workload_report(s, res) -> dict:
             "lm_bytes": step_bytes[0]["lm_head"]}
 
 
-def bs32_report(replays: int) -> dict:
-    """The Qwen3-8B-shaped drafter at batch 32 (concurrency-32 serving shape):
-    10 whole steps timed after 2, then the spread of `replays` steps, draft
-    calls and verify calls."""
+def workload_object(k: int, steps: int, warmup: int, replays: int, contexts: str) -> dict:
+    """One more workload of the default run, in the batch-1 line: `steps`
+    whole steps timed after `warmup`, then the spread of `replays` steps,
+    draft calls and verify calls, and the draft's per-phase roofline."""
     from synth.configs import CONFIGS
-    s = CONFIGS[3]
-    steps, warmup = 10, 2
-    log("batch-32 workload")
+    s = CONFIGS[k]
+    log(f"workload {s.name}")
     res, _ = run_gpu(s, steps, warmup, replays=replays)
     rep = workload_report(s, res)
     wl = res["wl"]
@@ -832,7 +831,7 @@ def bs32_report(replays: int) -> dict:
     lm_ms = res["lm_ms"] / max(res["lm_count"], 1)
     M = B * gamma
     return {"workload": s.name, "batch": B, "block": gamma,
-            "contexts": f"U[1024,4096] at the start, {int(wl.L_at[-1].mean())} mean at the end",
+            "contexts": f"{contexts} at the start, {int(wl.L_at[-1].mean())} mean at the end",
             "steps": steps, "warmup": warmup,
             "step_ms": round(ms_step, 4), "step_blocks_per_s": round(B * 1e3 / ms_step, 2),
             "step_spread": res["step_spread"],
@@ -840,6 +839,12 @@ def bs32_report(replays: int) -> dict:
             "lm_head": {"avg_launch_ms": round(lm_ms, 4),
                         "tflops": round(2.0 * M * s.vocab * s.hidden / (lm_ms * 1e-3) / 1e12, 1)},
             "replay_accept_match": res["replay_ok"], "mean_accept_len": round(res["mean_tau"], 3)}
+
+
+def bs32_report(replays: int) -> dict:
+    """The Qwen3-8B-shaped drafter at batch 32 (concurrency-32 serving
+    shape): 10 whole steps timed after 2, then the spreads."""
+    return workload_object(3, 10, 2, replays, "U[1024,4096]")
 
 
 def main():
@@ -851,6 +856,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bs32", action="store_true",
                     help="skip the batch-32 object of the default batch-1 run")
+    ap.add_argument("--no-long-wide", action="store_true",
+                    help="skip the long-context and wide-drafter objects of the default run")
     ap.add_argument("--replays", type=int, default=50,
                     help="steps and calls timed one by one for the spread")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -959,6 +966,10 @@ def main():
     del w_host
     if s.name == "qwen3-8b-bs1" and not args.no_bs32:
         line["bs32"] = bs32_report(args.replays)
+    if s.name == "qwen3-8b-bs1" and not args.no_long_wide:
+        # the other two workloads of the survey's configurations, shorter runs
+        line["long"] = workload_object(4, 5, 2, min(args.replays, 20), "4 x 32768")
+        line["wide"] = workload_object(5, 5, 2, min(args.replays, 20), "U[2048,8192]")
     print(json.dumps(line), flush=True)
 
 
