@@ -8,7 +8,7 @@
 //
 // Split-context (flash-decode) layout: workgroup (s, kvh, b) owns one KV head
 // of one sequence and one slice of keys -- context slice s < n_ctx_splits, or
-// the block's own keys (s == n_ctx_splits) -- and writes an
+// the block's own keys for query head kvh * G + (s - n_ctx_splits) -- and writes an
 // unnormalised partial (running max in log2 units, sum of weights, weighted
 // values) that k_attn_combine merges in split order.  Both kinds of slice run
 // in one launch (the block's slice takes a uniform branch).
@@ -31,80 +31,89 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxCtxSplits = 256;            // bounded by plan_attention
 constexpr int kMaxChunk = 1024;               // context keys per workgroup (64 pages)
 
-// The block's own gamma keys (workgroup s == n_ctx_splits of the same grid):
-// fp32 on the vector ALUs, since the block keys and values are transient fp32
-// values.  Wave w takes query head kvh*G + w; lane = (query j = lane / 4,
-// quarter qd = lane % 4 of the head dimension).  Each lane forms partial
-// dot products over its quarter for all gamma keys; two shuffles complete
-// them, so every lane of a query holds all its scores.
+// The block's own gamma keys: one workgroup per query head h of the KV
+// group (workgroups s = n_ctx_splits + (h mod G) of the same grid), in fp32
+// on the vector ALUs, since the block keys and values are transient fp32
+// values.  The head's gamma queries (hi + lo planes summed), the KV head's
+// block keys and values are staged in LDS; thread (j, k) of the first 256
+// forms the score of query j and key k over the whole head dimension, the
+// softmax runs over the 16 lanes of a query with shuffles, and thread
+// (j, d8) then sums 8 output dimensions over the keys.  One head per
+// workgroup keeps each thread's work to ~2 x DH multiply-adds.
 template <int DH>
 __device__ __forceinline__ void attn_block_keys(
     const uint16_t* __restrict__ q, size_t q_plane, const float* __restrict__ kb,
-    const float* __restrict__ vb, int gamma, int Hq, int Hkv, int kvh, int b, int B, int split,
-    float* __restrict__ part_o, float* __restrict__ part_ml, float (*ks)[DH + 4],
-    float (*vs)[DH + 4], int causal) {
-  constexpr int QW = DH / 4;   // head dimensions per lane
-  const int G = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = kvh * G + wave;
-  for (int c = threadIdx.x; c < gamma * (DH / 4); c += blockDim.x) {
-    const int key = c / (DH / 4), d = (c % (DH / 4)) * 4;
-    const size_t off = ((size_t)(b * gamma + key) * Hkv + kvh) * DH + d;
-    *(f32x4*)&ks[key][d] = *(const f32x4*)&kb[off];
-    *(f32x4*)&vs[key][d] = *(const f32x4*)&vb[off];
+    const float* __restrict__ vb, int gamma, int Hq, int Hkv, int h, int kvh, int b, int B,
+    int split, float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ lds,
+    int causal) {
+  constexpr int RS = DH + 4;   // padded row stride (floats)
+  float* ks = lds;             // [16][RS] block keys
+  float* vs = ks + 16 * RS;    // [16][RS] block values
+  float* qs = vs + 16 * RS;    // [16][RS] the head's queries (fp32)
+  float* ps = qs + 16 * RS;    // [16][16] weights of query j, key k
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int c = tid; c < gamma * (DH / 4); c += nthr) {
+    const int r = c / (DH / 4), d = (c % (DH / 4)) * 4;
+    const size_t off = ((size_t)(b * gamma + r) * Hkv + kvh) * DH + d;
+    *(f32x4*)&ks[r * RS + d] = *(const f32x4*)&kb[off];
+    *(f32x4*)&vs[r * RS + d] = *(const f32x4*)&vb[off];
+    const size_t qo = ((size_t)(b * gamma + r) * Hq + h) * DH + d;
+    const uint2 hi = *(const uint2*)(q + qo), lo = *(const uint2*)(q + q_plane + qo);
+    qs[r * RS + d + 0] = bf2f((uint16_t)(hi.x & 0xFFFFu)) + bf2f((uint16_t)(lo.x & 0xFFFFu));
+    qs[r * RS + d + 1] = bf2f((uint16_t)(hi.x >> 16)) + bf2f((uint16_t)(lo.x >> 16));
+    qs[r * RS + d + 2] = bf2f((uint16_t)(hi.y & 0xFFFFu)) + bf2f((uint16_t)(lo.y & 0xFFFFu));
+    qs[r * RS + d + 3] = bf2f((uint16_t)(hi.y >> 16)) + bf2f((uint16_t)(lo.y >> 16));
   }
   __syncthreads();
-  if (wave >= G) return;   // loader-only waves of a small KV group
-  const int j = lane >> 2, qd = lane & 3;
-  const int jj = j < gamma ? j : 0;
-  float qv[QW];
-  {
-    const size_t off = ((size_t)(b * gamma + jj) * Hq + h) * DH + qd * QW;
-#pragma unroll
-    for (int c = 0; c < QW / 8; ++c) {
-      const u32x4 hi = ld16(q + off + c * 8), lo = ld16(q + q_plane + off + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[c * 8 + 2 * e] = bf2f((uint16_t)(hi[e] & 0xFFFFu)) + bf2f((uint16_t)(lo[e] & 0xFFFFu));
-        qv[c * 8 + 2 * e + 1] = bf2f((uint16_t)(hi[e] >> 16)) + bf2f((uint16_t)(lo[e] >> 16));
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  const size_t prow = ((size_t)(split * B + b) * Hq + h) * gamma;   // partial row of query 0
+  if (tid < 256) {
+    // score of query j = tid / 16 and key k = tid % 16 (log2 units)
+    const int j = tid >> 4, k = tid & 15;
+    float dot = 0.f;
+    if (j < gamma && k < gamma) {
+#pragma unroll 8
+      for (int d = 0; d < DH; d += 4) {
+        const f32x4 qv = *(const f32x4*)&qs[j * RS + d];
+        const f32x4 kv = *(const f32x4*)&ks[k * RS + d];
+        dot = fmaf(qv[0], kv[0], dot);
+        dot = fmaf(qv[1], kv[1], dot);
+        dot = fmaf(qv[2], kv[2], dot);
+        dot = fmaf(qv[3], kv[3], dot);
       }
     }
-  }
-  const float sl2 = kLog2e / sqrtf((float)DH);
-  float sc[16];
+    const float sc = k < gamma && (!causal || k <= j) ? dot * sl2 : -INFINITY;
+    float mx = sc;
 #pragma unroll
-  for (int key = 0; key < 16; ++key) {
-    float acc = 0.f;
-    if (key < gamma) {
+    for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    // key 0 is visible to every query, so mx is finite for j < gamma
+    const float pw = j < gamma ? exp2f(sc - mx) : 0.f;
+    float l = pw;
 #pragma unroll
-      for (int e = 0; e < QW; ++e) acc = fmaf(qv[e], ks[key][qd * QW + e], acc);
+    for (int m = 8; m >= 1; m >>= 1) l += __shfl_xor(l, m, 64);
+    ps[j * 16 + k] = pw;
+    if (k == 0 && j < gamma) {
+      part_ml[(prow + j) * 2 + 0] = mx;
+      part_ml[(prow + j) * 2 + 1] = l;
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    sc[key] = key < gamma && (!causal || key <= j) ? acc * sl2 : -INFINITY;
   }
-  float mx = sc[0];
+  __syncthreads();
+  // output dimensions 8 d8 .. 8 d8 + 7 of query j
+  for (int c = tid; c < gamma * (DH / 8); c += nthr) {
+    const int j = c / (DH / 8), d = (c % (DH / 8)) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < gamma; ++k) {
+      const float pw = ps[j * 16 + k];
+      const f32x4 v0 = *(const f32x4*)&vs[k * RS + d], v1 = *(const f32x4*)&vs[k * RS + d + 4];
 #pragma unroll
-  for (int key = 1; key < 16; ++key) mx = fmaxf(mx, sc[key]);
-  float l = 0.f;
-#pragma unroll
-  for (int key = 0; key < 16; ++key) {
-    sc[key] = key < gamma ? exp2f(sc[key] - mx) : 0.f;
-    l += sc[key];
-  }
-  if (j < gamma) {
-    const size_t pr = ((size_t)(split * B + b) * Hq + h) * gamma + j;
-#pragma unroll
-    for (int e = 0; e < QW; ++e) {
-      float acc = 0.f;
-#pragma unroll
-      for (int key = 0; key < 16; ++key) acc = fmaf(sc[key], vs[key][qd * QW + e], acc);
-      part_o[pr * DH + qd * QW + e] = acc;
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(pw, v0[e], acc[e]);
+        acc[4 + e] = fmaf(pw, v1[e], acc[4 + e]);
+      }
     }
-    if (qd == 0) {
-      part_ml[pr * 2 + 0] = mx;
-      part_ml[pr * 2 + 1] = l;
-    }
+    float* po = part_o + (prow + j) * DH + d;
+    *(f32x4*)po = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -169,7 +178,8 @@ struct AttnItem {
   int s, b, L;
 };
 DF_DEV AttnItem attn_item_longest_first(int pair, const int32_t* __restrict__ ctx_lens, int B,
-                                        int P, int chunk, int cap, int report, uint32_t* err) {
+                                        int P, int G, int chunk, int cap, int report,
+                                        uint32_t* err) {
   const int lane = threadIdx.x & 63;
   const int Lb = lane < B ? ctx_lens[lane] : 0;
   if (report && __ballot(lane < B && (Lb < 0 || Lb > cap)) != 0 && threadIdx.x == 0)
@@ -197,11 +207,11 @@ DF_DEV AttnItem attn_item_longest_first(int pair, const int32_t* __restrict__ ct
   } else if (pair < F + Pp) {
     b = __ffsll((long long)__ballot(incp > pair - F)) - 1;
     s = __shfl(fb, b, 64);
-  } else if (pair < F + Pp + B) {
-    b = pair - F - Pp;
-    s = P;
+  } else if (pair < F + Pp + B * G) {
+    b = (pair - F - Pp) / G;           // the block keys: G heads per sequence
+    s = P + (pair - F - Pp) % G;
   } else {
-    const int idx = pair - F - Pp - B;
+    const int idx = pair - F - Pp - B * G;
     b = __ffsll((long long)__ballot(ince > idx)) - 1;
     s = __shfl(fb, b, 64) + __shfl(pb, b, 64) + idx - (__shfl(ince, b, 64) - __shfl(eb, b, 64));
   }
@@ -229,38 +239,61 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
   constexpr int CPR = DH / 8;                  // 16-byte chunks per K row
   constexpr int KPB = 1024 / (DH * 2);         // K rows per block
   constexpr int CTX_LDS = NST * SB;
-  constexpr int BLK_LDS = 2 * 16 * (DH + 4) * 4;
+  constexpr int BLK_LDS = (3 * 16 * (DH + 4) + 256) * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[CTX_LDS > BLK_LDS ? CTX_LDS : BLK_LDS];
   __shared__ int pg_s[64];
   const int B = gridDim.z;
+  const int G = Hq / Hkv;
   int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, L = 0;
   if (longest_first) {
     const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     kvh = lin % Hkv;
-    const AttnItem it = attn_item_longest_first(lin / Hkv, ctx_lens, B, n_ctx_splits, chunk,
+    const AttnItem it = attn_item_longest_first(lin / Hkv, ctx_lens, B, n_ctx_splits, G, chunk,
                                                 max_pages * 16, lin == 0, err);
     s = it.s;
     b = it.b;
     L = it.L;
   }
-  const int G = Hq / Hkv;
-  if (s == n_ctx_splits) {
-    attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh, b, B, s, part_o, part_ml,
-                        (float (*)[DH + 4])lds, (float (*)[DH + 4])(lds + (size_t)16 * (DH + 4) * 4),
-                        causal);
+  if (s >= n_ctx_splits) {   // the block keys, one query head per workgroup
+    attn_block_keys<DH>(q, q_plane, kb, vb, gamma, Hq, Hkv, kvh * G + (s - n_ctx_splits), kvh, b,
+                        B, n_ctx_splits, part_o, part_ml, (float*)lds, causal);
     return;
   }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const bool comp = wave < G;
   const int h = kvh * G + (comp ? wave : 0);
-  if (!longest_first) {
-    L = ctx_lens[b];
-    // The splits cover the page table's capacity; a longer context (or a
-    // negative one) cannot be read whole: report it.
-    if (s == 0 && kvh == 0 && tid == 0 && (L < 0 || L > max_pages * 16)) set_dev_error(err, 2u);
-  }
   const int kbeg = s * chunk;
+  const int pg0 = kbeg >> 4;   // page-table slot of the split's first key
+  constexpr int NI = DH / 32;   // MFMA K steps over the head dimension
+  constexpr int ND = DH / 16;   // 16-row tiles of the head dimension
+  // The context length, the Q fragments and the page-table entries of the
+  // split's whole chunk (at most 64 pages; splits start at multiples of 16
+  // keys) are loaded together, so the split waits for memory once before
+  // its first tile.  Entries past the context are read (clamped to the
+  // table) but not used.
+  if (!longest_first) L = ctx_lens[b];
+  int pg_raw = 0;
+  if (wave == 0) {
+    const int pi = pg0 + lane;
+    pg_raw = page_table[(size_t)b * max_pages + (pi < max_pages ? pi : max_pages - 1)];
+  }
+  u32x4 qop[NI], qlo[NI];
+  {
+    const int row = b * gamma + (lr < gamma ? lr : 0);
+    const uint16_t* qp = q + ((size_t)row * Hq + h) * DH + lg * 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {   // unpredicated loads, then a select (no branch)
+      const u32x4 hi = ld16(qp + i * 32), lo = ld16(qp + q_plane + i * 32);
+      qop[i] = lr < gamma ? hi : u32x4{0u, 0u, 0u, 0u};
+      qlo[i] = lr < gamma ? lo : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // The splits cover the page table's capacity; a longer context (or a
+  // negative one) cannot be read whole: report it (longest-first grids
+  // report it while mapping their workgroups).
+  if (!longest_first && s == 0 && kvh == 0 && tid == 0 && (L < 0 || L > max_pages * 16))
+    set_dev_error(err, 2u);
   const int kend = min(kbeg + chunk, L);
   const size_t prow = ((size_t)(s * B + b) * Hq + h) * gamma;   // partial row of query 0
   if (kend <= kbeg) {
@@ -270,25 +303,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
     }
     return;
   }
-
-  constexpr int NI = DH / 32;   // MFMA K steps over the head dimension
-  constexpr int ND = DH / 16;   // 16-row tiles of the head dimension
-  u32x4 qop[NI], qlo[NI];
-  {
-    const int row = b * gamma + (lr < gamma ? lr : 0);
-    const uint16_t* qp = q + ((size_t)row * Hq + h) * DH + lg * 8;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      qop[i] = lr < gamma ? ld16(qp + i * 32) : u32x4{0u, 0u, 0u, 0u};
-      qlo[i] = lr < gamma ? ld16(qp + q_plane + i * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // page-table slice of this split: pages kbeg/16 .. (kend-1)/16, at most
-  // 64 (splits start at multiples of 16 keys), read by wave 0 in one pass
-  const int pg0 = kbeg >> 4, npg = ((kend - 1) >> 4) - pg0 + 1;
+  // pages kbeg/16 .. (kend-1)/16 of the split; slots past the last repeat it
+  const int npg = ((kend - 1) >> 4) - pg0 + 1;
   if (wave == 0) {
-    const int pi = pg0 + (lane < npg ? lane : npg - 1);
-    int pg = page_table[(size_t)b * max_pages + (pi < max_pages ? pi : max_pages - 1)];
+    const int sl = lane < npg ? lane : npg - 1;
+    const int pg = __shfl(pg_raw, sl, 64);
+    const int pi = pg0 + sl;
     const bool bad = pi >= max_pages || pg < 0 || pg >= n_pages;
     if (bad && lane < npg) set_dev_error(err, pi < max_pages ? 1u : 2u);
     pg_s[lane] = bad ? -1 : pg;
@@ -625,7 +645,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 // Longest-first order when the grid exceeds what the GPU holds at once
 // (768 workgroups: three per CU), for batches of 2..64 sequences.
 int longest_first(const AttnArgs& a, const AttnPlan& p) {
-  const long wgs = (long)(p.n_ctx_splits + 1) * a.Hkv * a.batch;
+  const long wgs = (long)(p.n_ctx_splits + a.Hq / a.Hkv) * a.Hkv * a.batch;
   return a.batch > 1 && a.batch <= 64 && wgs > 768 ? 1 : 0;
 }
 
@@ -675,7 +695,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, const AttnPlan& p, hip
     return hipGetLastError();
   }
   // splits 0 .. n_ctx_splits-1: cached context; split n_ctx_splits: block keys
-  dim3 grid(p.n_ctx_splits + 1, a.Hkv, a.batch);
+  dim3 grid(p.n_ctx_splits + a.Hq / a.Hkv, a.Hkv, a.batch);
   if (a.gamma > 16 || p.chunk > kMaxChunk || p.chunk % 128 || p.n_ctx_splits > kMaxCtxSplits ||
       a.page_size != 16 || a.Hq % a.Hkv != 0 || a.Hq / a.Hkv > 8 || a.n_pages < 1)
     return hipErrorInvalidValue;
