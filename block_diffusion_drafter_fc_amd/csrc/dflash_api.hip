@@ -817,8 +817,13 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     gu.row_end[1] = 2 * d.I;
     gu.n = 2;
     p = plan_gemm(bf, M, 2 * d.I, d.D, false);
-    HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, gu, 2 * d.I, d.D, part, nullptr, nullptr, st));
-    HIPCHK(launch_swiglu(bf, part, p.splits, M, d.I, h, h_pl, st));
+    if (bf && gemm_swiglu_ok(p, d.I)) {
+      HIPCHK(launch_gemm_swiglu(p, y, lo(y, y_pl), d.D, M, gu, d.I, d.D, h, h_pl, st));
+    } else {
+      HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, gu, 2 * d.I, d.D, part, nullptr, nullptr,
+                         st));
+      HIPCHK(launch_swiglu(bf, part, p.splits, M, d.I, h, h_pl, st));
+    }
 
     WSeg dn{};
     dn.ptr[0] = W.w_down;

@@ -406,11 +406,16 @@ constexpr int big_stages(int wm) { return wm == 4 ? 3 : 4; }
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* glb_void_t;
 
-template <bool SPLIT, bool ARGMAX, int WM, int BN, int NWN = 2>
+// SWIGLU (one K split, W = [W_gate; W_up] with I rows each): tile t takes
+// the gate rows [t BN/2, t BN/2 + BN/2) as its first BN/2 columns and the
+// same up rows as the rest; the up waves hand their accumulators to the
+// gate waves through LDS, which write h = silu(gate) * up as split planes
+// (N is then BN * ceil(I / (BN/2))).
+template <bool SPLIT, bool ARGMAX, int WM, int BN, int NWN = 2, bool SWIGLU = false>
 __global__ __launch_bounds__(64 * WM * NWN, 1) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo, int lda, int M, WSeg w,
     int N, int K, int kps, float* __restrict__ part, uint64_t* __restrict__ best,
-    float* __restrict__ logits, DrawArgs dr) {
+    float* __restrict__ logits, DrawArgs dr, void* __restrict__ hout, size_t h_plane, int I) {
   constexpr int BM = 64 * WM, NWAVE = WM * NWN, G = big_stages(WM);
   constexpr bool DBUF = NWAVE == 4;            // one wave per SIMD; else two groups
   constexpr int WCOL = BN / NWN;               // weight columns per wave
@@ -451,7 +456,13 @@ __global__ __launch_bounds__(64 * WM * NWN, 1) void k_gemm_big(
       row = (pl ? Alo : A) + (size_t)r * lda;
     } else {
       // (spare blocks past the tile re-read its first weight row)
-      row = seg_row_bf16(w, min(R < NR ? n0 + (R - RA) : n0, N - 1), K);
+      const int c = R < NR ? R - RA : 0;
+      int vrow = min(n0 + c, N - 1);
+      if (SWIGLU) {
+        const int gi = min(ntile * (BN / 2) + c % (BN / 2), I - 1);
+        vrow = c < BN / 2 ? gi : I + gi;
+      }
+      row = seg_row_bf16(w, vrow, K);
     }
     gp[j] = row + kbeg + c * 8;
   }
@@ -561,6 +572,59 @@ __global__ __launch_bounds__(64 * WM * NWN, 1) void k_gemm_big(
     if (grp == 0) __builtin_amdgcn_s_barrier();
   }
 
+  if constexpr (SWIGLU) {
+    static_assert(!ARGMAX && NWN % 2 == 0 && (BN / 2) % 8 == 0, "SwiGLU pairs gate and up waves");
+    constexpr int HN = NWN / 2;    // waves per half of the tile
+    constexpr int HC = BN / 2;     // h columns of the tile
+    constexpr int NT = 64 * WM * NWN;
+    float* sm = (float*)lds;       // [BM rows][HC]: the up values, then h
+    __syncthreads();               // every wave is past its last fragment reads
+    if (wn >= HN) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int b = 0; b < NBF; ++b)
+            sm[(wm * 64 + a * 16 + lg * 4 + i) * HC + (wn - HN) * WCOL + b * 16 + lr] = acc[a][b][i];
+    }
+    __syncthreads();
+    if (wn < HN) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int b = 0; b < NBF; ++b) {
+            float* e = &sm[(wm * 64 + a * 16 + lg * 4 + i) * HC + wn * WCOL + b * 16 + lr];
+            const float g = acc[a][b][i];
+            *e = __fdividef(g, 1.0f + __expf(-g)) * *e;   // silu(gate) * up
+          }
+    }
+    __syncthreads();
+    // h rows m0.., columns ntile * HC..: 8 consecutive columns per thread,
+    // one 16-byte store per plane (I is a multiple of 8)
+    for (int e = tid; e < BM * (HC / 8); e += NT) {
+      const int r = e / (HC / 8), c8 = (e % (HC / 8)) * 8;
+      const int row = m0 + r, col = ntile * HC + c8;
+      if (row >= M || col >= I) continue;
+      const f32x4 v0 = *(const f32x4*)&sm[r * HC + c8], v1 = *(const f32x4*)&sm[r * HC + c8 + 4];
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x0 = v0[2 * k], x1 = v0[2 * k + 1], y0 = v1[2 * k], y1 = v1[2 * k + 1];
+        hw[k] = pack_bf2(x0, x1);
+        lw[k] = pack_bf2(x0 - __uint_as_float(hw[k] << 16), x1 - __uint_as_float(hw[k] & 0xFFFF0000u));
+        hw[2 + k] = pack_bf2(y0, y1);
+        lw[2 + k] = pack_bf2(y0 - __uint_as_float(hw[2 + k] << 16),
+                             y1 - __uint_as_float(hw[2 + k] & 0xFFFF0000u));
+      }
+      uint16_t* hp = (uint16_t*)hout + (size_t)row * I + col;
+      st16(hp, u32x4{hw[0], hw[1], hw[2], hw[3]});
+      st16(hp + h_plane, u32x4{lw[0], lw[1], lw[2], lw[3]});
+    }
+    return;
+  }
   if (!ARGMAX) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -820,7 +884,7 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
     const uint16_t* al = (const uint16_t*)Alo;
 #define DF_BIG(SPL, AM, WM, BN, NWN)                                                          \
   hipLaunchKernelGGL((k_gemm_big<SPL, AM, WM, BN, NWN>), grid, dim3(64 * WM * NWN), 0, st, a, al, \
-                     lda, M, w, N, K, p.kpw, part, best, logits, dr)
+                     lda, M, w, N, K, p.kpw, part, best, logits, dr, nullptr, (size_t)0, 0)
 #define DF_BIG2(WM, NWN)                                       \
   if (al && best) DF_BIG(true, true, WM, GBN, NWN);             \
   else if (best) DF_BIG(false, true, WM, GBN, NWN);             \
@@ -846,4 +910,33 @@ hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* 
   DF_SKINNY(4, 1, 2);
 #undef DF_SKINNY
   return hipErrorInvalidValue;
+}
+
+bool gemm_swiglu_ok(const GemmPlan& p, int I) {
+  return p.kind == GEMM_BIG && p.splits == 1 && p.nt == 192 && I > 0 && I % 8 == 0 &&
+         (p.mt == 4 || p.mt == 2);
+}
+
+hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* Alo, int lda, int M,
+                              const WSeg& w, int I, int K, void* h, size_t h_plane,
+                              hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (!gemm_swiglu_ok(p, I) || Alo == nullptr || p.kpw != K || K % (2 * GBK) != 0 ||
+      lda % 8 != 0 || (p.waves != 2 * p.mt && !(p.mt == 2 && p.waves == 8)))
+    return hipErrorInvalidValue;
+  constexpr int BN = 192;
+  const int N = BN * ((I + BN / 2 - 1) / (BN / 2));   // paired tiles, the last one ragged
+  const int bm = 64 * p.mt;
+  dim3 grid((N / BN + 7) / 8 * 8 * ((M + bm - 1) / bm), 1, 1);
+  const uint16_t* a = (const uint16_t*)A;
+  const uint16_t* al = (const uint16_t*)Alo;
+  const DrawArgs dr{};
+#define DF_SW(WM, NWN)                                                                         \
+  hipLaunchKernelGGL((k_gemm_big<true, false, WM, BN, NWN, true>), grid, dim3(64 * WM * NWN), 0, \
+                     st, a, al, lda, M, w, N, K, K, nullptr, nullptr, nullptr, dr, h, h_plane, I)
+  if (p.mt == 4) DF_SW(4, 2);
+  else if (p.waves == 8) DF_SW(2, 4);
+  else DF_SW(2, 2);
+#undef DF_SW
+  return hipGetLastError();
 }

@@ -49,6 +49,14 @@ int gemm_argmax_groups(const GemmPlan& p, int N);
 hipError_t launch_gemm(const GemmPlan& p, bool bf16, const void* A, const void* Alo, int lda,
                        int M, const WSeg& w, int N, int K, float* part, uint64_t* best,
                        float* logits, hipStream_t stream, const DrawArgs& draw = DrawArgs{});
+// gate/up product with the SwiGLU in its epilogue: w = [W_gate; W_up] (I
+// rows each), two activation planes, h = silu(A W_gate^T) * (A W_up^T) as
+// split planes [M][I].  Only for plans gemm_swiglu_ok accepts (the large
+// product, one K split, 192-column tiles).
+bool gemm_swiglu_ok(const GemmPlan& p, int I);
+hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* Alo, int lda, int M,
+                              const WSeg& w, int I, int K, void* h, size_t h_plane,
+                              hipStream_t stream);
 
 // ---- skinny product with fused epilogues (bf16 models, M <= 64) -----------
 // Activation source of the product.
