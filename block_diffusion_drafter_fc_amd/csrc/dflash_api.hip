@@ -264,7 +264,7 @@ DraftLayout draft_layout(const dflash_model* m, int B, int gamma, int max_pages)
   L.x = take(M * d.D * 4);
   if (!L.fused) L.y = take(M * d.D * 4);
   L.ss = take(M * std::max(d.D / 64, 1) * 4);
-  if (L.fused) L.rope = take(M * d.dh * 4);   // (cos, sin) per row and dimension pair
+  L.rope = take(M * d.dh * 4);   // (cos, sin) per row and dimension pair
   L.q = take(M * d.QD * 4);
   L.k = take(M * d.KVD * 4);
   L.v = take(M * d.KVD * 4);
@@ -780,8 +780,9 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     return DFLASH_OK;
   }
 
+  float* rope_t = (float*)(ws + L.rope);
   HIPCHK(launch_embed(bf, anchor, batch, gamma, m->cfg.mask_token_id, d.V, m->w.embed, d.D, x,
-                      m->w.layer[0].attn_norm, eps, y, y_pl, nullptr, nullptr, nullptr, d.dh,
+                      m->w.layer[0].attn_norm, eps, y, y_pl, nullptr, rope_t, kv->ctx_lens, d.dh,
                       m->cfg.rope_theta, m->err, st, ar ? ar->tokens : nullptr,
                         ar ? ar->stride : 0));
   for (int l = 0; l < d.NL; ++l) {
@@ -796,8 +797,8 @@ static int draft_impl(const dflash_model* mc, const dflash_kv* kv, const int32_t
     qkv.n = 3;
     GemmPlan p = plan_gemm(bf, M, Nqkv, d.D, false);
     HIPCHK(launch_gemm(p, bf, y, lo(y, y_pl), d.D, M, qkv, Nqkv, d.D, part, nullptr, nullptr, st));
-    HIPCHK(launch_qkv_epilogue(bf, part, p.splits, M, gamma, d.Hq, d.Hkv, d.dh, kv->ctx_lens,
-                               m->cfg.rope_theta, q, q_pl, k, v, st));
+    HIPCHK(launch_qkv_epilogue(bf, part, p.splits, M, d.Hq, d.Hkv, d.dh, rope_t, q, q_pl, k, v,
+                               st));
     at.layer = l;
     HIPCHK(launch_attention(bf, at, L.ap, st));
     HIPCHK(launch_attn_combine(bf, att_o, att_ml, L.parts, batch, gamma, d.Hq, d.dh, o, q_pl, st));

@@ -151,14 +151,16 @@ __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict
   }
 }
 
-// Sum the QKV partials, rotate q and k (rotate-half form) at position
-// ctx_lens[b] + j, store q [M][Hq][dh] (split planes for bf16 models) and the
-// block's k and v [M][Hkv][dh] in fp32.
+// Sum the QKV partials, rotate q and k (rotate-half form) with row r's
+// (cos, sin) pairs from the call's RoPE table (positions ctx_lens[b] + j,
+// angles evaluated once per call by the embedding kernel), store q
+// [M][Hq][dh] (split planes for bf16 models) and the block's k and v
+// [M][Hkv][dh] in fp32.
 template <bool BF16>
-__global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M, int gamma,
-                               int Hq, int Hkv, int dh, const int32_t* __restrict__ ctx_lens,
-                               float theta, void* __restrict__ q, size_t q_plane,
-                               float* __restrict__ k, float* __restrict__ v) {
+__global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M, int Hq,
+                               int Hkv, int dh, const float* __restrict__ rope,
+                               void* __restrict__ q, size_t q_plane, float* __restrict__ k,
+                               float* __restrict__ v) {
   const int r = blockIdx.x, hh = blockIdx.y, i = threadIdx.x, half = dh / 2;
   const int N = (Hq + 2 * Hkv) * dh;
   (void)M;
@@ -170,9 +172,8 @@ __global__ void k_qkv_epilogue(const float* __restrict__ part, int splits, int M
     c2 += part[((size_t)s * M + r) * N + col + half];
   }
   if (hh < Hq + Hkv) {
-    const int pos = ctx_lens[r / gamma] + r % gamma;
-    float cs, sn;
-    rope_cs(pos, i, dh, (double)theta, &cs, &sn);
+    const float2 t = ((const float2*)rope)[(size_t)r * half + i];
+    const float cs = t.x, sn = t.y;
     const float a2 = a * cs - c2 * sn, b2 = c2 * cs + a * sn;
     a = a2;
     c2 = b2;
@@ -481,17 +482,17 @@ hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int spli
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int gamma, int Hq,
-                               int Hkv, int dh, const int32_t* ctx_lens, float theta, void* q,
-                               size_t q_plane, float* k, float* v, hipStream_t st) {
+hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int Hq,
+                               int Hkv, int dh, const float* rope, void* q, size_t q_plane,
+                               float* k, float* v, hipStream_t st) {
   dim3 grid(M, Hq + 2 * Hkv);
   dim3 block(dh / 2);
   if (bf16)
-    hipLaunchKernelGGL(k_qkv_epilogue<true>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
-                       dh, ctx_lens, theta, q, q_plane, k, v);
+    hipLaunchKernelGGL(k_qkv_epilogue<true>, grid, block, 0, st, part, splits, M, Hq, Hkv, dh,
+                       rope, q, q_plane, k, v);
   else
-    hipLaunchKernelGGL(k_qkv_epilogue<false>, grid, block, 0, st, part, splits, M, gamma, Hq, Hkv,
-                       dh, ctx_lens, theta, q, q_plane, k, v);
+    hipLaunchKernelGGL(k_qkv_epilogue<false>, grid, block, 0, st, part, splits, M, Hq, Hkv, dh,
+                       rope, q, q_plane, k, v);
   return hipGetLastError();
 }
 

@@ -209,9 +209,10 @@ hipError_t launch_rmsnorm(bool bf16, const float* x, int M, int D, const void* g
 hipError_t launch_residual_norm(bool bf16, float* x, const float* part, int splits, int M, int D,
                                 const void* g, float eps, void* y, size_t y_plane,
                                 hipStream_t stream);
-hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int gamma, int Hq,
-                               int Hkv, int dh, const int32_t* ctx_lens, float theta, void* q,
-                               size_t q_plane, float* k, float* v, hipStream_t stream);
+// rope: the call's table [M][dh/2] of (cos, sin) pairs (launch_embed writes it)
+hipError_t launch_qkv_epilogue(bool bf16, const float* part, int splits, int M, int Hq,
+                               int Hkv, int dh, const float* rope, void* q, size_t q_plane,
+                               float* k, float* v, hipStream_t stream);
 hipError_t launch_swiglu(bool bf16, const float* part, int splits, int M, int I, void* h,
                          size_t h_plane, hipStream_t stream);
 // block_tokens[r] = r % gamma == 0 && anchor ? anchor[r / gamma] : column of
