@@ -32,27 +32,47 @@ __global__ __launch_bounds__(1024) void k_embed(const int32_t* __restrict__ anch
                                                 int tok_stride) {
   __shared__ float red[16];
   const int r = blockIdx.x, b = r / gamma, j = r % gamma;
+  int tok = tokens != nullptr ? tokens[(size_t)b * tok_stride + j] : (j == 0 ? anchor[b] : mask_id);
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) set_dev_error(err, 4u);
+    tok = 0;
+  }
+  // four elements per thread and pass, loaded unconditionally (a clamped
+  // column, D % 4 == 0) and selected afterwards: a predicated load here
+  // becomes a branch that waits for each load in turn
+  float v[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int d = (p * 1024 + threadIdx.x) * 4;
+    const size_t src = (size_t)tok * D + (d < D ? d : 0);
+    float t[4];
+    if (BF16) {
+      const uint2 raw = *(const uint2*)((const uint16_t*)E + src);
+      t[0] = __uint_as_float(raw.x << 16);
+      t[1] = __uint_as_float(raw.x & 0xFFFF0000u);
+      t[2] = __uint_as_float(raw.y << 16);
+      t[3] = __uint_as_float(raw.y & 0xFFFF0000u);
+    } else {
+      const f32x4 raw = *(const f32x4*)((const float*)E + src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = raw[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[p][e] = d < D ? t[e] : 0.f;
+  }
+  // the RoPE angles (fp64) while the embedding row is in flight
   if (rope != nullptr && (int)threadIdx.x < dh / 2) {
     float cs, sn;
     rope_cs(ctx_lens[b] + j, threadIdx.x, dh, (double)theta, &cs, &sn);
     rope[((size_t)r * (dh / 2) + threadIdx.x) * 2] = cs;
     rope[((size_t)r * (dh / 2) + threadIdx.x) * 2 + 1] = sn;
   }
-  int tok = tokens != nullptr ? tokens[(size_t)b * tok_stride + j] : (j == 0 ? anchor[b] : mask_id);
-  if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) set_dev_error(err, 4u);
-    tok = 0;
-  }
-  float v[2][4];
   float ss = 0.f;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int d = (p * 1024 + threadIdx.x) * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[p][e] = d < D ? Act<BF16>::load(E, (size_t)tok * D + d + e) : 0.f;
-      ss += v[p][e] * v[p][e];
-    }
+    for (int e = 0; e < 4; ++e) ss += v[p][e] * v[p][e];
     if (d < D) *(f32x4*)&x[(size_t)r * D + d] = f32x4{v[p][0], v[p][1], v[p][2], v[p][3]};
   }
   ss = block_sum(ss, red);
@@ -357,17 +377,31 @@ __global__ __launch_bounds__(256) void k_verify_argmax(const void* __restrict__ 
   const int row = blockIdx.y;
   const int c0 = blockIdx.x * chunk, c1 = min(vocab, c0 + chunk);
   uint64_t key = 0;
+  // (vector paths: PU loads per thread are issued before any is used, at
+  // clamped in-bounds columns whose keys are then skipped, so a thread waits
+  // for memory once per PU loads rather than once per load)
+  constexpr int PU = 4;
   if (BF16) {
     const uint16_t* p = (const uint16_t*)target + (size_t)row * vocab;
     if ((vocab & 7) == 0) {
-      for (int c = c0 + threadIdx.x * 8; c < c1; c += blockDim.x * 8) {
-        const u32x4 v = ld16(p + c);
+      const int step = blockDim.x * 8;
+      for (int c = c0 + threadIdx.x * 8; c < c1; c += step * PU) {
+        u32x4 vs[PU];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint64_t k0 = argmax_key(bf2f((uint16_t)(v[e] & 0xFFFFu)), (uint32_t)(c + 2 * e));
-          const uint64_t k1 = argmax_key(bf2f((uint16_t)(v[e] >> 16)), (uint32_t)(c + 2 * e + 1));
-          key = k0 > key ? k0 : key;
-          key = k1 > key ? k1 : key;
+        for (int u = 0; u < PU; ++u) vs[u] = ld16(p + min(c + u * step, c1 - 8));
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+          const int cu = c + u * step;
+          if (cu >= c1) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint64_t k0 =
+                argmax_key(bf2f((uint16_t)(vs[u][e] & 0xFFFFu)), (uint32_t)(cu + 2 * e));
+            const uint64_t k1 =
+                argmax_key(bf2f((uint16_t)(vs[u][e] >> 16)), (uint32_t)(cu + 2 * e + 1));
+            key = k0 > key ? k0 : key;
+            key = k1 > key ? k1 : key;
+          }
         }
       }
     } else {
@@ -379,12 +413,20 @@ __global__ __launch_bounds__(256) void k_verify_argmax(const void* __restrict__ 
   } else {
     const float* p = (const float*)target + (size_t)row * vocab;
     if ((vocab & 3) == 0) {
-      for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4) {
-        const u32x4 v = ld16(p + c);
+      const int step = blockDim.x * 4;
+      for (int c = c0 + threadIdx.x * 4; c < c1; c += step * PU) {
+        u32x4 vs[PU];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint64_t k0 = argmax_key(__uint_as_float(v[e]), (uint32_t)(c + e));
-          key = k0 > key ? k0 : key;
+        for (int u = 0; u < PU; ++u) vs[u] = ld16(p + min(c + u * step, c1 - 4));
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+          const int cu = c + u * step;
+          if (cu >= c1) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint64_t k0 = argmax_key(__uint_as_float(vs[u][e]), (uint32_t)(cu + e));
+            key = k0 > key ? k0 : key;
+          }
         }
       }
     } else {
@@ -421,7 +463,13 @@ __global__ __launch_bounds__(256) void k_verify_finalize(
   for (int j = threadIdx.x; j < gamma; j += blockDim.x) {
     const uint64_t* bk = best + ((size_t)b * gamma + j) * nchunk;
     uint64_t key = 0;
-    for (int c = 0; c < nchunk; ++c) key = bk[c] > key ? bk[c] : key;
+    for (int c = 0; c < nchunk; c += 8) {   // 8 loads in flight (clamped repeats are harmless)
+      uint64_t k8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k8[u] = bk[min(c + u, nchunk - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) key = k8[u] > key ? k8[u] : key;
+    }
     T_s[j] = (int32_t)argmax_key_index(key);
   }
   __syncthreads();
