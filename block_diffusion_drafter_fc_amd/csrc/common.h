@@ -63,6 +63,20 @@ template <> struct Split<true> {
     return bf2f(hi[i]) + bf2f(hi[plane + i]);
   }
 };
+// Four consecutive values (element i, i a multiple of 4) as hi and lo bf16
+// planes, 8 bytes per plane, rounded as Split<true>::store rounds.
+DF_DEV void split_store4(void* base, size_t plane, size_t i, f32x4 v) {
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf(v[e]);
+    l[e] = f2bf(v[e] - bf2f(h[e]));
+  }
+  uint16_t* hp = (uint16_t*)base + i;
+  *(uint2*)hp = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+  *(uint2*)(hp + plane) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+}
+
 template <> struct Split<false> {
   static DF_DEV void store(void* base, size_t, size_t i, float v) { ((float*)base)[i] = v; }
   static DF_DEV float load(const void* base, size_t, size_t i) { return ((const float*)base)[i]; }

@@ -130,9 +130,9 @@ DF_DEV int seq_of(const int32_t* cu_new, int batch, int t) {
 }
 
 // Rotate the pairs (x1[e], x2[e]) = dims (i + e, i + e + dh/2) with the
-// (cos, sin) values cs[2e], cs[2e+1] of one table row.
-DF_DEV void rope4(const float* cs, f32x4& x1, f32x4& x2) {
-  const f32x4 c01 = *(const f32x4*)cs, c23 = *(const f32x4*)(cs + 4);
+// (cos, sin) values (c01, c23) = cs[0..7] of one table row: cs[2e], cs[2e+1]
+// for pair e.
+DF_DEV void rope4(f32x4 c01, f32x4 c23, f32x4& x1, f32x4& x2) {
   const float c[4] = {c01[0], c01[2], c23[0], c23[2]};
   const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
 #pragma unroll
@@ -173,17 +173,18 @@ DF_DEV void epi_qkv(const SkinnyArgs& a, int S, int hh) {
   const int c0 = hh * a.dh;
   for (int task = threadIdx.x; task < a.M * quads; task += blockDim.x) {
     const int row = task / quads, i = (task % quads) * 4;
+    // the row's cos/sin pairs load with the partials (one wait for both;
+    // value heads read them too and leave them unused)
+    const float* cs = a.rope + ((size_t)row * half + i) * 2;
+    const f32x4 c01 = *(const f32x4*)cs, c23 = *(const f32x4*)(cs + 4);
     f32x4 x1, x2;
     const size_t o = (size_t)row * a.N + c0 + i;
     sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + half, x1, x2);
-    if (hh < a.Hq + a.Hkv) rope4(a.rope + ((size_t)row * half + i) * 2, x1, x2);
+    if (hh < a.Hq + a.Hkv) rope4(c01, c23, x1, x2);
     if (hh < a.Hq) {
       const size_t base = ((size_t)row * a.Hq + hh) * a.dh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Split<true>::store(a.q, a.q_plane, base + i + e, x1[e]);
-        Split<true>::store(a.q, a.q_plane, base + i + e + half, x2[e]);
-      }
+      split_store4(a.q, a.q_plane, base + i, x1);
+      split_store4(a.q, a.q_plane, base + i + half, x2);
     } else {
       const bool isk = hh < a.Hq + a.Hkv;
       float* dst = isk ? a.kb : a.vb;
@@ -203,11 +204,10 @@ DF_DEV void epi_swiglu(const SkinnyArgs& a, int S, int tile) {
     f32x4 g, u;
     const size_t o = (size_t)row * a.N + (2 * tile) * 64 + c;
     sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + 64, g, u);
+    f32x4 y;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sg = g[e] / (1.0f + expf(-g[e]));
-      Split<true>::store(a.h, a.h_plane, (size_t)row * a.I + tile * 64 + c + e, sg * u[e]);
-    }
+    for (int e = 0; e < 4; ++e) y[e] = g[e] / (1.0f + expf(-g[e])) * u[e];
+    split_store4(a.h, a.h_plane, (size_t)row * a.I + tile * 64 + c, y);
   }
 }
 
@@ -231,10 +231,12 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
       if (i == 0) set_dev_error(a.err, 1u);
       continue;
     }
+    const float* cs = a.rope + ((size_t)t * half + i) * 2;
+    const f32x4 c01 = *(const f32x4*)cs, c23 = *(const f32x4*)(cs + 4);
     f32x4 x1, x2;
     const size_t o = (size_t)t * a.N + c0 + i;
     sum_parts2(a.part, S, (size_t)a.M * a.N, o, o + half, x1, x2);
-    if (kv == 0) rope4(a.rope + ((size_t)t * half + i) * 2, x1, x2);
+    if (kv == 0) rope4(c01, c23, x1, x2);
     // K rows are [page_size][dh], values transposed [dh][page_size]
     uint16_t* dst = (uint16_t*)a.pages +
                     ((((size_t)layer * a.n_pages + pg) * 2 + kv) * a.Hkv + kvh) * a.page_size * a.dh;
