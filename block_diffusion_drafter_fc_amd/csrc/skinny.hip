@@ -268,11 +268,18 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 // loads, and publishes it through LDS in the second, after that sub-chunk's
 // loads (so the wait for the claim only covers loads the MFMAs need anyway);
 // the group's last sub-chunk starts loading the claimed group.  Needs an even
-// number (>= 4) of sub-chunks per group.
-template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8, bool DYN = false>
-__global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
+// number (>= 4) of sub-chunks per group (per wave set, with KS > 1).
+//
+// KS > 1 (dynamic LM head): KS sets of 4 waves share the group, set s taking
+// the s-th 1/KS of K with its own activation stream, and the other sets'
+// sums join set 0's through LDS when the group ends.  A group then takes
+// 1/KS of the time, so the last groups claimed end the launch sooner (one
+// such workgroup per CU: no second workgroup to compete for the CU).
+template <int MT, int ASRC, int OUT, bool PACKED, int UW = 8, bool DYN = false, int KS = 1>
+__global__ __launch_bounds__(256 * KS, KS > 1 ? 1 : (OUT == SO_ARGMAX || UW == 16 ? 2 : 4)) void k_skinny(SkinnyArgs a, int S, int kps, int n_tiles,
                                                    int gpw) {
   static_assert(!DYN || (OUT == SO_ARGMAX && PACKED), "dynamic groups: packed LM head only");
+  static_assert(KS == 1 || DYN, "wave sets: dynamic LM head only");
   constexpr int U = UW / MT, KC = 32 * U, ROWS = 16 * MT, CPR = KC / 8;
   constexpr int NCH = ROWS * CPR / 256;
   constexpr bool NORM = ASRC == SA_NORM || ASRC == SA_NORM1;   // RMSNorm while staging
@@ -281,12 +288,16 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   constexpr int LPR = 256 / ROWS;         // threads per row in the norm prologue
   static_assert(ROWS * CPR % 256 == 0 && 256 % CPR == 0,
                 "sub-chunk must split evenly over 256 threads, same columns per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][NP][ROWS][KC + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t As[KS][2][NP][ROWS][KC + 8];
   __shared__ float inv_s[ROWS];
   __shared__ unsigned long long sh_old;
   __shared__ int sh_grp[2];   // DYN: the group after group q, in slot (q + 1) & 1
+  __shared__ float red[KS > 1 ? KS - 1 : 1][KS > 1 ? ROWS : 1][KS > 1 ? 68 : 1];   // wave-set sums
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // tid: the thread within its wave set (256 threads); ks: the set
+  const int ks = KS > 1 ? (int)(threadIdx.x >> 8) : 0;
+  const int tid = KS > 1 ? (int)(threadIdx.x & 255) : (int)threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int tg = tile_groups(OUT, a.dh);
   const int per = tg * S;
@@ -296,7 +307,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   // queue rotation of the workgroup -> XCD placement (see the publish step)
   const unsigned rot = (OUT != SO_ARGMAX && a.qhint_rd != nullptr) ? (*a.qhint_rd & 7u) : 0u;
   const int grp = OUT == SO_ARGMAX ? tile * gpw : tile * tg + member / S, split = member % S;
-  const int kbeg = split * kps;
+  const int kset = ks * (kps / KS);   // the set's first column within the slice
+  const int kbeg = split * kps + kset;
   const int M = a.M, N = a.N, K = a.K;
   int vcol0 = grp * 64 + wave * 16;                        // virtual column of the wave
   const bool active = vcol0 < N;
@@ -383,11 +395,11 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
           hw[e] = pack_bf2(ya, yb);
           lw[e] = pack_bf2(ya - __uint_as_float(hw[e] << 16), yb - __uint_as_float(hw[e] & 0xFFFF0000u));
         }
-        st16(&As[buf][0][srow[i]][scol[i]], u32x4{hw[0], hw[1], hw[2], hw[3]});
-        if (TWO) st16(&As[buf][NP - 1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
+        st16(&As[ks][buf][0][srow[i]][scol[i]], u32x4{hw[0], hw[1], hw[2], hw[3]});
+        if (TWO) st16(&As[ks][buf][NP - 1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
       } else {
-        st16(&As[buf][0][srow[i]][scol[i]], r0[i]);
-        if (TWO) st16(&As[buf][NP - 1][srow[i]][scol[i]], r1[i]);
+        st16(&As[ks][buf][0][srow[i]][scol[i]], r0[i]);
+        if (TWO) st16(&As[ks][buf][NP - 1][srow[i]][scol[i]], r1[i]);
       }
     }
   };
@@ -418,7 +430,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
 #pragma unroll
     for (int q = 0; q < Q; ++q) s += ssv[q] * (q * LPR + nrm_j < a.ss_tiles ? 1.f : 0.f);
     for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
-    if (nrm_j == 0) inv_s[nrm_row] = nrm_row < M ? 1.0f / sqrtf(s / (float)K + a.eps) : 0.f;
+    if (nrm_j == 0 && ks == 0) inv_s[nrm_row] = nrm_row < M ? 1.0f / sqrtf(s / (float)K + a.eps) : 0.f;
     __syncthreads();
   }
   stage(0);
@@ -431,7 +443,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   // across the barrier, and the MFMAs wait only for their own batch (loads
   // retire in order).  The loads are not predicated (waves past N read a
   // clamped row), so the wait counts stay exact.
-  const int nsub = kps / KC;   // >= 1 sub-chunks per group
+  const int nsub = kps / KS / KC;   // >= 1 sub-chunks per group (per wave set)
   const int ngroups = (N + 63) / 64;
   auto step = [&](auto load_tag, int J, int buf, const u32x4* bw, u32x4* bnext,
                   unsigned& claim) {
@@ -443,7 +455,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
       // the start of the next group once J + 1 opens it)
       fetch(((J + 1) % nsub) * KC);
       if (DYN && jq == nsub - 1)
-        bp = a.packed + (((size_t)sh_grp[(q + 1) & 1] * (K / 32)) * 4 + wave) * 512 + lane * 8;
+        bp = a.packed + (((size_t)sh_grp[(q + 1) & 1] * (K / 32) + kset / 32) * 4 + wave) * 512 +
+             lane * 8;
 #pragma unroll
       for (int u = 0; u < U; ++u) bnext[u] = wload((DYN ? (J + 1) % nsub : J + 1) * KC, u);
       __builtin_amdgcn_sched_barrier(0);
@@ -451,18 +464,18 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
       // waiting for it waits for nothing the MFMAs below do not need anyway.
       // (Published before a claim is made in program order, so the compiler
       // never counts a claim of this same step as pending here.)
-      if (DYN && jq == 1 && tid == 0) sh_grp[(q + 1) & 1] = n_tiles + (int)claim;
-      if (DYN && jq == 0 && tid == 0) claim = atomicAdd(a.wctr, 1u);
+      if (DYN && jq == 1 && tid == 0 && ks == 0) sh_grp[(q + 1) & 1] = n_tiles + (int)claim;
+      if (DYN && jq == 0 && tid == 0 && ks == 0) claim = atomicAdd(a.wctr, 1u);
       __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u32x4 av = ld16(&As[buf][0][m * 16 + lr][u * 32 + lg * 8]);
+        const u32x4 av = ld16(&As[ks][buf][0][m * 16 + lr][u * 32 + lg * 8]);
         acc[m] = mfma_16x16x32(av, bw[u], acc[m]);
         if (TWO) {
-          const u32x4 al = ld16(&As[buf][NP - 1][m * 16 + lr][u * 32 + lg * 8]);
+          const u32x4 al = ld16(&As[ks][buf][NP - 1][m * 16 + lr][u * 32 + lg * 8]);
           acc[m] = mfma_16x16x32(al, bw[u], acc[m]);
         }
       }
@@ -484,13 +497,32 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
   // start the next group
   auto group_end = [&](int J) {
     if (OUT != SO_ARGMAX || (J + 1) % nsub != 0) return;
+    if (KS > 1) {
+      // the other wave sets' sums join set 0's, in set order (the last
+      // step's barrier ordered every earlier read of red before this write)
+      if (ks > 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[ks - 1][m * 16 + lg * 4 + i][wave * 16 + lr] = acc[m][i];
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < KS - 1; ++s2)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][i] += red[s2][m * 16 + lg * 4 + i][wave * 16 + lr];
+      }
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + lg * 4 + i;
         const int col = vcol0 + lr;
-        if (col < N) {
+        if (col < N && ks == 0) {
           const float v = acc[m][i];
           const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
                                                         (uint32_t)(row % a.gamma), (uint32_t)col)
@@ -559,11 +591,12 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + lg * 4 + i;
         const uint64_t key = max16(best[m][i]);
-        if (lr == 0) wkeys[wave][row] = key;
+        if (lr == 0 && ks == 0) wkeys[wave][row] = key;
       }
     __syncthreads();
+    const bool lead = ks == 0;   // wave sets > 0 hold no keys (they still meet the barriers)
     const unsigned slot = xcc_id() & 7u;
-    if (tid < ROWS && tid < M) {
+    if (lead && tid < ROWS && tid < M) {
       uint64_t key = wkeys[0][tid];
 #pragma unroll
       for (int w = 1; w < 4; ++w) key = wkeys[w][tid] > key ? wkeys[w][tid] : key;
@@ -571,10 +604,10 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
     }
     __builtin_amdgcn_s_waitcnt(0);   // the atomics are performed
     __syncthreads();
-    if (tid == 0) sh_old = atomicAdd(a.actr, 1ull);
+    if (lead && tid == 0) sh_old = atomicAdd(a.actr, 1ull);
     __syncthreads();
     if (sh_old != (unsigned long long)(n_tiles - 1)) return;
-    if (tid < M) {
+    if (lead && tid < M) {
       uint64_t key = 0;
 #pragma unroll
       for (int x = 0; x < kXcds; ++x) {
@@ -587,6 +620,7 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
                                                : (int32_t)argmax_key_index(key);
     }
     __syncthreads();
+    if (!lead) return;
     for (int i = tid; i < kXcds * 64; i += 256) atomicExch(&a.amax[i], 0ull);
     if (tid == 0) atomicExch(a.actr, 0ull);
     if (DYN && tid == 0) atomicExch(a.wctr, 0u);
@@ -676,6 +710,8 @@ __global__ __launch_bounds__(256, OUT == SO_ARGMAX || UW == 16 ? 2 : 4) void k_s
 // contiguous run of groups (one long chunk per workgroup keeps HBM pages open
 // and pays the start and publish latency once).
 constexpr int kArgmaxWgTarget = 512;
+// Dynamic LM head with two wave sets per group: one 8-wave workgroup per CU.
+constexpr int kArgmaxWgTargetKs = 256;
 
 template <int MT, int ASRC, int OUT>
 hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t st) {
@@ -689,6 +725,16 @@ hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t 
     // claim is made at sub-chunk 0, published at 1 and used from the last
     const int nsub = p.kpw / (32 * 16 / MT);
     dyn = a.wctr != nullptr && w16 && nsub >= 4 && nsub % 2 == 0;
+    if constexpr (OUT == SO_ARGMAX) {
+      if (dyn && nsub >= 8 && nsub % 4 == 0) {
+        // two wave sets (each needs an even number >= 4 of sub-chunks)
+        n_tiles = n_tiles < kArgmaxWgTargetKs ? n_tiles : kArgmaxWgTargetKs;   // workgroups
+        const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16, true, 2>), dim3(padded * per),
+                           dim3(512), 0, st, a, p.splits, p.kpw, n_tiles, gpw);
+        return hipGetLastError();
+      }
+    }
     if (dyn) {
       n_tiles = n_tiles < kArgmaxWgTarget ? n_tiles : kArgmaxWgTarget;   // workgroups
     } else {
