@@ -608,16 +608,18 @@ __global__ __launch_bounds__(256 * KS, KS > 1 ? 1 : (OUT == SO_ARGMAX || UW == 1
     __syncthreads();
     if (sh_old != (unsigned long long)(n_tiles - 1)) return;
     if (lead && tid < M) {
+      uint64_t ks8[kXcds];
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x)
+        ks8[x] = __hip_atomic_load(&a.amax[x * 64 + tid], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      // the anchor loads behind the slots (one wait for all)
+      const int32_t anc = a.anchor ? a.anchor[tid / a.gamma] : 0;
       uint64_t key = 0;
 #pragma unroll
-      for (int x = 0; x < kXcds; ++x) {
-        const uint64_t k2 = __hip_atomic_load(&a.amax[x * 64 + tid], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-        key = k2 > key ? k2 : key;
-      }
+      for (int x = 0; x < kXcds; ++x) key = ks8[x] > key ? ks8[x] : key;
       const int j = tid % a.gamma;
-      a.block_tokens[tid] = j == 0 && a.anchor ? a.anchor[tid / a.gamma]
-                                               : (int32_t)argmax_key_index(key);
+      a.block_tokens[tid] = j == 0 && a.anchor ? anc : (int32_t)argmax_key_index(key);
     }
     __syncthreads();
     if (!lead) return;
