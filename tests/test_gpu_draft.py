@@ -10,8 +10,8 @@ ones; the first, last and every fourth sequence of the batch-32 one, plus
 its longest and shortest contexts), block sizes 4, 8 and 10 at the batch-1 Qwen3-8B shape, every GEMM path (1, 2, 4 row tiles and the tiled kernel,
 packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
-one, determinism, batch invariance, other streams, and the device error
-word."""
+one, determinism, batch invariance, other streams, replays from a captured
+HIP graph, and the device error word."""
 import numpy as np
 import pytest
 
@@ -188,6 +188,52 @@ def test_draft_on_other_streams_is_bit_identical():
             b2, l2 = gpu_draft(drafter, kv, anc, 16, pps)
         assert np.array_equal(blk, b2) and np.array_equal(lg, l2)
         assert drafter.device_error() == 0
+
+
+@pytest.mark.parametrize("which", ["mini", "qwen3-8b-bs1"])
+def test_draft_replays_from_a_captured_graph(which):
+    # The draft call allocates nothing, never waits on the host and records no
+    # memset, so a HIP graph can capture it.  Each replay (with eager draft
+    # calls and host synchronisation between replays) must reproduce the eager
+    # call's tokens and logits exactly.  The full-size case runs the dynamic
+    # LM head and the split-K products at their benchmark launch shapes.
+    import torch
+    if which == "mini":
+        s, w, ctx = MINI, make_weights(MINI), [33, 250, 7]
+    else:
+        s = CONFIGS[2]
+        w, ctx = _c2_weights(), list(context_lengths(s))
+    drafter, _, _ = make_drafter(s, w)
+    pps = pages_for(max(ctx))
+    cache, kv, _ = setup_cache(s, ctx, pps)
+    anc = anchors(s, len(ctx), tag="draft.graph")
+    blk, lg = gpu_draft(drafter, kv, anc, s.block, pps)
+    B, gamma = len(ctx), s.block
+    ws = workspace(drafter, B, gamma, 1, pps)
+    a = torch.from_numpy(np.asarray(anc, np.int32)).cuda()
+    b2 = torch.full((B, gamma), -5, dtype=torch.int32, device="cuda")
+    l2 = torch.full((B, gamma, drafter.cfg.vocab), float("nan"), device="cuda")
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        drafter.draft(kv, a, gamma, b2, ws, logits=l2)   # first use of the capture stream
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        drafter.draft(kv, a, gamma, b2, ws, logits=l2)
+    for r in range(4):
+        b2.fill_(-7)
+        l2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"  {which}: replay {r}")
+        assert np.array_equal(b2.cpu().numpy(), blk)
+        assert np.array_equal(l2.cpu().numpy(), lg)
+        b3, l3 = gpu_draft(drafter, kv, anc, gamma, pps)      # eager work between replays
+        assert np.array_equal(b3, blk) and np.array_equal(l3, lg)
+    assert drafter.device_error() == 0
 
 
 def test_draft_device_error_word_reports_bad_page_and_anchor():
