@@ -52,7 +52,7 @@ if ROOT not in sys.path:
 METRIC = "draft blocks/s & draft tokens/s (block 16, Qwen3-8B-shaped, bs 1/32); %HBM peak"
 # LM head at M <= 16 rows: packed, norm-staged, argmax, 16-block batches, column
 # groups taken dynamically
-LM_KERNEL = {"bf16-skinny": "k_skinny<1, 2, 1, true, 16, true>"}
+LM_KERNEL = {"bf16-skinny": "k_skinny<1, 2, 1, true, 16, true, 2>"}
 COPY_BYTES = 1 << 30                               # calibration copy size
 KERNEL_SOURCES = ("block_diffusion_drafter_fc_amd/csrc/skinny.hip",
                   "block_diffusion_drafter_fc_amd/csrc/common.h",
