@@ -727,9 +727,11 @@ hipError_t run(const GemmPlan& p, const SkinnyArgs& a, int n_tiles, hipStream_t 
     // claim is made at sub-chunk 0, published at 1 and used from the last
     const int nsub = p.kpw / (32 * 16 / MT);
     dyn = a.wctr != nullptr && w16 && nsub >= 4 && nsub % 2 == 0;
-    if constexpr (OUT == SO_ARGMAX) {
+    if constexpr (OUT == SO_ARGMAX && MT == 1) {
+      // two wave sets (each needs an even number >= 4 of sub-chunks); one
+      // row tile only: at four (64 rows) the kernel spills and the 4 x 32K
+      // draft measured 1775 -> 1873 us
       if (dyn && nsub >= 8 && nsub % 4 == 0) {
-        // two wave sets (each needs an even number >= 4 of sub-chunks)
         n_tiles = n_tiles < kArgmaxWgTargetKs ? n_tiles : kArgmaxWgTargetKs;   // workgroups
         const int padded = (n_tiles + kXcds - 1) / kXcds * kXcds;
         hipLaunchKernelGGL((k_skinny<MT, ASRC, OUT, true, 16, true, 2>), dim3(padded * per),
