@@ -11,7 +11,8 @@ its longest and shortest contexts), block sizes 4, 8 and 10 at the batch-1 Qwen3
 packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
 one, determinism, batch invariance, other streams, replays from a captured
-HIP graph, and the device error word."""
+HIP graph, the two-wave-set LM head with fewer groups than workgroups, and
+the device error word."""
 import numpy as np
 import pytest
 
@@ -188,6 +189,19 @@ def test_draft_on_other_streams_is_bit_identical():
             b2, l2 = gpu_draft(drafter, kv, anc, 16, pps)
         assert np.array_equal(blk, b2) and np.array_equal(lg, l2)
         assert drafter.device_error() == 0
+
+
+@pytest.mark.parametrize("vocab", [1000, 130])
+def test_draft_lm_head_wave_sets_few_groups(vocab):
+    # Hidden 4096 at one row tile runs the LM head with two wave sets per
+    # 64-column group.  A small vocabulary leaves fewer groups than
+    # workgroups and a ragged last group (1000 = 15 x 64 + 40, 130 = 2 x 64
+    # + 2); blocks of 16 and 5 rows.
+    s = Shape(f"ks-bf16-v{vocab}", 4096, 1, 32, 8, 128, 1024, vocab, 16, 1, True,
+              seed=995 + vocab)
+    w = make_weights(s)
+    run_case(s, [70], 16, weights=w)
+    run_case(s, [37], 5, weights=w)
 
 
 @pytest.mark.parametrize("which", ["mini", "qwen3-8b-bs1"])
