@@ -132,6 +132,17 @@ DF_DEV void store4(void* base, size_t plane, size_t i, const f32x4& v) {
   }
 }
 
+// Four consecutive gains as fp32 (one 8-byte load for bf16 gains).
+template <bool BF16>
+DF_DEV f32x4 load_gain4(const typename Act<BF16>::T* g, int d) {
+  if (BF16) {
+    const uint2 w = *(const uint2*)((const uint16_t*)g + d);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+  return *(const f32x4*)((const float*)g + d);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict__ x,
                                                                const float* __restrict__ part,
@@ -142,6 +153,16 @@ __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict
   __shared__ float red[16];
   const int r = blockIdx.x;
   float* xr = x + (size_t)r * D;
+  // the residual and the gains (needed only after the row sum) load first,
+  // at clamped in-bounds columns, so the wait for the partial slices that
+  // follow covers them too
+  f32x4 xv[kResMaxPass], gv[kResMaxPass];
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4, dc = d < D ? d : 0;
+    xv[p] = *(const f32x4*)&xr[dc];
+    gv[p] = load_gain4<BF16>(g, dc);
+  }
   f32x4 v[kResMaxPass];
   float ss = 0.f;
 #pragma unroll
@@ -152,7 +173,7 @@ __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict
       f32x4 add = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int s = 0; s < splits; ++s) add += *(const f32x4*)&part[((size_t)s * M + r) * D + d];
-      v[p] = *(const f32x4*)&xr[d] + add;
+      v[p] = xv[p] + add;
       *(f32x4*)&xr[d] = v[p];
       ss += v[p][0] * v[p][0] + v[p][1] * v[p][1] + v[p][2] * v[p][2] + v[p][3] * v[p][3];
     }
@@ -165,7 +186,7 @@ __global__ __launch_bounds__(kResThreads) void k_residual_norm(float* __restrict
     if (d < D) {
       f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * Act<BF16>::load(g, d + e);
+      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * gv[p][e];
       store4<BF16>(y, y_plane, (size_t)r * D + d, o);
     }
   }
@@ -274,6 +295,12 @@ __global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __rest
                                                              float eps, void* __restrict__ c) {
   __shared__ float red[16];
   const int t = blockIdx.x;
+  f32x4 gv[kResMaxPass];   // loaded first: the slices' wait covers them
+#pragma unroll
+  for (int p = 0; p < kResMaxPass; ++p) {
+    const int d = (p * kResThreads + threadIdx.x) * 4;
+    gv[p] = load_gain4<BF16>(g, d < D ? d : 0);
+  }
   f32x4 v[kResMaxPass];
   float ss = 0.f;
 #pragma unroll
@@ -294,7 +321,7 @@ __global__ __launch_bounds__(kResThreads) void k_inject_norm(const float* __rest
     if (d < D) {
       f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * Act<BF16>::load(g, d + e);
+      for (int e = 0; e < 4; ++e) o[e] = v[p][e] * inv * gv[p][e];
       if (BF16)   // c is held in the model dtype: one rounded bf16 plane
         *(uint2*)&((uint16_t*)c)[(size_t)t * D + d] = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
       else
