@@ -302,6 +302,42 @@ def test_draft_mini_bf16_longest_first_order(ctx, gamma):
     run_case(MINI, ctx, gamma)
 
 
+GREEDY_NO_LOGITS = [[40] * 8, [3 + 19 * b for b in range(17)], [250, 0] * 16]
+
+
+@pytest.mark.parametrize("zero_norm", [False, True])
+@pytest.mark.parametrize("ctx", GREEDY_NO_LOGITS)
+def test_draft_greedy_without_logits_matches_with_logits(ctx, zero_norm):
+    # Without a logits output the large LM-head product takes its short
+    # argmax scan (columns past the vocabulary masked, fragments scanned in
+    # order); with one it takes the general path that run_case checks
+    # against the oracle.  The tokens must agree exactly: 128, 272 and 512
+    # rows, a ragged last column tile (vocabulary 1000), and with a zero
+    # final-norm gain every row one tie resolved to column 0.
+    w = make_weights(MINI)
+    if zero_norm:
+        w["final_norm"] = np.zeros_like(w["final_norm"])
+    drafter, kv, anc, blk, lg, pps = run_case(MINI, ctx, 16, weights=w,
+                                              sample=[0, len(ctx) - 1])
+    blk2, _ = gpu_draft(drafter, kv, anc, 16, pps, logits=False)
+    assert drafter.device_error() == 0
+    assert np.array_equal(blk, blk2)
+    if zero_norm:
+        for b in range(len(ctx)):
+            assert list(blk2[b][1:]) == [0] * 15
+
+
+def test_draft_qwen3_8b_batch32_greedy_without_logits():
+    # the measured configuration: batch-32 LM head over the full vocabulary
+    # (151936 = 593 x 256 + 128: a ragged last tile) without a logits output
+    s = CONFIGS[3]
+    L = context_lengths(s)
+    drafter, kv, anc, blk, lg, pps = run_case(s, L, s.block, sample=[0, s.batch - 1])
+    blk2, _ = gpu_draft(drafter, kv, anc, s.block, pps, logits=False)
+    assert drafter.device_error() == 0
+    assert np.array_equal(blk, blk2)
+
+
 @pytest.mark.parametrize("ctx", [[37], [5, 0, 129, 64, 17], [40] * 8])
 def test_draft_lm_head_ties_take_the_lowest_index(ctx):
     # A zero final-norm gain makes every logit exactly zero, so each row is
