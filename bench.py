@@ -369,6 +369,63 @@ def host_description() -> dict:
             "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
 
 
+def hipblaslt_lm_head(s, rows):
+    """Vendor-library comparison for the LM head: torch.mm (hipBLASLt on
+    ROCm) of random bf16 activations [rows][hidden] with a random bf16
+    weight [vocab][hidden] (bf16 logits out), alone and followed by the row
+    argmax that the fused kernel also does, at the workload's rows and at
+    twice as many.  A measurement beside the product path, not part of it."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(s.seed)
+    w = (torch.randn(s.vocab, s.hidden, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    out = {}
+    for m in (rows, 2 * rows):
+        a = torch.randn(m, s.hidden, device="cuda", generator=g).to(torch.bfloat16)
+        flops = 2.0 * m * s.vocab * s.hidden
+        rec = {}
+        for name, fn in (("mm", lambda: torch.mm(a, w.t())),
+                         ("mm_argmax", lambda: torch.mm(a, w.t()).argmax(dim=1))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            rec[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        out[f"rows_{m}"] = rec
+        del a
+    del w
+    torch.cuda.empty_cache()
+    return out
+
+
+def lm_roofline(s, rows, lm_bytes, lm_avg_ms, launches):
+    """Roofline object of the LM head, the dominant kernel.  Up to 64 rows it
+    is the fused weight-streaming product (HBM-bound: the bytes it must read
+    over the launch time against 8 TB/s); from 128 rows on it is the
+    large-tile MFMA product (2 * rows * vocab * hidden flops against the
+    2.5 PFLOP/s bf16 peak).  Counter traffic is recorded for the first."""
+    if rows >= 128:
+        flops = 2.0 * rows * s.vocab * s.hidden
+        tf = flops / (lm_avg_ms * 1e-3) / 1e12
+        return {"kernel": "LM head: bf16 MFMA 256 x 256 tiles + argmax (k_gemm_big)",
+                "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                "avg_launch_ms": round(lm_avg_ms, 5), "launches": launches,
+                "flops_per_launch": flops, "traffic": None}
+    gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
+    return {"kernel": "LM head: final RMSNorm staged + bf16 MFMA + argmax (k_skinny)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_ms": round(lm_avg_ms, 5), "launches": launches,
+            "bytes_per_launch": lm_bytes, "traffic": recorded_traffic(s.name)}
+
+
 def cpu_baseline(s, w_host, budget_s=15.0):
     """The oracle, as committed, on a bounded sample of the same step: per
     block, inject the new context tokens of a step (their target features),
@@ -880,6 +937,9 @@ def main():
                     help="time the packed forward + loss of N blocks of one sequence instead")
     ap.add_argument("--block-sweep", default=None, metavar="G1,G2,...",
                     help="time the step at each block size instead (one JSON line)")
+    ap.add_argument("--lm-head-hipblaslt", action="store_true",
+                    help="also time hipBLASLt (torch.mm) on the LM-head shape, bare and with "
+                         "the row argmax, at the workload's rows and twice as many")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -927,7 +987,6 @@ def main():
     blocks_per_s = B * args.steps / res["elapsed"]
     lm_bytes = rep["lm_bytes"]
     lm_avg_ms = res["lm_ms"] / max(res["lm_count"], 1)
-    lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(blocks_per_s, 3),
@@ -955,12 +1014,10 @@ def main():
         "verify_only": res["verify_spread"],
         "replay_accept_match": res["replay_ok"],
         "prefill": {"tokens": res["prefill_tokens"], "s": round(res["prefill_s"], 4)},
-        "roofline": {"kernel": "LM head: final RMSNorm staged + bf16 MFMA + argmax (k_skinny)",
-                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "avg_launch_ms": round(lm_avg_ms, 5), "launches": res["lm_count"],
-                     "bytes_per_launch": lm_bytes, "traffic": recorded_traffic(s.name)},
+        "roofline": lm_roofline(s, B * gamma, lm_bytes, lm_avg_ms, res["lm_count"]),
     }
+    if args.lm_head_hipblaslt:
+        line["lm_head_hipblaslt"] = hipblaslt_lm_head(s, B * gamma)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(s, w_host, args.cpu_budget)
     del w_host

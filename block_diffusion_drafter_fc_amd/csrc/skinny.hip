@@ -252,7 +252,7 @@ DF_DEV void epi_kv(const SkinnyArgs& a, int S, int y) {
 }
 
 // --------------------------------------------------------------- the kernel
-// grid: (n_tiles rounded up to a multiple of 8) * per workgroups of 256
+// grid: (n_tiles rounded up to a multiple of 8) * per workgroups of 256 * KS
 // threads, per = tile_groups * S.  The LM head (SO_ARGMAX) over packed
 // weights: workgroup t takes the gpw consecutive 64-column groups
 // [t * gpw, t * gpw + gpw) as one run of sub-chunks -- their packed tiles are
