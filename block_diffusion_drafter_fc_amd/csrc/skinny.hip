@@ -516,23 +516,38 @@ __global__ __launch_bounds__(256 * KS, KS > 1 ? 1 : (OUT == SO_ARGMAX || UW == 1
             for (int i = 0; i < 4; ++i) acc[m][i] += red[s2][m * 16 + lg * 4 + i][wave * 16 + lr];
       }
     }
+    if (!a.draw.on && a.logits == nullptr) {
+      // greedy, no logits: a select per value, no branch (a branch per
+      // value over the noise and store code costs an instruction fetch)
+      const int col = vcol0 + lr;
+      const bool ok = col < N && ks == 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m * 16 + lg * 4 + i;
-        const int col = vcol0 + lr;
-        if (col < N && ks == 0) {
-          const float v = acc[m][i];
-          const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
-                                                        (uint32_t)(row % a.gamma), (uint32_t)col)
-                                     : v;
-          const uint64_t key = argmax_key(kv, (uint32_t)col);
-          best[m][i] = key > best[m][i] ? key : best[m][i];
-          if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t key = argmax_key(acc[m][i], (uint32_t)col);
+          best[m][i] = ok && key > best[m][i] ? key : best[m][i];
+          acc[m][i] = 0.f;
         }
-        acc[m][i] = 0.f;
-      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m * 16 + lg * 4 + i;
+          const int col = vcol0 + lr;
+          if (col < N && ks == 0) {
+            const float v = acc[m][i];
+            const float kv = a.draw.on ? v + gumbel_noise(a.draw.seed, (uint32_t)(row / a.gamma),
+                                                          (uint32_t)(row % a.gamma), (uint32_t)col)
+                                       : v;
+            const uint64_t key = argmax_key(kv, (uint32_t)col);
+            best[m][i] = key > best[m][i] ? key : best[m][i];
+            if (a.logits != nullptr && row < M) a.logits[(size_t)row * N + col] = v;
+          }
+          acc[m][i] = 0.f;
+        }
+    }
     vcol0 = DYN ? sh_grp[(J / nsub + 1) & 1] * 64 + wave * 16 : vcol0 + 64;
   };
   // DYN: sub-chunk J ends the stream when it closes a group and the group

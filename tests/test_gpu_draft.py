@@ -11,8 +11,9 @@ its longest and shortest contexts), block sizes 4, 8 and 10 at the batch-1 Qwen3
 packed and row-major weights),
 ragged and empty contexts, several context splits, ragged blocks, a block of
 one, determinism, batch invariance, other streams, replays from a captured
-HIP graph, the two-wave-set LM head with fewer groups than workgroups, and
-the device error word."""
+HIP graph, the two-wave-set LM head with fewer groups than workgroups, the
+greedy LM heads without a logits output (their branch-free argmax, against
+the oracle-checked run with logits), and the device error word."""
 import numpy as np
 import pytest
 
@@ -200,8 +201,10 @@ def test_draft_lm_head_wave_sets_few_groups(vocab):
     s = Shape(f"ks-bf16-v{vocab}", 4096, 1, 32, 8, 128, 1024, vocab, 16, 1, True,
               seed=995 + vocab)
     w = make_weights(s)
-    run_case(s, [70], 16, weights=w)
-    run_case(s, [37], 5, weights=w)
+    for ctx, gamma in (([70], 16), ([37], 5)):
+        drafter, kv, anc, blk, _, pps = run_case(s, ctx, gamma, weights=w)
+        blk2, _ = gpu_draft(drafter, kv, anc, gamma, pps, logits=False)   # branch-free fold
+        assert np.array_equal(blk, blk2)
 
 
 @pytest.mark.parametrize("which", ["mini", "qwen3-8b-bs1"])
@@ -302,18 +305,21 @@ def test_draft_mini_bf16_longest_first_order(ctx, gamma):
     run_case(MINI, ctx, gamma)
 
 
-GREEDY_NO_LOGITS = [[40] * 8, [3 + 19 * b for b in range(17)], [250, 0] * 16]
+GREEDY_NO_LOGITS = [[37], [5, 129], [64, 17, 300, 31], [40] * 8, [3 + 19 * b for b in range(17)],
+                    [250, 0] * 16]
 
 
 @pytest.mark.parametrize("zero_norm", [False, True])
 @pytest.mark.parametrize("ctx", GREEDY_NO_LOGITS)
 def test_draft_greedy_without_logits_matches_with_logits(ctx, zero_norm):
-    # Without a logits output the large LM-head product takes its short
-    # argmax scan (columns past the vocabulary masked, fragments scanned in
-    # order); with one it takes the general path that run_case checks
-    # against the oracle.  The tokens must agree exactly: 128, 272 and 512
-    # rows, a ragged last column tile (vocabulary 1000), and with a zero
-    # final-norm gain every row one tie resolved to column 0.
+    # Without a logits output both LM-head kernels take their branch-free
+    # argmax (the fused skinny head at 16, 32 and 64 rows folds each group
+    # with selects; the large product at 128, 272 and 512 rows scans its
+    # fragments in order with columns past the vocabulary masked); with one
+    # they take the general path that run_case checks against the oracle.
+    # The tokens must agree exactly, with a ragged last column group or tile
+    # (vocabulary 1000), and with a zero final-norm gain, where every row is
+    # one tie resolved to column 0.
     w = make_weights(MINI)
     if zero_norm:
         w["final_norm"] = np.zeros_like(w["final_norm"])
@@ -325,6 +331,17 @@ def test_draft_greedy_without_logits_matches_with_logits(ctx, zero_norm):
     if zero_norm:
         for b in range(len(ctx)):
             assert list(blk2[b][1:]) == [0] * 15
+
+
+def test_draft_qwen3_8b_batch1_greedy_without_logits():
+    # the headline configuration's LM head (two wave sets, dynamic groups)
+    # without a logits output
+    s = CONFIGS[2]
+    drafter, kv, anc, blk, lg, pps = run_case(s, context_lengths(s), s.block,
+                                              weights=_c2_weights())
+    blk2, _ = gpu_draft(drafter, kv, anc, s.block, pps, logits=False)
+    assert drafter.device_error() == 0
+    assert np.array_equal(blk, blk2)
 
 
 def test_draft_qwen3_8b_batch32_greedy_without_logits():
