@@ -626,6 +626,20 @@ __global__ __launch_bounds__(64 * WM * NWN, 1) void k_gemm_big(
     return;
   }
   if (!ARGMAX) {
+    if (m0 + BM <= M && n0 + BN <= N) {
+      // interior tile: stores without a bounds test each (one branch per
+      // store was the epilogue's code)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* dst = part + ((size_t)split * M + m0 + wm * 64 + a * 16 + lg * 4 + i) * N + n0 +
+                       wn * WCOL + lr;
+#pragma unroll
+          for (int b = 0; b < NBF; ++b) dst[b * 16] = acc[a][b][i];
+        }
+      return;
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
