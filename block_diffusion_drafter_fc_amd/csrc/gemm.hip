@@ -349,29 +349,57 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(
   // Row argmax of the tile's 128 columns: per wave (lanes, then tiles), then
   // over the two column halves in LDS; keys[blockIdx.x][row], no atomics.
   __shared__ uint64_t hkeys[2][TBM];
+  if (!dr.on && logits == nullptr) {
+    // greedy: the short branch-free scan of the large product's epilogue
+    // (columns past N become -inf; a strict > over ascending fragments keeps
+    // the lowest column among equal values)
+    if (n0 + TBN > N) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < 4; ++b)
+        if (n0 + wn * 64 + b * 16 + lr >= N)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rloc = wm * 64 + a * 16 + lg * 4 + i;
-      const int row = m0 + rloc;
-      uint64_t key = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = n0 + wn * 64 + b * 16 + lr;
-        if (col < N) {
-          const float v = acc[a][b][i];
-          const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
-                                                               (uint32_t)(row % dr.gamma), (uint32_t)col)
-                                            : v;
-          const uint64_t k2 = argmax_key(kv, (uint32_t)col);
-          key = k2 > key ? k2 : key;
-          if (logits != nullptr && row < M) logits[(size_t)row * N + col] = v;
-        }
-      }
-      key = max16(key);
-      if (lr == 0) hkeys[wn][rloc] = key;
+          for (int a = 0; a < 4; ++a) acc[a][b] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float bv = acc[a][0][i];
+        int bb = 0;
+#pragma unroll
+        for (int b = 1; b < 4; ++b) {
+          const bool gt = acc[a][b][i] > bv;
+          bv = gt ? acc[a][b][i] : bv;
+          bb = gt ? b : bb;
+        }
+        const uint64_t key = max16(argmax_key(bv, (uint32_t)(n0 + wn * 64 + bb * 16 + lr)));
+        if (lr == 0) hkeys[wn][wm * 64 + a * 16 + lg * 4 + i] = key;
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rloc = wm * 64 + a * 16 + lg * 4 + i;
+        const int row = m0 + rloc;
+        uint64_t key = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int col = n0 + wn * 64 + b * 16 + lr;
+          if (col < N) {
+            const float v = acc[a][b][i];
+            const float kv = dr.on && row < M ? v + gumbel_noise(dr.seed, (uint32_t)(row / dr.gamma),
+                                                                 (uint32_t)(row % dr.gamma), (uint32_t)col)
+                                              : v;
+            const uint64_t k2 = argmax_key(kv, (uint32_t)col);
+            key = k2 > key ? k2 : key;
+            if (logits != nullptr && row < M) logits[(size_t)row * N + col] = v;
+          }
+        }
+        key = max16(key);
+        if (lr == 0) hkeys[wn][rloc] = key;
+      }
+  }
   __syncthreads();
   if (tid < TBM && m0 + tid < M) {
     const uint64_t k0 = hkeys[0][tid], k1 = hkeys[1][tid];

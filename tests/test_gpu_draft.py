@@ -305,17 +305,18 @@ def test_draft_mini_bf16_longest_first_order(ctx, gamma):
     run_case(MINI, ctx, gamma)
 
 
-GREEDY_NO_LOGITS = [[37], [5, 129], [64, 17, 300, 31], [40] * 8, [3 + 19 * b for b in range(17)],
-                    [250, 0] * 16]
+GREEDY_NO_LOGITS = [[37], [5, 129], [64, 17, 300, 31], [5, 0, 129, 64, 17], [40] * 8,
+                    [3 + 19 * b for b in range(17)], [250, 0] * 16]
 
 
 @pytest.mark.parametrize("zero_norm", [False, True])
 @pytest.mark.parametrize("ctx", GREEDY_NO_LOGITS)
 def test_draft_greedy_without_logits_matches_with_logits(ctx, zero_norm):
-    # Without a logits output both LM-head kernels take their branch-free
+    # Without a logits output the LM-head kernels take their branch-free
     # argmax (the fused skinny head at 16, 32 and 64 rows folds each group
-    # with selects; the large product at 128, 272 and 512 rows scans its
-    # fragments in order with columns past the vocabulary masked); with one
+    # with selects; the tiled product at 80 rows and the large product at
+    # 128, 272 and 512 rows scan their fragments in order with columns past
+    # the vocabulary masked); with one
     # they take the general path that run_case checks against the oracle.
     # The tokens must agree exactly, with a ragged last column group or tile
     # (vocabulary 1000), and with a zero final-norm gain, where every row is
