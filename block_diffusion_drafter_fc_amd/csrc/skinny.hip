@@ -723,6 +723,178 @@ __global__ __launch_bounds__(256 * KS, KS > 1 ? 1 : (OUT == SO_ARGMAX || UW == 1
   }
 }
 
+// Gate/up product with the SwiGLU at one row tile (M <= 16), without split
+// K: workgroup b owns the 16-column output tiles [T b, T b + T) of h; its
+// waves 0 .. T-1 stream the gate rows of those tiles and waves T .. 2T-1 the
+// up rows, each over all of K, straight from the packed gate/up layout (tile
+// w of 64-row group 2 (r / 64) for gate row r, of group 2 (r / 64) + 1 for
+// the up row).  The normalised activations are staged as in k_skinny by the
+// first 256 threads (the other waves issue the same loads, so every wave
+// keeps the same count of loads in flight).  At the end the gate sums pass
+// through LDS to the up waves, which form silu(gate) * up; the workgroup then
+// stores its 16 x 16T block of h as split planes.  No partial slices,
+// arrival counters or last-arrival epilogue: with T = 3 and I = 12288, one
+// workgroup per CU over 256 CUs.  Waves past the last tile re-read the last
+// tile and store nothing.
+constexpr int kGluTiles = 3;
+constexpr int kGluMaxWgs = 256;   // one round on the chip, else the split-K path
+
+template <int U, int T>
+__global__ __launch_bounds__(128 * T, 1) void k_glu1(SkinnyArgs a) {
+  constexpr int KC = 32 * U, CPR = KC / 8, NCH = 16 * CPR / 256;
+  constexpr int LPR = 16;   // threads per row in the norm prologue
+  static_assert(16 * CPR % 256 == 0 && 256 % CPR == 0, "sub-chunk must split evenly over 256 threads");
+  static_assert(2 * T >= 4, "the first four waves stage the activations");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][2][16][KC + 8];
+  __shared__ float inv_s[16];
+  __shared__ float gx[T][16][17];
+  __shared__ __attribute__((aligned(16))) float hy[16][16 * T];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int stid = tid & 255;   // staging slot (waves 4.. mirror waves 0..)
+  const bool stager = tid < 256;
+  const int M = a.M, K = a.K, I = a.I, ntl = I / 16;
+  const int t = wave % T, ht0 = (int)blockIdx.x * T;
+  const bool up = wave >= T;
+  const int ht = ht0 + t < ntl ? ht0 + t : ntl - 1;
+  const int r = 16 * ht, g = 2 * (r / 64) + (up ? 1 : 0), wt = (r % 64) / 16;
+  const uint16_t* bp = a.packed + ((size_t)g * (K / 32) * 4 + wt) * 512 + lane * 8;
+  auto wload = [&](int k, int u) { return ld16_stream(bp + (size_t)(k / 32 + u) * (4 * 512)); };
+
+  int srow[NCH], scol[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = stid + i * 256;
+    srow[i] = c / CPR;
+    scol[i] = (c % CPR) * 8;
+  }
+  u32x4 r0[NCH], r1[NCH], rg;
+  auto fetch = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int row = srow[i] < M ? srow[i] : M - 1;
+      const float* xp = (const float*)a.A + (size_t)row * a.lda + k + scol[i];
+      r0[i] = ld16(xp);
+      r1[i] = ld16(xp + 4);
+      if (i == 0) rg = ld16((const uint16_t*)a.gain + k + scol[i]);
+    }
+  };
+  // y = x * inv * g, split into hi = bf16(y) and lo = bf16(y - hi)
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float inv = inv_s[srow[i]];
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xa = __uint_as_float(e < 2 ? r0[i][2 * e] : r1[i][2 * e - 4]);
+        const float xb = __uint_as_float(e < 2 ? r0[i][2 * e + 1] : r1[i][2 * e - 3]);
+        const uint32_t gw = rg[e];
+        const float ya = xa * inv * __uint_as_float(gw << 16);
+        const float yb = xb * inv * __uint_as_float(gw & 0xFFFF0000u);
+        hw[e] = pack_bf2(ya, yb);
+        lw[e] = pack_bf2(ya - __uint_as_float(hw[e] << 16), yb - __uint_as_float(hw[e] & 0xFFFF0000u));
+      }
+      st16(&As[buf][0][srow[i]][scol[i]], u32x4{hw[0], hw[1], hw[2], hw[3]});
+      st16(&As[buf][1][srow[i]][scol[i]], u32x4{lw[0], lw[1], lw[2], lw[3]});
+    }
+  };
+
+  // Prologue: row sums of squares, the activations of sub-chunk 0, then its
+  // weights (loads retire in order; the weights stay in flight meanwhile).
+  constexpr int Q = kMaxSsTiles / LPR;
+  const int nrm_row = stid / LPR, nrm_j = stid % LPR;
+  float ssv[Q];
+  {
+    const int rr = nrm_row < M ? nrm_row : M - 1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = q * LPR + nrm_j;
+      ssv[q] = a.ss_in[(size_t)(i < a.ss_tiles ? i : a.ss_tiles - 1) * M + rr];
+    }
+  }
+  fetch(0);
+  u32x4 bc[U], bn[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) bc[u] = wload(0, u);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) s += ssv[q] * (q * LPR + nrm_j < a.ss_tiles ? 1.f : 0.f);
+    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
+    if (nrm_j == 0 && tid < 256) inv_s[nrm_row] = nrm_row < M ? 1.0f / sqrtf(s / (float)K + a.eps) : 0.f;
+  }
+  __syncthreads();
+  if (stager) stage(0);
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](auto load_tag, int J, int buf, const u32x4* bw, u32x4* bnext) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    if (LOAD) {
+      fetch((J + 1) * KC);
+#pragma unroll
+      for (int u = 0; u < U; ++u) bnext[u] = wload((J + 1) * KC, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 ah = ld16(&As[buf][0][lr][u * 32 + lg * 8]);
+      acc = mfma_16x16x32(ah, bw[u], acc);
+      const u32x4 al = ld16(&As[buf][1][lr][u * 32 + lg * 8]);
+      acc = mfma_16x16x32(al, bw[u], acc);
+    }
+    if (LOAD) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (stager) stage(buf ^ 1);
+    }
+    __syncthreads();
+  };
+  using Load = std::integral_constant<bool, true>;
+  using Last = std::integral_constant<bool, false>;
+  const int nsub = K / KC;
+  int j = 0;
+  for (; j + 2 < nsub; j += 2) {
+    step(Load{}, j, 0, bc, bn);
+    step(Load{}, j + 1, 1, bn, bc);
+  }
+  if (nsub - j == 2) {
+    step(Load{}, j, 0, bc, bn);
+    step(Last{}, j + 1, 1, bn, bc);
+  } else {
+    step(Last{}, j, 0, bc, bn);
+  }
+
+  // silu(gate) * up, as the split-K epilogue computes it
+  if (!up) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gx[t][lg * 4 + i][lr] = acc[i];
+  }
+  __syncthreads();
+  if (up) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gv = gx[t][lg * 4 + i][lr];
+      hy[lg * 4 + i][t * 16 + lr] = gv / (1.0f + expf(-gv)) * acc[i];
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < 16 * 4 * T; p += 128 * T) {
+    const int row = p / (4 * T), c4 = (p % (4 * T)) * 4, col = ht0 * 16 + c4;
+    if (row < M && col < I) split_store4(a.h, a.h_plane, (size_t)row * I + col, *(const f32x4*)&hy[row][c4]);
+  }
+  // keep the split-K launches' XCD rotation hint current (see the publish step)
+  if (blockIdx.x == 0 && tid == 0 && a.qhint_wr != nullptr) *a.qhint_wr = xcc_id() & 7u;
+}
+
+// Whether the gate/up product at one row tile takes k_glu1.
+bool glu1_fits(const GemmPlan& p, const SkinnyArgs& a) {
+  const int wgs = (a.I / 16 + kGluTiles - 1) / kGluTiles;
+  return p.mt == 1 && a.M <= 16 && a.packed != nullptr && a.K % 512 == 0 && a.I % 64 == 0 &&
+         a.N == 2 * a.I && wgs <= kGluMaxWgs;
+}
+
 // LM head over packed weights: about this many workgroups, each streaming a
 // contiguous run of groups (one long chunk per workgroup keeps HBM pages open
 // and pays the start and publish latency once).
@@ -893,6 +1065,11 @@ hipError_t launch_skinny(const GemmPlan& p, int asrc, int out, const SkinnyArgs&
     if (a.cu_new == nullptr || a.ctx_lens == nullptr || a.dh % 2 ||
         (long long)a.rope_rows * (a.dh / 2) > wgs * 256)
       return hipErrorInvalidValue;
+  }
+  if (asrc == SA_NORM && out == SO_SWIGLU && glu1_fits(p, a)) {
+    const int wgs = (a.I / 16 + kGluTiles - 1) / kGluTiles;
+    hipLaunchKernelGGL((k_glu1<16, kGluTiles>), dim3(wgs), dim3(128 * kGluTiles), 0, st, a);
+    return hipGetLastError();
   }
 #define DF_RUN(A_, O_) \
   if (asrc == A_ && out == O_) return run_mt<A_, O_>(p, a, n_tiles, st)
